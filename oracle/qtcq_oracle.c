@@ -1,0 +1,566 @@
+/*
+ * qtcq_oracle.c -- plain, slow, single-threaded CPU oracle for the bitshift-trellis
+ * hot path (computed codes, Viterbi search, bitstream pack, window decode, BCJR).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  It shares no code, header, table or constant
+ * generator with the HIP library; the two only ever see the same seeded input arrays.
+ *
+ * Built with:  gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (x86-64 SSE arithmetic: every float operation below is one IEEE-754 binary32 or
+ * binary64 operation rounded to nearest-even; no fused multiply-add anywhere).
+ *
+ * Sources, cited by page title and section:
+ *  [QTIP]  "QTIP: Trellis-Coded Quantization Puts 2-Bit LLM Weights 10% Above the
+ *          Rate-Distortion Bound, and a Monotone Codebook Loses to Scalar Rounding"
+ *          (blog reimplementation of QTIP).  Sections "The trellis: a stateful
+ *          codebook" (the decode and Viterbi listings), "The codebook is computed"
+ *          (1MAD listing, 3INST prose), "Tail-biting is worth its complexity".
+ *  [XOR]   "XOR-Trellis -- Trellis-coded quantization vs VQ codebooks -- What does it
+ *          mean?" (explainer).  Sections "Directions, not an atlas" (16-bit state),
+ *          "The sign at each junction has to be cheap" (3INST cost: an FP16 add),
+ *          "Cliff edges: weighting errors instead of rotating them" (each step's
+ *          squared error multiplied by a per-weight weight D).
+ *  [BCJR]  "BCJR-QAT: A Differentiable Relaxation of Trellis-Coded Weight
+ *          Quantization" (abstract): forward-backward sum-product at temperature,
+ *          soft codeword = Boltzmann expectation over trellis paths.
+ *
+ * Readings where the pages are silent (each listed with its reason in the design
+ * notes): the search runs in binary32 with separate sub, square, [weight-multiply] and
+ * add, each rounded; ties go to the lowest predecessor index and the lowest final
+ * state; the start state is free (plain trellis); the 3INST LCG is the 1MAD LCG,
+ * its mask keeps the sign, 2 low exponent bits and 10 mantissa bits of each fp16 half,
+ * the magic constant is the fp16 nearest 0.922, the halves are added in fp16 (RNE)
+ * and the sum is divided by the printed raw sigma 1.244.  BCJR energy = the Viterbi
+ * path cost (a sum), path weight exp(-E / tau), uniform start prior, binary64.
+ *
+ * PARITY UNPINNED: the LCG inside 3INST.  The page names no LCG for 3INST; every
+ * other 3INST choice above is pinned by the printed raw sigma, the LCG choice is not
+ * (sigma is insensitive to it).
+ *
+ * Return codes: 0 = ok, 1 = invalid argument, 2 = out of memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ENOMEM 2
+
+enum { ORC_CODE_1MAD = 0, ORC_CODE_3INST = 1 };
+
+/* ------------------------------------------------------------------------------ */
+/* Computed codes  ([QTIP] "The codebook is computed")                              */
+/* ------------------------------------------------------------------------------ */
+
+/* The LCG step of 1MAD: multiply-add, kept modulo 2^32. */
+static uint32_t lcg(uint32_t x) { return 34038481u * x + 76625530u; }
+
+/* 1MAD: LCG, then the sum of the four bytes of the result (Irwin-Hall, n = 4), then
+ * centre by 510 and divide by 147.8 in binary64, rounded once to binary32. */
+float oracle_code_1mad(uint32_t x)
+{
+    uint32_t u = lcg(x);
+    uint32_t s = (u & 255u) + ((u >> 8) & 255u) + ((u >> 16) & 255u) + ((u >> 24) & 255u);
+    double c = ((double)s - 510.0) / 147.8;
+    return (float)c;
+}
+
+/* IEEE binary16 bit pattern -> its exact value as a double. */
+static double half_to_double(uint32_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24); /* subnormal */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value (ties to even); finite range only. */
+static double round_to_half(double x)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    double ax = fabs(x);
+    int e2;
+    frexp(ax, &e2);              /* ax = m * 2^e2, m in [0.5, 1) */
+    int q = e2 - 11;             /* spacing of binary16 values near ax is 2^(e2-11) */
+    if (q < -24) q = -24;        /* subnormal spacing */
+    double scaled = ldexp(ax, -q);     /* exact */
+    double r = nearbyint(scaled);      /* default rounding mode: nearest, ties to even */
+    double v = ldexp(r, q);
+    if (v > 65504.0) v = INFINITY;
+    return x < 0 ? -v : v;
+}
+
+/* 3INST before its scale: the LCG output, masked to the sign, the 2 low exponent bits
+ * and the 10 mantissa bits of each 16-bit half, XORed into the fp16 bit pattern of the
+ * magic constant on both halves, and the two fp16 halves added in fp16. */
+double oracle_code_3inst_raw(uint32_t x)
+{
+    const uint32_t magic16 = 0x3B60u; /* binary16 nearest to 0.922 (= 0.921875) */
+    uint32_t u = lcg(x);
+    uint32_t v = (u & 0x8FFF8FFFu) ^ ((magic16 << 16) | magic16);
+    double hi = half_to_double(v >> 16);
+    double lo = half_to_double(v & 0xFFFFu);
+    return round_to_half(hi + lo); /* hi + lo is exact in binary64 */
+}
+
+/* 3INST: the raw fp16 sum divided by the printed raw sigma (1.244) in binary64,
+ * rounded once to binary32. */
+float oracle_code_3inst(uint32_t x)
+{
+    double h = oracle_code_3inst_raw(x);
+    return (float)(h / 1.244);
+}
+
+/* Fill C[0 .. 2^L) with the code value of every L-bit state. */
+int oracle_code_table(int code, int L, float* C)
+{
+    if (L < 1 || L > 24 || !C) return ORC_EINVAL;
+    if (code != ORC_CODE_1MAD && code != ORC_CODE_3INST) return ORC_EINVAL;
+    uint32_t n = 1u << L;
+    for (uint32_t j = 0; j < n; ++j)
+        C[j] = code == ORC_CODE_1MAD ? oracle_code_1mad(j) : oracle_code_3inst(j);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Viterbi on the bitshift trellis  ([QTIP] "The trellis: a stateful codebook")     */
+/* ------------------------------------------------------------------------------ */
+
+/* Squared error of reconstructing target s with value c, in binary32, optionally
+ * multiplied by the per-weight error weight ([XOR] "Cliff edges ...").  Each of the
+ * sub, square and multiply is one rounded binary32 operation. */
+static float step_error(float c, float s, const float* w, int t)
+{
+    float d = c - s;
+    float e = d * d;
+    if (w) e = w[t] * e;
+    return e;
+}
+
+static int check_trellis(int T, int L, int k)
+{
+    if (T < 1 || L < 1 || L > 20 || k < 1 || k > L) return 0;
+    return 1;
+}
+
+/* Minimum-cost walk through the (L, k) bitshift trellis for targets s[0..T).
+ * State j follows state i when the top L-k bits of j equal the bottom L-k bits of i,
+ * so the predecessors of j are (j >> k) | (a << (L-k)) for the 2^k values of a.
+ * cost_0(j) = err_0(j); cost_t(j) = min over predecessors i of cost_{t-1}(i), plus
+ * err_t(j); the first (lowest) predecessor wins a tie, and the first (lowest) final
+ * state wins a tie.  The walk is read back through the stored predecessors.
+ * Outputs: st[0..T) the state sequence, *cost_out its (binary32) cost. */
+int oracle_viterbi(const float* C, const float* s, const float* w, int T, int L, int k,
+                   uint32_t* st, float* cost_out)
+{
+    if (!C || !s || !st || !check_trellis(T, L, k)) return ORC_EINVAL;
+    const uint32_t N = 1u << L;
+    const uint32_t K = 1u << k;
+    float* cost = (float*)malloc(sizeof(float) * N);
+    float* next = (float*)malloc(sizeof(float) * N);
+    uint32_t* back = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)T * N);
+    if (!cost || !next || !back) {
+        free(cost); free(next); free(back);
+        return ORC_ENOMEM;
+    }
+
+    for (uint32_t j = 0; j < N; ++j)
+        cost[j] = step_error(C[j], s[0], w, 0);
+
+    for (int t = 1; t < T; ++t) {
+        for (uint32_t j = 0; j < N; ++j) {
+            uint32_t best_i = j >> k;            /* a = 0 */
+            float best = cost[best_i];
+            for (uint32_t a = 1; a < K; ++a) {
+                uint32_t i = (j >> k) | (a << (L - k));
+                if (cost[i] < best) {            /* strict: the lowest index keeps ties */
+                    best = cost[i];
+                    best_i = i;
+                }
+            }
+            back[(size_t)t * N + j] = best_i;
+            next[j] = best + step_error(C[j], s[t], w, t);
+        }
+        float* tmp = cost; cost = next; next = tmp;
+    }
+
+    uint32_t jstar = 0;
+    for (uint32_t j = 1; j < N; ++j)
+        if (cost[j] < cost[jstar]) jstar = j;
+    *cost_out = cost[jstar];
+
+    st[T - 1] = jstar;
+    for (int t = T - 1; t > 0; --t)
+        st[t - 1] = back[(size_t)t * N + st[t]];
+
+    free(cost); free(next); free(back);
+    return ORC_OK;
+}
+
+/* Per-sequence MSE as the page defines it: the minimum path cost divided by T (in
+ * binary32). */
+static float mse_of(float cost, int T) { return cost / (float)T; }
+
+/* Batch driver: B independent sequences, row-major s[B][T], w[B][T] (or NULL).
+ * st[B][T], cost[B], mse[B] (cost and mse may be NULL). */
+int oracle_viterbi_batch(const float* C, const float* s, const float* w, int64_t B, int T,
+                         int L, int k, uint32_t* st, float* cost, float* mse)
+{
+    if (B < 0) return ORC_EINVAL;
+    for (int64_t b = 0; b < B; ++b) {
+        float c;
+        int rc = oracle_viterbi(C, s + b * T, w ? w + b * T : NULL, T, L, k, st + b * T, &c);
+        if (rc) return rc;
+        if (cost) cost[b] = c;
+        if (mse) mse[b] = mse_of(c, T);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Bitstream: pack and window decode  ([QTIP] "The trellis: a stateful codebook",    */
+/* "Tail-biting is worth its complexity" for the plain-trellis bit count)            */
+/* ------------------------------------------------------------------------------ */
+
+/* A plain trellis stream stores the start state (L bits) and then k new bits per
+ * later weight. */
+int64_t oracle_stream_bits(int L, int k, int T) { return (int64_t)L + (int64_t)(T - 1) * k; }
+int64_t oracle_stream_words(int L, int k, int T) { return (oracle_stream_bits(L, k, T) + 31) / 32; }
+
+/* Stream position p (0 = most significant bit of the stream) lives in word p / 32 at
+ * bit 31 - p % 32. */
+static void put_bit(uint32_t* words, int64_t p, uint32_t bit)
+{
+    if (bit) words[p / 32] |= 1u << (31 - (int)(p % 32));
+}
+static uint32_t get_bit(const uint32_t* words, int64_t p)
+{
+    return (words[p / 32] >> (31 - (int)(p % 32))) & 1u;
+}
+
+/* Pack one state sequence: the L bits of st[0] most significant first, then for each
+ * t >= 1 the k low bits of st[t] (the bits that entered the window).  Pad bits = 0. */
+int oracle_pack(const uint32_t* st, int T, int L, int k, uint32_t* words)
+{
+    if (!st || !words || !check_trellis(T, L, k)) return ORC_EINVAL;
+    int64_t nw = oracle_stream_words(L, k, T);
+    memset(words, 0, sizeof(uint32_t) * (size_t)nw);
+    for (int b = 0; b < L; ++b)
+        put_bit(words, b, (st[0] >> (L - 1 - b)) & 1u);
+    for (int t = 1; t < T; ++t)
+        for (int b = 0; b < k; ++b)
+            put_bit(words, (int64_t)L + (int64_t)(t - 1) * k + b, (st[t] >> (k - 1 - b)) & 1u);
+    return ORC_OK;
+}
+
+int oracle_pack_batch(const uint32_t* st, int64_t B, int T, int L, int k, uint32_t* words)
+{
+    int64_t nw = oracle_stream_words(L, k, T);
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_pack(st + b * T, T, L, k, words + b * nw);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* Window decode: weight t reads the L stream bits starting at position t*k (the
+ * window the page shifts out of the big-integer stream), and its value is the code
+ * of that window.  windows[] (may be NULL) receives the window integers. */
+int oracle_decode(const uint32_t* words, int T, int L, int k, const float* C,
+                  uint32_t* windows, float* recon)
+{
+    if (!words || !C || !check_trellis(T, L, k)) return ORC_EINVAL;
+    for (int t = 0; t < T; ++t) {
+        uint32_t win = 0;
+        for (int b = 0; b < L; ++b)
+            win = (win << 1) | get_bit(words, (int64_t)t * k + b);
+        if (windows) windows[t] = win;
+        if (recon) recon[t] = C[win];
+    }
+    return ORC_OK;
+}
+
+int oracle_decode_batch(const uint32_t* words, int64_t B, int T, int L, int k, const float* C,
+                        uint32_t* windows, float* recon)
+{
+    int64_t nw = oracle_stream_words(L, k, T);
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_decode(words + b * nw, T, L, k, C, windows ? windows + b * T : NULL,
+                               recon ? recon + b * T : NULL);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* Path cost of a reconstruction: the binary32 sum over t = 0, 1, ..., T-1 (in that
+ * order) of the step errors.  Dividing by T gives the per-sequence MSE. */
+float oracle_path_cost(const float* recon, const float* s, const float* w, int T)
+{
+    float acc = 0.0f;
+    for (int t = 0; t < T; ++t)
+        acc = acc + step_error(recon[t], s[t], w, t);
+    return acc;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* BCJR soft relaxation, binary64  ([BCJR] abstract)                                */
+/* ------------------------------------------------------------------------------ */
+
+/* Energy of state j at step t: the same weighted squared error as the search, but
+ * evaluated exactly in binary64 from the binary32 inputs. */
+static double energy64(const float* C, const float* s, const float* w, int t, uint32_t j)
+{
+    double d = (double)C[j] - (double)s[t];
+    double e = d * d;
+    if (w) e *= (double)w[t];
+    return e;
+}
+
+/* log(sum_i exp(x_i)) of n values, shifted by their maximum. */
+static double logsumexp(const double* x, int n)
+{
+    double m = -INFINITY;
+    for (int i = 0; i < n; ++i)
+        if (x[i] > m) m = x[i];
+    if (m == -INFINITY) return m;
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+        acc += exp(x[i] - m);
+    return m + log(acc);
+}
+
+/* Forward-backward over the plain bitshift trellis with a uniform start prior.
+ * Path weight exp(-E/tau), E = sum_t energy_t(state_t).
+ *   la_0(j) = -e_0(j)/tau;  la_t(j) = LSE_{i in pred(j)} la_{t-1}(i) - e_t(j)/tau
+ *   lb_{T-1}(i) = 0;        lb_t(i) = LSE_{j in succ(i)} (lb_{t+1}(j) - e_{t+1}(j)/tau)
+ *   log Z = LSE_j la_{T-1}(j);  gamma_t(j) = exp(la_t(j) + lb_t(j) - log Z)
+ *   soft_t = sum_j gamma_t(j) C_j / sum_j gamma_t(j)
+ * Successors of i are ((i << k) | b) mod 2^L for the 2^k values of b.
+ * Outputs soft[0..T) and *logz (natural log). */
+int oracle_bcjr(const float* C, const float* s, const float* w, int T, int L, int k,
+                double tau, double* soft, double* logz)
+{
+    if (!C || !s || !soft || !check_trellis(T, L, k) || !(tau > 0.0) || !isfinite(tau))
+        return ORC_EINVAL;
+    const uint32_t N = 1u << L;
+    const uint32_t K = 1u << k;
+    double* la = (double*)malloc(sizeof(double) * (size_t)T * N);
+    double* lb = (double*)malloc(sizeof(double) * N);
+    double* lb_next = (double*)malloc(sizeof(double) * N);
+    double* terms = (double*)malloc(sizeof(double) * (K > N ? K : N));
+    if (!la || !lb || !lb_next || !terms) {
+        free(la); free(lb); free(lb_next); free(terms);
+        return ORC_ENOMEM;
+    }
+
+    for (uint32_t j = 0; j < N; ++j)
+        la[j] = -energy64(C, s, w, 0, j) / tau;
+    for (int t = 1; t < T; ++t) {
+        const double* prev = la + (size_t)(t - 1) * N;
+        double* cur = la + (size_t)t * N;
+        for (uint32_t j = 0; j < N; ++j) {
+            for (uint32_t a = 0; a < K; ++a)
+                terms[a] = prev[(j >> k) | (a << (L - k))];
+            cur[j] = logsumexp(terms, (int)K) - energy64(C, s, w, t, j) / tau;
+        }
+    }
+    double lz = logsumexp(la + (size_t)(T - 1) * N, (int)N);
+    if (logz) *logz = lz;
+
+    for (uint32_t i = 0; i < N; ++i)
+        lb[i] = 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+        /* posterior at t */
+        const double* cur = la + (size_t)t * N;
+        double num = 0.0, den = 0.0;
+        for (uint32_t j = 0; j < N; ++j) {
+            double g = exp(cur[j] + lb[j] - lz);
+            num += g * (double)C[j];
+            den += g;
+        }
+        soft[t] = num / den;
+        if (t == 0) break;
+        /* lb_{t-1} from lb_t */
+        for (uint32_t i = 0; i < N; ++i) {
+            for (uint32_t b = 0; b < K; ++b) {
+                uint32_t j = ((i << k) | b) & (N - 1);
+                terms[b] = lb[j] - energy64(C, s, w, t, j) / tau;
+            }
+            lb_next[i] = logsumexp(terms, (int)K);
+        }
+        double* tmp = lb; lb = lb_next; lb_next = tmp;
+    }
+
+    free(la); free(lb); free(lb_next); free(terms);
+    return ORC_OK;
+}
+
+int oracle_bcjr_batch(const float* C, const float* s, const float* w, int64_t B, int T, int L,
+                      int k, double tau, double* soft, double* logz)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_bcjr(C, s + b * T, w ? w + b * T : NULL, T, L, k, tau, soft + b * T,
+                             logz ? logz + b : NULL);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* Min-sum forward-backward in binary64: best[t][j] = the least energy of any walk
+ * that is in state j at step t (exact-arithmetic counterpart of the Viterbi values).
+ * Used to find how far the best walk with a different value at step t lies above the
+ * optimum, which bounds how fast BCJR approaches the hard code as tau -> 0. */
+int oracle_minsum_marginals(const float* C, const float* s, const float* w, int T, int L, int k,
+                            double* best)
+{
+    if (!C || !s || !best || !check_trellis(T, L, k)) return ORC_EINVAL;
+    const uint32_t N = 1u << L;
+    const uint32_t K = 1u << k;
+    double* fa = (double*)malloc(sizeof(double) * (size_t)T * N);
+    double* fb = (double*)malloc(sizeof(double) * N);
+    double* fb_next = (double*)malloc(sizeof(double) * N);
+    if (!fa || !fb || !fb_next) {
+        free(fa); free(fb); free(fb_next);
+        return ORC_ENOMEM;
+    }
+    for (uint32_t j = 0; j < N; ++j)
+        fa[j] = energy64(C, s, w, 0, j);
+    for (int t = 1; t < T; ++t) {
+        const double* prev = fa + (size_t)(t - 1) * N;
+        double* cur = fa + (size_t)t * N;
+        for (uint32_t j = 0; j < N; ++j) {
+            double m = INFINITY;
+            for (uint32_t a = 0; a < K; ++a) {
+                double v = prev[(j >> k) | (a << (L - k))];
+                if (v < m) m = v;
+            }
+            cur[j] = m + energy64(C, s, w, t, j);
+        }
+    }
+    for (uint32_t i = 0; i < N; ++i)
+        fb[i] = 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+        for (uint32_t j = 0; j < N; ++j)
+            best[(size_t)t * N + j] = fa[(size_t)t * N + j] + fb[j];
+        if (t == 0) break;
+        for (uint32_t i = 0; i < N; ++i) {
+            double m = INFINITY;
+            for (uint32_t b = 0; b < K; ++b) {
+                uint32_t j = ((i << k) | b) & (N - 1);
+                double v = fb[j] + energy64(C, s, w, t, j);
+                if (v < m) m = v;
+            }
+            fb_next[i] = m;
+        }
+        double* tmp = fb; fb = fb_next; fb_next = tmp;
+    }
+    free(fa); free(fb); free(fb_next);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Brute force over every walk (tiny instances only)                                */
+/* ------------------------------------------------------------------------------ */
+
+/* Walk number n (0 <= n < 2^(L + k(T-1))) read as a stream of L + k(T-1) bits, most
+ * significant first: its first L bits are the start state, then k bits per step. */
+static void walk_states(uint64_t n, int T, int L, int k, uint32_t* st)
+{
+    int nbits = L + k * (T - 1);
+    uint32_t mask = (1u << L) - 1u;
+    st[0] = (uint32_t)(n >> (nbits - L)) & mask;
+    for (int t = 1; t < T; ++t) {
+        uint32_t branch = (uint32_t)(n >> (nbits - L - t * k)) & ((1u << k) - 1u);
+        st[t] = ((st[t - 1] << k) | branch) & mask;
+    }
+}
+
+/* Every walk's binary32 cost (sequential sum, same step error as the search).
+ * Returns the minimum cost, the number of walks attaining it, and among those the walk
+ * whose state sequence read from the last step backwards is smallest (st_T-1 first). */
+int oracle_brute_viterbi(const float* C, const float* s, const float* w, int T, int L, int k,
+                         float* best_cost, uint32_t* best_path, int64_t* n_optimal)
+{
+    if (!C || !s || !best_cost || !check_trellis(T, L, k)) return ORC_EINVAL;
+    int nbits = L + k * (T - 1);
+    if (nbits > 26) return ORC_EINVAL;
+    uint64_t nwalks = 1ull << nbits;
+    uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    uint32_t* cand = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    if (!st || !cand) { free(st); free(cand); return ORC_ENOMEM; }
+    float best = INFINITY;
+    int64_t count = 0;
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        walk_states(n, T, L, k, st);
+        float acc = 0.0f;
+        for (int t = 0; t < T; ++t)
+            acc = acc + step_error(C[st[t]], s[t], w, t);
+        int take = 0;
+        if (acc < best) {
+            best = acc;
+            count = 1;
+            take = 1;
+        } else if (acc == best) {
+            ++count;
+            /* reverse-lexicographic comparison: last state first */
+            for (int t = T - 1; t >= 0; --t) {
+                if (st[t] != cand[t]) { take = st[t] < cand[t]; break; }
+            }
+        }
+        if (take) memcpy(cand, st, sizeof(uint32_t) * T);
+    }
+    *best_cost = best;
+    if (best_path) memcpy(best_path, cand, sizeof(uint32_t) * T);
+    if (n_optimal) *n_optimal = count;
+    free(st); free(cand);
+    return ORC_OK;
+}
+
+/* Boltzmann expectation by explicit enumeration of every walk, binary64.
+ * soft[t] = sum_walks p(walk) C[state_t]; *logz = log sum_walks exp(-E/tau). */
+int oracle_brute_bcjr(const float* C, const float* s, const float* w, int T, int L, int k,
+                      double tau, double* soft, double* logz)
+{
+    if (!C || !s || !soft || !check_trellis(T, L, k) || !(tau > 0.0)) return ORC_EINVAL;
+    int nbits = L + k * (T - 1);
+    if (nbits > 22) return ORC_EINVAL;
+    uint64_t nwalks = 1ull << nbits;
+    uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    double* E = (double*)malloc(sizeof(double) * nwalks);
+    if (!st || !E) { free(st); free(E); return ORC_ENOMEM; }
+    double emin = INFINITY;
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        walk_states(n, T, L, k, st);
+        double e = 0.0;
+        for (int t = 0; t < T; ++t)
+            e += energy64(C, s, w, t, st[t]);
+        E[n] = e;
+        if (e < emin) emin = e;
+    }
+    double zsum = 0.0;
+    for (int t = 0; t < T; ++t)
+        soft[t] = 0.0;
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        double p = exp(-(E[n] - emin) / tau);
+        zsum += p;
+        walk_states(n, T, L, k, st);
+        for (int t = 0; t < T; ++t)
+            soft[t] += p * (double)C[st[t]];
+    }
+    for (int t = 0; t < T; ++t)
+        soft[t] /= zsum;
+    if (logz) *logz = -emin / tau + log(zsum);
+    free(st); free(E);
+    return ORC_OK;
+}
