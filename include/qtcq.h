@@ -1,0 +1,154 @@
+/*
+ * qtcq.h -- C ABI of the MI355X (gfx950) bitshift-trellis library: batched Viterbi
+ * encoding of weight sequences with computed codes, parallel window decode, and the
+ * BCJR soft relaxation.
+ *
+ * Sources, cited by page title and section:
+ *  [QTIP] "QTIP: Trellis-Coded Quantization Puts 2-Bit LLM Weights 10% Above the
+ *         Rate-Distortion Bound, and a Monotone Codebook Loses to Scalar Rounding"
+ *         (blog) -- "The trellis: a stateful codebook" (bitshift trellis, window
+ *         decode, Viterbi with shift-computed predecessors), "The codebook is
+ *         computed" (1MAD, 3INST), "Tail-biting is worth its complexity" (a plain
+ *         trellis stores its L-k start bits).
+ *  [XOR]  "XOR-Trellis -- Trellis-coded quantization vs VQ codebooks -- What does it
+ *         mean?" (explainer) -- "Cliff edges: weighting errors instead of rotating
+ *         them" (per-weight error weights in the path cost), "The sign at each junction
+ *         has to be cheap" (3INST ends with an FP16 add).
+ *  [BCJR] "BCJR-QAT: A Differentiable Relaxation of Trellis-Coded Weight
+ *         Quantization" (abstract) -- forward-backward at temperature, soft codeword =
+ *         Boltzmann expectation over trellis paths.
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *    row-major and contiguous; [B][T] means sequence b's element t at b*T + t.
+ *  - The caller owns every buffer.  The library allocates no device memory and keeps
+ *    no mutable global state; calls on different streams may run concurrently as long
+ *    as their output and workspace buffers do not overlap.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    enqueued on it and the call returns without synchronising; outputs are valid
+ *    once the stream has reached that point.
+ *  - Arguments are validated before anything is launched; a non-OK status means
+ *    nothing was enqueued (except QTCQ_ERR_DEVICE, which reports a failed launch).
+ *    No C++ exception crosses this ABI.
+ *  - Supported on the GPU: k = 2, L in {6, 8, 10, 12, 14, 16}, 1 <= T <= 4096.
+ *    Inputs must be finite and weights > 0; other inputs give unspecified (but
+ *    memory-safe) results.
+ *  - Results are bit-deterministic: the same inputs give the same bits on every run
+ *    and for every batch split.
+ *
+ * Bitstream layout (plain, non-tail-biting trellis [QTIP]): a sequence's stream holds
+ * nbits = L + k*(T-1) bits -- the L bits of the start state, then the k newest bits of
+ * each later state -- most significant first.  Stream bit p is bit 31 - (p mod 32) of
+ * 32-bit word p / 32; each sequence owns qtcq_bitstream_words(L, k, T) words and the
+ * bits after nbits are zero.  Weight t reads the window of stream bits [t*k, t*k + L)
+ * as an L-bit integer (its trellis state) and decodes to code(window).
+ */
+#ifndef QTCQ_H
+#define QTCQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QTCQ_OK = 0,
+    QTCQ_ERR_INVALID_ARG = 1, /* NULL required pointer, B < 0, T out of range, tau <= 0 */
+    QTCQ_ERR_UNSUPPORTED = 2, /* (L, k) or code id not built for the GPU */
+    QTCQ_ERR_WORKSPACE = 3,   /* workspace smaller than one sequence needs, or misaligned */
+    QTCQ_ERR_DEVICE = 4       /* a kernel launch failed (hipGetLastError) */
+} qtcq_status;
+
+/* Computed codes [QTIP "The codebook is computed"].  Both start from the LCG
+ * u = 34038481 * x + 76625530 (mod 2^32) of the L-bit state x.
+ *  1MAD : value = float( (S - 510) / 147.8 ) with S the sum of u's four bytes and the
+ *         division done in binary64 (one rounding to binary32 at the end).
+ *  3INST: v = (u & 0x8FFF8FFF) ^ 0x3B603B60 (sign, 2 low exponent bits and mantissa of
+ *         each half XORed into fp16(0.922)); h = fp16 sum of the two halves (RNE);
+ *         value = float( h / 1.244 ) in binary64 -- unit variance. */
+typedef enum { QTCQ_CODE_1MAD = 0, QTCQ_CODE_3INST = 1 } qtcq_code_id;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qtcq_status_string(qtcq_status s);
+
+/* Words per sequence of the bitstream: ceil((L + k*(T-1)) / 32).  17 at (16, 2, 256).
+ * Returns -1 for arguments outside 1 <= k <= L <= 32, T >= 1. */
+int64_t qtcq_bitstream_words(int L, int k, int T);
+
+/* Workspace bytes qtcq_viterbi_encode needs to encode `B` sequences in one pass
+ * (backpointers: 2 bits per trellis group per step, plus a final state and cost per
+ * sequence).  Any smaller workspace that still holds one sequence works: the batch is
+ * then encoded in chunks.  Returns 0 for unsupported arguments. */
+size_t qtcq_encode_workspace_bytes(int64_t B, int T, int L, int k);
+
+/* Workspace bytes qtcq_bcjr_soft needs to process `B` sequences in one pass (the
+ * forward messages of every step).  Smaller workspaces are used in chunks as above.
+ * Returns 0 for unsupported arguments. */
+size_t qtcq_bcjr_workspace_bytes(int64_t B, int T, int L, int k);
+
+/* Code value of every L-bit state [QTIP "The codebook is computed"], evaluated by the
+ * same device code the kernels use.  out: [2^L] float32 (device).  L in 1..24. */
+qtcq_status qtcq_code_table(int code, int L, float* out, void* stream);
+
+/* Viterbi encoding [QTIP "The trellis: a stateful codebook"; XOR "Cliff edges"].
+ * For each sequence b, finds the walk st[0..T) through the bitshift trellis (state j
+ * may follow state i iff the top L-k bits of j equal the bottom L-k bits of i) that
+ * minimises the binary32 path cost
+ *     cost = (((e_0 + e_1) + e_2) + ... + e_{T-1}),
+ *     e_t  = fl( fl(code(st[t]) - seq[b][t])^2 )          (unweighted)
+ *     e_t  = fl( err_w[b][t] * fl( fl(code(st[t]) - seq[b][t])^2 ) )   (weighted)
+ * with every operation rounded separately (no fused multiply-add).  Ties go to the
+ * lowest-numbered predecessor at each step and to the lowest-numbered final state.
+ * The start state is free (stored in the stream).
+ *   seq       [B][T] float32 targets (in)
+ *   err_w     [B][T] float32 positive error weights (in), or NULL for unweighted
+ *   B         number of sequences (>= 0; 0 is a no-op)
+ *   code      qtcq_code_id
+ *   bits      [B][qtcq_bitstream_words(L,k,T)] uint32 (out) -- the layout above
+ *   mse       [B] float32 (out) = cost / T, or NULL
+ *   states    [B][T] uint32 (out) = st, or NULL
+ *   workspace device scratch, 16-byte aligned, `workspace_bytes` long; its contents
+ *             are overwritten and meaningless after the call.
+ * Errors: QTCQ_ERR_INVALID_ARG, QTCQ_ERR_UNSUPPORTED, QTCQ_ERR_WORKSPACE (workspace
+ * NULL, misaligned or below qtcq_encode_workspace_bytes(1, T, L, k)), QTCQ_ERR_DEVICE. */
+qtcq_status qtcq_viterbi_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
+                                int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Window decode [QTIP "The trellis: a stateful codebook"]: recon[b][t] = code(window
+ * of stream bits [t*k, t*k + L)) -- every weight independently.
+ *   bits   [B][qtcq_bitstream_words(L,k,T)] uint32 (in)
+ *   recon  [B][T] float32 (out), or NULL (then only mse is produced)
+ *   seq    [B][T] float32 targets (in), required when mse != NULL
+ *   err_w  [B][T] float32 weights (in) or NULL
+ *   mse    [B] float32 (out) or NULL: the binary32 path cost of the reconstruction,
+ *          summed in t order exactly as qtcq_viterbi_encode defines it, divided by T.
+ *          Decoding an encoder's output with the same seq/err_w reproduces its mse
+ *          bit for bit.
+ * Errors: QTCQ_ERR_INVALID_ARG (also: mse requested without seq, or neither recon nor
+ * mse requested), QTCQ_ERR_UNSUPPORTED, QTCQ_ERR_DEVICE. */
+qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+                        float* recon, const float* seq, const float* err_w, float* mse,
+                        void* stream);
+
+/* BCJR soft relaxation [BCJR abstract].  Each walk's energy E is its path cost as in
+ * qtcq_viterbi_encode (weighted if err_w != NULL) and its weight exp(-E / temperature);
+ * the start state is uniform.  Outputs, per sequence:
+ *   soft  [B][T] float32: soft[b][t] = E_Boltzmann[ code(st[t]) ], the posterior mean
+ *         of the reconstructed value at step t (forward-backward, log domain, fp32);
+ *   log_z [B] float32 (or NULL): natural log of sum over walks of exp(-E / temperature).
+ * temperature: finite, > 0.  As it tends to 0 soft tends to the Viterbi code.
+ * workspace: 16-byte aligned, >= qtcq_bcjr_workspace_bytes(1, T, L, k); larger
+ * workspaces let more sequences run per pass.
+ * Errors: as qtcq_viterbi_encode. */
+qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
+                           int code, float temperature, float* soft, float* log_z,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QTCQ_H */

@@ -1,0 +1,129 @@
+"""The C-ABI library loads on the host, exports every entry point include/qtcq.h
+declares, and rejects bad arguments before launching anything.  No GPU needed: every
+call here returns from host-side validation (or is a pure size query).
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def nat():
+    from trellis_coded_weight_amd import _native
+    return _native
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "qtcq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qtcq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(nat):
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    for name in syms:
+        assert hasattr(nat._lib, name), name
+    assert set(syms) == set(nat.EXPORTED)
+
+
+def test_status_strings(nat):
+    for s in range(5):
+        assert nat.qtcq_status_string(s)
+    assert nat.qtcq_status_string(99) == "unknown status"
+
+
+def test_bitstream_words(nat):
+    assert nat.qtcq_bitstream_words(16, 2, 256) == 17
+    assert nat.qtcq_bitstream_words(16, 2, 1) == 1
+    assert nat.qtcq_bitstream_words(6, 2, 14) == 1       # 6 + 26 = 32 bits
+    assert nat.qtcq_bitstream_words(6, 2, 15) == 2
+    assert nat.qtcq_bitstream_words(16, 0, 256) == -1
+    assert nat.qtcq_bitstream_words(16, 2, 0) == -1
+
+
+def test_workspace_sizes(nat):
+    per = nat.qtcq_encode_workspace_bytes(1, 256, 16, 2)
+    assert per == 255 * 1024 * 4 + 8                      # 2 bits x 16384 groups x 255 steps
+    assert nat.qtcq_encode_workspace_bytes(10, 256, 16, 2) == 10 * per
+    assert nat.qtcq_encode_workspace_bytes(1, 256, 7, 2) == 0
+    assert nat.qtcq_encode_workspace_bytes(1, 256, 16, 3) == 0
+    assert nat.qtcq_encode_workspace_bytes(1, 5000, 16, 2) == 0
+    bper = nat.qtcq_bcjr_workspace_bytes(1, 256, 16, 2)
+    assert bper >= 255 * 16384 * 4
+    assert nat.qtcq_bcjr_workspace_bytes(3, 256, 16, 2) == 3 * bper
+
+
+FAKE = 1 << 20   # a non-NULL pointer value; never dereferenced by validation paths
+
+
+def test_encode_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_viterbi_encode", *a)
+    ws = nat.qtcq_encode_workspace_bytes(1, 256, 16, 2)
+    ok_args = [FAKE, None, 4, 256, 16, 2, 0, FAKE, FAKE, None, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(ok_args)
+        names = ["seq", "w", "B", "T", "L", "k", "code", "bits", "mse", "states", "ws", "wsb", "stream"]
+        for kk, v in kw.items():
+            a[names.index(kk)] = v
+        return st(*a)
+
+    assert call(B=-1) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(T=0) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(T=4097) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(L=18) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(k=1) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(code=2) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(B=0, seq=None, bits=None, ws=None) == nat.QTCQ_OK
+    assert call(seq=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(bits=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(ws=None) == nat.QTCQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == nat.QTCQ_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == nat.QTCQ_ERR_WORKSPACE
+
+
+def test_decode_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_decode", *a)
+    # bits, B, T, L, k, code, recon, seq, w, mse, stream
+    assert st(FAKE, 4, 256, 16, 2, 0, None, None, None, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, 4, 256, 16, 2, 0, None, None, None, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, 4, 256, 12, 3, 0, FAKE, None, None, None, None) == nat.QTCQ_ERR_UNSUPPORTED
+    assert st(FAKE, 4, 0, 16, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(None, 4, 256, 16, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(None, 0, 256, 16, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_OK
+
+
+def test_bcjr_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_bcjr_soft", *a)
+    ws = nat.qtcq_bcjr_workspace_bytes(1, 256, 16, 2)
+    # seq, w, B, T, L, k, code, tau, soft, logz, ws, wsb, stream
+    assert st(FAKE, None, 4, 256, 16, 2, 0, 0.0, FAKE, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, None, 4, 256, 16, 2, 0, -1.0, FAKE, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, None, 4, 256, 16, 2, 0, float("inf"), FAKE, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, None, 4, 256, 16, 2, 0, float("nan"), FAKE, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, None, 4, 256, 9, 2, 0, 1.0, FAKE, None, FAKE, ws, None) == nat.QTCQ_ERR_UNSUPPORTED
+    assert st(FAKE, None, 4, 256, 16, 2, 0, 1.0, None, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert st(FAKE, None, 4, 256, 16, 2, 0, 1.0, FAKE, None, FAKE, ws - 1, None) == nat.QTCQ_ERR_WORKSPACE
+    assert st(None, None, 0, 256, 16, 2, 0, 1.0, None, None, None, 0, None) == nat.QTCQ_OK
+
+
+def test_code_table_validation(nat):
+    assert nat.raw_status("qtcq_code_table", 0, 16, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert nat.raw_status("qtcq_code_table", 0, 25, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert nat.raw_status("qtcq_code_table", 5, 16, FAKE, None) == nat.QTCQ_ERR_UNSUPPORTED
+
+
+def test_product_does_not_import_oracle():
+    # the HIP path's package never references the oracle
+    pkg = os.path.join(ROOT, "trellis_coded_weight_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "qtcq_oracle" not in text, f

@@ -1,0 +1,123 @@
+"""ctypes binding of the C ABI in include/qtcq.h -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes the same
+arguments, with device pointers passed as Python ints (e.g. ``tensor.data_ptr()``)
+and the stream as an int handle (``torch.cuda.current_stream().cuda_stream``) or 0.
+A non-OK status raises :class:`QtcqError`.  The library must have been built
+(``trellis_coded_weight_amd.build.build_native()``); if it is missing this module
+raises at import time -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqtcq.so")
+
+QTCQ_OK = 0
+QTCQ_ERR_INVALID_ARG = 1
+QTCQ_ERR_UNSUPPORTED = 2
+QTCQ_ERR_WORKSPACE = 3
+QTCQ_ERR_DEVICE = 4
+
+QTCQ_CODE_1MAD = 0
+QTCQ_CODE_3INST = 1
+
+
+class QtcqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, qtcq_status_string(status), status))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libqtcq.so is not built (expected at %s); run "
+                      "trellis_coded_weight_amd.build.build_native()" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "qtcq_status_string": (ctypes.c_char_p, [_int]),
+    "qtcq_bitstream_words": (_i64, [_int, _int, _int]),
+    "qtcq_encode_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
+    "qtcq_bcjr_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
+    "qtcq_code_table": (_int, [_int, _int, _vp, _vp]),
+    "qtcq_viterbi_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+                                   _sz, _vp]),
+    "qtcq_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "qtcq_bcjr_soft": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp,
+                              _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _ptr(p):
+    return None if (p is None or p == 0) else ctypes.c_void_p(int(p))
+
+
+def _check(status: int, where: str) -> None:
+    if status != QTCQ_OK:
+        raise QtcqError(status, where)
+
+
+def qtcq_status_string(status: int) -> str:
+    return _lib.qtcq_status_string(status).decode()
+
+
+def qtcq_bitstream_words(L: int, k: int, T: int) -> int:
+    return _lib.qtcq_bitstream_words(L, k, T)
+
+
+def qtcq_encode_workspace_bytes(B: int, T: int, L: int, k: int) -> int:
+    return _lib.qtcq_encode_workspace_bytes(B, T, L, k)
+
+
+def qtcq_bcjr_workspace_bytes(B: int, T: int, L: int, k: int) -> int:
+    return _lib.qtcq_bcjr_workspace_bytes(B, T, L, k)
+
+
+def qtcq_code_table(code: int, L: int, out: int, stream: int = 0) -> None:
+    _check(_lib.qtcq_code_table(code, L, _ptr(out), _ptr(stream)), "qtcq_code_table")
+
+
+def qtcq_viterbi_encode(seq: int, err_w, B: int, T: int, L: int, k: int, code: int, bits: int,
+                        mse, states, workspace: int, workspace_bytes: int,
+                        stream: int = 0) -> None:
+    _check(_lib.qtcq_viterbi_encode(_ptr(seq), _ptr(err_w), B, T, L, k, code, _ptr(bits),
+                                    _ptr(mse), _ptr(states), _ptr(workspace), workspace_bytes,
+                                    _ptr(stream)), "qtcq_viterbi_encode")
+
+
+def qtcq_decode(bits: int, B: int, T: int, L: int, k: int, code: int, recon, seq, err_w, mse,
+                stream: int = 0) -> None:
+    _check(_lib.qtcq_decode(_ptr(bits), B, T, L, k, code, _ptr(recon), _ptr(seq), _ptr(err_w),
+                            _ptr(mse), _ptr(stream)), "qtcq_decode")
+
+
+def qtcq_bcjr_soft(seq: int, err_w, B: int, T: int, L: int, k: int, code: int,
+                   temperature: float, soft: int, log_z, workspace: int, workspace_bytes: int,
+                   stream: int = 0) -> None:
+    _check(_lib.qtcq_bcjr_soft(_ptr(seq), _ptr(err_w), B, T, L, k, code, float(temperature),
+                               _ptr(soft), _ptr(log_z), _ptr(workspace), workspace_bytes,
+                               _ptr(stream)), "qtcq_bcjr_soft")
+
+
+def raw_status(name: str, *args) -> int:
+    """Call an entry point and return its status without raising (for argument-validation
+    tests).  Pointer arguments are ints or None."""
+    fn = getattr(_lib, name)
+    conv = []
+    for a, t in zip(args, _SIGS[name][1]):
+        conv.append(_ptr(a) if t is _vp else a)
+    return fn(*conv)

@@ -1,0 +1,106 @@
+"""Torch-facing convenience layer over the C ABI: allocates outputs and workspaces as
+CUDA (HIP) tensors and calls the entry points on the current stream.  Only argument
+marshalling happens here; every step of the path runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _native as nat
+
+CODES = {"1mad": nat.QTCQ_CODE_1MAD, "3inst": nat.QTCQ_CODE_3INST}
+
+
+def _code(code) -> int:
+    return CODES[code] if isinstance(code, str) else int(code)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_f32(x: torch.Tensor, name: str) -> torch.Tensor:
+    if not (x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2):
+        raise ValueError("%s must be a contiguous 2-D float32 device tensor" % name)
+    return x
+
+
+def bitstream_words(L: int = 16, k: int = 2, T: int = 256) -> int:
+    return nat.qtcq_bitstream_words(L, k, T)
+
+
+def code_table(code="1mad", L: int = 16) -> torch.Tensor:
+    out = torch.empty(1 << L, dtype=torch.float32, device="cuda")
+    nat.qtcq_code_table(_code(code), L, out.data_ptr(), _stream())
+    return out
+
+
+def encode_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
+                     max_bytes: int | None = None) -> torch.Tensor:
+    need = nat.qtcq_encode_workspace_bytes(B, T, L, k)
+    if max_bytes is not None:
+        per = nat.qtcq_encode_workspace_bytes(1, T, L, k)
+        need = max(per, min(need, max_bytes // per * per))
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def bcjr_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
+                   max_bytes: int | None = None) -> torch.Tensor:
+    need = nat.qtcq_bcjr_workspace_bytes(B, T, L, k)
+    if max_bytes is not None:
+        per = nat.qtcq_bcjr_workspace_bytes(1, T, L, k)
+        need = max(per, min(need, max_bytes // per * per))
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16, k: int = 2,
+           code="1mad", want_states: bool = False, workspace: torch.Tensor | None = None):
+    """Viterbi-encode [B][T] targets.  Returns (bits [B][W] int32 view of uint32 words,
+    mse [B] float32, states [B][T] int32 view of uint32 or None)."""
+    _dev_f32(seq, "seq")
+    B, T = seq.shape
+    if weights is not None:
+        _dev_f32(weights, "weights")
+        if weights.shape != seq.shape:
+            raise ValueError("weights must have the shape of seq")
+    W = nat.qtcq_bitstream_words(L, k, T)
+    bits = torch.empty((B, W), dtype=torch.int32, device=seq.device)
+    mse = torch.empty(B, dtype=torch.float32, device=seq.device)
+    states = torch.empty((B, T), dtype=torch.int32, device=seq.device) if want_states else None
+    if workspace is None:
+        workspace = encode_workspace(B, T, L, k)
+    nat.qtcq_viterbi_encode(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T,
+                            L, k, _code(code), bits.data_ptr(), mse.data_ptr(),
+                            None if states is None else states.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), _stream())
+    return bits, mse, states
+
+
+def decode(bits: torch.Tensor, T: int, L: int = 16, k: int = 2, code="1mad",
+           seq: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+           want_recon: bool = True, want_mse: bool = False):
+    """Window-decode [B][W] streams.  Returns (recon [B][T] or None, mse [B] or None)."""
+    B = bits.shape[0]
+    recon = torch.empty((B, T), dtype=torch.float32, device=bits.device) if want_recon else None
+    mse = torch.empty(B, dtype=torch.float32, device=bits.device) if want_mse else None
+    nat.qtcq_decode(bits.data_ptr(), B, T, L, k, _code(code),
+                    None if recon is None else recon.data_ptr(),
+                    None if seq is None else seq.data_ptr(),
+                    None if weights is None else weights.data_ptr(),
+                    None if mse is None else mse.data_ptr(), _stream())
+    return recon, mse
+
+
+def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | None = None,
+              L: int = 16, k: int = 2, code="1mad", workspace: torch.Tensor | None = None):
+    """BCJR soft codewords.  Returns (soft [B][T] float32, log_z [B] float32)."""
+    _dev_f32(seq, "seq")
+    B, T = seq.shape
+    soft = torch.empty((B, T), dtype=torch.float32, device=seq.device)
+    logz = torch.empty(B, dtype=torch.float32, device=seq.device)
+    if workspace is None:
+        workspace = bcjr_workspace(B, T, L, k, max_bytes=8 << 30)
+    nat.qtcq_bcjr_soft(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
+                       _code(code), temperature, soft.data_ptr(), logz.data_ptr(),
+                       workspace.data_ptr(), workspace.numel(), _stream())
+    return soft, logz

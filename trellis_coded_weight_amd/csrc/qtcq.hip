@@ -1,0 +1,292 @@
+// qtcq.hip -- host side of the C ABI declared in include/qtcq.h: argument validation,
+// workspace sizing, batch chunking and kernel launches on the caller's stream.
+// Everything the path computes runs in the kernels included below.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qtcq.h"
+#include "codes.hpp"
+#include "viterbi.hpp"
+#include "decode.hpp"
+#include "bcjr.hpp"
+
+namespace {
+
+using namespace qtcq;
+
+constexpr int kMaxT = 4096;
+
+bool supported_trellis(int L, int k)
+{
+    return k == 2 && L >= 6 && L <= 16 && (L % 2) == 0;
+}
+
+bool valid_code(int code) { return code == QTCQ_CODE_1MAD || code == QTCQ_CODE_3INST; }
+
+int64_t stream_words(int L, int k, int T)
+{
+    return ((int64_t)L + (int64_t)k * (T - 1) + 31) / 32;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qtcq_status launch_status()
+{
+    return hipGetLastError() == hipSuccess ? QTCQ_OK : QTCQ_ERR_DEVICE;
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+// ---- encode ------------------------------------------------------------------------
+
+size_t encode_bytes_per_seq(int T, int L)
+{
+    // backpointer words per step = 2^(L-6); final state + final cost
+    const size_t words = (size_t)(T - 1) * ((size_t)1 << (L - 6));
+    return words * 4 + 8;
+}
+
+template <int L, int CODE, bool W>
+qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n, int T,
+                         uint32_t* bits, float* mse, uint32_t* states, char* ws, hipStream_t st)
+{
+    using Tr = Trellis<L>;
+    uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
+    float* fin_cost = reinterpret_cast<float*>(fin + n);
+    hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0, st,
+                       seq, w, T, b0, bp, fin, fin_cost, mse);
+    qtcq_status rc = launch_status();
+    if (rc != QTCQ_OK) return rc;
+    const int Wd = (int)stream_words(L, 2, T);
+    hipLaunchKernelGGL((viterbi_traceback<L>), dim3(blocks_for(n, 256)), dim3(256), 0, st,
+                       bp, fin, T, n, b0, Wd, bits, states);
+    return launch_status();
+}
+
+template <int L, int CODE, bool W>
+qtcq_status encode_all(const float* seq, const float* w, int64_t B, int T, uint32_t* bits,
+                       float* mse, uint32_t* states, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t per_chunk = (int64_t)(ws_bytes / encode_bytes_per_seq(T, L));
+    for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
+        const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
+        qtcq_status rc = encode_chunk<L, CODE, W>(seq, w, b0, n, T, bits, mse, states,
+                                                  static_cast<char*>(ws), st);
+        if (rc != QTCQ_OK) return rc;
+    }
+    return QTCQ_OK;
+}
+
+template <int L>
+qtcq_status encode_dispatch_code(int code, bool weighted, const float* seq, const float* w,
+                                 int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
+                                 void* ws, size_t wsb, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return weighted ? encode_all<L, kCode1Mad, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
+                        : encode_all<L, kCode1Mad, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
+    return weighted ? encode_all<L, kCode3Inst, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
+                    : encode_all<L, kCode3Inst, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
+}
+
+// ---- decode ------------------------------------------------------------------------
+
+template <int L, int CODE>
+qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, const float* seq,
+                        const float* w, float* mse, hipStream_t st)
+{
+    const int Wd = (int)stream_words(L, 2, T);
+    if (recon) {
+        const int64_t total = B * T;
+        hipLaunchKernelGGL((window_decode<L, CODE>), dim3(blocks_for(total, 256)), dim3(256), 0, st,
+                           bits, total, T, Wd, recon);
+        qtcq_status rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+    }
+    if (mse) {
+        if (w)
+            hipLaunchKernelGGL((decode_path_mse<L, CODE, true>), dim3(blocks_for(B, 256)), dim3(256),
+                               0, st, bits, seq, w, B, T, Wd, mse);
+        else
+            hipLaunchKernelGGL((decode_path_mse<L, CODE, false>), dim3(blocks_for(B, 256)), dim3(256),
+                               0, st, bits, seq, w, B, T, Wd, mse);
+        return launch_status();
+    }
+    return QTCQ_OK;
+}
+
+template <int L>
+qtcq_status decode_dispatch_code(int code, const uint32_t* bits, int64_t B, int T, float* recon,
+                                 const float* seq, const float* w, float* mse, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD) return decode_impl<L, kCode1Mad>(bits, B, T, recon, seq, w, mse, st);
+    return decode_impl<L, kCode3Inst>(bits, B, T, recon, seq, w, mse, st);
+}
+
+// ---- bcjr --------------------------------------------------------------------------
+
+template <int L, int CODE, bool W>
+qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float temperature,
+                     float* soft, float* log_z, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    using Tr = Trellis<L>;
+    const size_t per = BcjrLayout<L>::bytes_per_seq(T);
+    const int64_t per_chunk = (int64_t)(ws_bytes / per);
+    // kappa = log2(e) / tau; code values and targets are scaled by sqrt(kappa)
+    const double kappa = 1.4426950408889634074 / (double)temperature;
+    const float sk = (float)__builtin_sqrt(kappa);
+    const float inv_sk = (float)(1.0 / __builtin_sqrt(kappa));
+    char* wsc = static_cast<char*>(ws);
+    for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
+        const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
+        hipLaunchKernelGGL((bcjr_sweep<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0, st,
+                           seq, w, T, b0, sk, wsc);
+        qtcq_status rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+        hipLaunchKernelGGL((bcjr_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
+                           wsc, T, n, b0, inv_sk, soft, log_z);
+        rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+    }
+    return QTCQ_OK;
+}
+
+template <int L>
+qtcq_status bcjr_dispatch_code(int code, bool weighted, const float* seq, const float* w,
+                               int64_t B, int T, float temperature, float* soft, float* log_z,
+                               void* ws, size_t wsb, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return weighted ? bcjr_all<L, kCode1Mad, true>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st)
+                        : bcjr_all<L, kCode1Mad, false>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st);
+    return weighted ? bcjr_all<L, kCode3Inst, true>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st)
+                    : bcjr_all<L, kCode3Inst, false>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st);
+}
+
+// L dispatch: instantiate every supported trellis size.
+template <template <int> class F, typename... Args>
+qtcq_status by_L(int L, Args&&... args)
+{
+    switch (L) {
+    case 6: return F<6>::run(args...);
+    case 8: return F<8>::run(args...);
+    case 10: return F<10>::run(args...);
+    case 12: return F<12>::run(args...);
+    case 14: return F<14>::run(args...);
+    case 16: return F<16>::run(args...);
+    default: return QTCQ_ERR_UNSUPPORTED;
+    }
+}
+
+template <int L>
+struct EncodeF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return encode_dispatch_code<L>(a...); }
+};
+template <int L>
+struct DecodeF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return decode_dispatch_code<L>(a...); }
+};
+template <int L>
+struct BcjrF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return bcjr_dispatch_code<L>(a...); }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* qtcq_status_string(qtcq_status s)
+{
+    switch (s) {
+    case QTCQ_OK: return "ok";
+    case QTCQ_ERR_INVALID_ARG: return "invalid argument";
+    case QTCQ_ERR_UNSUPPORTED: return "unsupported trellis or code";
+    case QTCQ_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case QTCQ_ERR_DEVICE: return "device launch failed";
+    }
+    return "unknown status";
+}
+
+int64_t qtcq_bitstream_words(int L, int k, int T)
+{
+    if (k < 1 || L < k || L > 32 || T < 1) return -1;
+    return stream_words(L, k, T);
+}
+
+size_t qtcq_encode_workspace_bytes(int64_t B, int T, int L, int k)
+{
+    if (!supported_trellis(L, k) || T < 1 || T > kMaxT || B < 0) return 0;
+    return (size_t)(B > 0 ? B : 1) * encode_bytes_per_seq(T, L);
+}
+
+size_t qtcq_bcjr_workspace_bytes(int64_t B, int T, int L, int k)
+{
+    if (!supported_trellis(L, k) || T < 1 || T > kMaxT || B < 0) return 0;
+    return (size_t)(B > 0 ? B : 1) * bcjr_bytes_per_seq(T, L);
+}
+
+qtcq_status qtcq_code_table(int code, int L, float* out, void* stream)
+{
+    if (!out || L < 1 || L > 24) return QTCQ_ERR_INVALID_ARG;
+    if (!valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    const int64_t n = (int64_t)1 << L;
+    if (code == QTCQ_CODE_1MAD)
+        hipLaunchKernelGGL((code_table_kernel<kCode1Mad>), dim3(blocks_for(n, 256)), dim3(256), 0,
+                           as_stream(stream), out, n);
+    else
+        hipLaunchKernelGGL((code_table_kernel<kCode3Inst>), dim3(blocks_for(n, 256)), dim3(256), 0,
+                           as_stream(stream), out, n);
+    return launch_status();
+}
+
+qtcq_status qtcq_viterbi_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
+                                int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (B == 0) return QTCQ_OK;
+    if (!seq || !bits) return QTCQ_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < encode_bytes_per_seq(T, L))
+        return QTCQ_ERR_WORKSPACE;
+    return by_L<EncodeF>(L, code, err_w != nullptr, seq, err_w, B, T, bits, mse, states, workspace,
+                         workspace_bytes, as_stream(stream));
+}
+
+qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+                        float* recon, const float* seq, const float* err_w, float* mse,
+                        void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (!recon && !mse) return QTCQ_ERR_INVALID_ARG;
+    if (mse && !seq) return QTCQ_ERR_INVALID_ARG;
+    if (B == 0) return QTCQ_OK;
+    if (!bits) return QTCQ_ERR_INVALID_ARG;
+    return by_L<DecodeF>(L, code, bits, B, T, recon, seq, err_w, mse, as_stream(stream));
+}
+
+qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
+                           int code, float temperature, float* soft, float* log_z,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!(temperature > 0.0f) || !__builtin_isfinite(temperature)) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (B == 0) return QTCQ_OK;
+    if (!seq || !soft) return QTCQ_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < bcjr_bytes_per_seq(T, L))
+        return QTCQ_ERR_WORKSPACE;
+    return by_L<BcjrF>(L, code, err_w != nullptr, seq, err_w, B, T, temperature, soft, log_z,
+                       workspace, workspace_bytes, as_stream(stream));
+}
+
+}  // extern "C"
