@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the bitshift-trellis hot path on one MI355X.
+
+A step = one pass of the path over one 4096x4096 weight matrix (65,536 sequences x
+T = 256 i.i.d. N(0,1) float32 targets, L = 16, k = 2, 1MAD code): Viterbi encode
+(forward ACS + traceback/pack) and parallel window decode with the round-trip MSE.
+Inputs are resident in HBM before timing starts.  Prints ONE JSON line.
+
+Extra objects on the line:
+  roofline      -- the dominant kernel (the ACS forward pass) against the VALU peak,
+                   from algorithmic ops / HIP-event-timed duration of the encode call
+  cpu_baseline  -- the CPU oracle on a bounded sample, on this host's cores
+  bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
+  decode        -- the decode kernels' own time and algorithmic HBM bytes
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published figures
+PEAK_HBM_GBS = 8000.0
+CUS, LANES_PER_CU, CLOCK_GHZ = 256, 64, 2.4
+PEAK_VALU_TOPS = CUS * LANES_PER_CU * CLOCK_GHZ / 1000.0   # 39.32 T lane-ops/s (no packed math)
+
+L, K, T = 16, 2, 256
+N_STATES = 1 << L
+N_GROUPS = N_STATES >> K
+
+
+def acs_ops_per_sequence(T: int, weighted: bool = False) -> int:
+    """Algorithmic VALU work of the Viterbi forward pass for one sequence: per step
+    t = 1..T-1 every state's cost is rebuilt (sub, square[, weight], add) and every
+    group takes a 4-way minimum (3 compares); the last step rebuilds all costs once more
+    and takes the argmin over 2^L states (2^L - 1 compares)."""
+    per_state = 4 if weighted else 3
+    per_step = N_STATES * per_state + N_GROUPS * 3
+    final = N_STATES * per_state + (N_STATES - 1)
+    return (T - 1) * per_step + final
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
+    ap.add_argument("--cpu-seqs", type=int, default=48)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are "
+              "independent; see the design notes on sharding)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from trellis_coded_weight_amd import api, inputs
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    name = "enc4096x4096_1mad"
+    s_host, _, code = inputs.workload(name)
+    B = s_host.shape[0]
+    seq = torch.from_numpy(s_host).to(dev)
+    W = api.bitstream_words(L, K, T)
+    bits = torch.empty((B, W), dtype=torch.int32, device=dev)
+    mse = torch.empty(B, dtype=torch.float32, device=dev)
+    recon = torch.empty((B, T), dtype=torch.float32, device=dev)
+    mse_rt = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = api.encode_workspace(B, T, L, K, max_bytes=64 << 30)
+
+    from trellis_coded_weight_amd import _native as nat
+    sptr = stream.cuda_stream
+
+    def encode():
+        nat.qtcq_viterbi_encode(seq.data_ptr(), None, B, T, L, K, nat.QTCQ_CODE_1MAD,
+                                bits.data_ptr(), mse.data_ptr(), None, ws.data_ptr(),
+                                ws.numel(), sptr)
+
+    def decode():
+        nat.qtcq_decode(bits.data_ptr(), B, T, L, K, nat.QTCQ_CODE_1MAD, recon.data_ptr(),
+                        seq.data_ptr(), None, mse_rt.data_ptr(), sptr)
+
+    for _ in range(args.warmup):
+        encode()
+        decode()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        encode()
+        e1.record(stream)
+        decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    ms_per_step = wall * 1000.0 / args.steps
+    print("[bench] timed %d steps: %.2f ms/step (encode %.2f ms, decode %.3f ms)"
+          % (args.steps, ms_per_step, float(np.mean(enc_ms)), float(np.mean(dec_ms))),
+          file=sys.stderr, flush=True)
+    if not torch.equal(mse, mse_rt):
+        print("[bench] WARNING: decoded MSE differs from the encoder's", file=sys.stderr)
+
+    weights_per_step = B * T
+    value = weights_per_step / (ms_per_step / 1000.0)
+    enc_s = float(np.mean(enc_ms)) / 1000.0
+    ops = acs_ops_per_sequence(T) * B
+    achieved_tops = ops / enc_s / 1e12
+    dec_s = float(np.mean(dec_ms)) / 1000.0
+    # decode: read 17 words + write 256 floats per sequence; the MSE pass reads the
+    # targets and the stream again
+    dec_bytes = B * (W * 4 + T * 4) + B * (W * 4 + T * 4 + 4)
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "viterbi_forward_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            traffic = json.load(open(tpath)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "trellis-encoded weights/s (L=16,k=2, 1 GPU); % of VALU peak; HBM GB/s",
+        "value": value,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "viterbi encode + window decode, 4096x4096 matrix = 65536 "
+                               "sequences x T=256, N(0,1) seed 2, L=16 k=2, 1MAD, plain trellis",
+                   "sequences": B, "T": T, "L": L, "k": K, "code": "1mad"},
+        "seq_per_s": B / (ms_per_step / 1000.0),
+        "encode_ms": float(np.mean(enc_ms)),
+        "decode_ms": float(np.mean(dec_ms)),
+        "roofline": {
+            "bound": "alu",
+            "kernel": "viterbi_forward<16,1MAD> (event-timed with its traceback launch)",
+            "achieved": achieved_tops,
+            "peak": PEAK_VALU_TOPS,
+            "unit": "Top/s",
+            "frac": achieved_tops / PEAK_VALU_TOPS,
+            "traffic": traffic,
+        },
+        "decode": {"bound": "hbm", "achieved": dec_bytes / dec_s / 1e9, "peak": PEAK_HBM_GBS,
+                   "unit": "GB/s", "frac": dec_bytes / dec_s / 1e9 / PEAK_HBM_GBS},
+        "mse_mean": float(mse.mean().item()),
+    }
+    del ws
+
+    if not args.no_bcjr:
+        bname = "bcjr4096x4096_1mad"
+        sb_host, _, _ = inputs.workload(bname)
+        sb = torch.from_numpy(sb_host).to(dev)
+        bws = api.bcjr_workspace(sb.shape[0], T, L, K, max_bytes=16 << 30)
+        api.bcjr_soft(sb[:256], 0.1, workspace=bws)      # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        soft, logz = api.bcjr_soft(sb, 0.1, workspace=bws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bsec = e0.elapsed_time(e1) / 1000.0
+        out["bcjr"] = {"workload": "65536 sequences x T=256, N(0,1) seed 5, L=16, 1MAD, tau=0.1",
+                       "seconds": bsec, "seq_per_s": sb.shape[0] / bsec,
+                       "weights_per_s": sb.shape[0] * T / bsec}
+        print("[bench] bcjr %.3f s" % bsec, file=sys.stderr, flush=True)
+        del bws
+
+    if not args.no_cpu:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        cores = max(1, min(16, ncpu))
+        nseq = max(cores, args.cpu_seqs)
+        C = oracle.code_table("1mad", L)
+        sample = s_host[:nseq]
+        chunks = np.array_split(np.arange(nseq), cores)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(cores) as ex:
+            list(ex.map(lambda ix: oracle.viterbi(C, sample[ix], L=L, k=K), chunks))
+        csec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": nseq * T / csec, "unit": "weights/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": "oracle Viterbi encode of the first %d of the 65536 "
+                                         "sequences, %d host threads, %.1f s" % (nseq, cores, csec)}
+        print("[bench] cpu baseline %.1f s on %d threads" % (csec, cores), file=sys.stderr,
+              flush=True)
+
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
