@@ -54,6 +54,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
     ap.add_argument("--cpu-seqs", type=int, default=48)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sequences are "
@@ -92,6 +94,14 @@ def main() -> int:
     def decode():
         nat.qtcq_decode(bits.data_ptr(), B, T, L, K, nat.QTCQ_CODE_1MAD, recon.data_ptr(),
                         seq.data_ptr(), None, mse_rt.data_ptr(), sptr)
+
+    if args.calib_copy:
+        # a plain elementwise copy of known size: 1 GiB read + 1 GiB written
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)     # an elementwise kernel, not a DMA blit
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         encode()

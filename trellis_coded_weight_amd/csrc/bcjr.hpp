@@ -6,23 +6,30 @@
 // cost.  Start state uniform (plain trellis), so the recursion is the Viterbi one with
 // (min, +) replaced by (log-sum-exp, +).
 //
-// Log2 domain, fp32.  kappa = log2(e) / tau and every code value is pre-scaled by
-// sqrt(kappa), so kappa * e_t(j) = w_t * (C'_j - s'_t)^2 with C' = sqrt(kappa) C,
-// s' = sqrt(kappa) s: two VALU ops per state (sub, fma) unweighted.
+// Log2 domain, kappa = log2(e) / tau.  Forward messages per group (a group m = j >> 2
+// shares its predecessors, as in the search):
+//     A_t[(c, x)] = LSE2_a( A_{t-1}[(a, c)] - kappa e_{t-1}((a, c, x)) ),   A_0 = 0,
+// backward messages per low-(L-2)-bit group:
+//     B_{t-1}[(a, c)] = LSE2_x( B_t[(c, x)] - kappa e_t((a, c, x)) ),       B_{T-1} = 0.
+// The same 16 states (a, c, x) and code values serve both directions, so the thread
+// mapping and the LDS chunk swizzle are the search kernel's (viterbi.hpp).
 //
-// Forward messages per group (as in the search, a group m = j >> 2 shares its
-// predecessors): A_t[(c, x)] = LSE2_a( A_{t-1}[(a, c)] - kappa e_{t-1}((a, c, x)) ),
-// A_0 = 0.  Stored values X_t = A_t - G_{t-1} where g_t = max X_t is subtracted on the
-// next read and G accumulates the g's (in fp64).  Every X_t goes to an HBM stash.
-// Backward messages per low-(L-2)-bit group: B_{t-1}[(a, c)] = LSE2_x( B_t[(c, x)] -
-// kappa e_t((a, c, x)) ), B_{T-1} = 0, normalised the same way (h_t, H_t).  The same
-// 16 states (a, c, x) and code values serve both directions, so the thread mapping,
-// LDS layout and swizzle are the search kernel's (see viterbi.hpp).
-// Posterior at t: gamma_t(j) = 2^( la_t(j) + lb_t(j) - log2 Z ), computed in the
-// backward sweep from the stash value X_t[(a, c)], the backward input Y_t[(c, x)] and
-// the step energy, with the exact offset O_t = log2 Z - G_{t-1} - H_t, so the largest
-// exponent is <= 0 and >= -L.  soft_t = sum gamma C / sum gamma: per-wave partial sums
-// per step go to the workspace and a small kernel divides them.
+// Precision.  A message accumulates one rounding per step; in fp32 at tau = 0.01 the
+// per-step increments (kappa e ~ 10 log2 units) make those roundings ~1e-6 each, which
+// over ~250 steps shifts competing walks' weights by ~1e-5.  So messages are stored and
+// combined in fp64: the energy is computed in fp32 (d = C - s, e = d*d [* w]) and
+// widened exactly, each LSE's four inputs are held as an fp64 reference (their maximum)
+// plus fp32 differences (the dominant input is then exact), the LSE's max and
+// differences are fp64, and only exp2 / log2 of small arguments run in fp32.
+// Messages live in one fp64 LDS buffer (128 KiB at L = 16): each step reads all its
+// inputs, barrier, writes all outputs, barrier.
+// Normalisation: stored X_t = A_t - G_{t-1}; the next step subtracts g_t = max X_t
+// (from per-wave maxima) and G accumulates the g's, likewise h/H for the backward.
+// Every X_t also goes to an fp32 HBM stash (rounding there does not accumulate).
+// Posterior at t: gamma_t(j) = 2^( la_t(j) + lb_t(j) - log2 Z ), computed in the backward
+// sweep from the stash value X_t[(a, c)], the backward input Y_t[(c, x)] and the step
+// energy, with the exact offset O_t = log2 Z - G_{t-1} - H_t.  soft_t = sum gamma C /
+// sum gamma: per-wave partial sums per step go to the workspace, a small kernel divides.
 #pragma once
 
 #include "codes.hpp"
@@ -33,11 +40,13 @@ namespace qtcq {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float lse2_4(float v0, float v1, float v2, float v3)
+// log2(2^v0 + 2^v1 + 2^v2 + 2^v3) with the max and the differences in fp64.
+__device__ __forceinline__ double lse2_4(double v0, double v1, double v2, double v3)
 {
-    const float m = __builtin_fmaxf(__builtin_fmaxf(v0, v1), __builtin_fmaxf(v2, v3));
-    const float s = (fast_exp2(v0 - m) + fast_exp2(v1 - m)) + (fast_exp2(v2 - m) + fast_exp2(v3 - m));
-    return m + fast_log2(s);
+    const double m = __builtin_fmax(__builtin_fmax(v0, v1), __builtin_fmax(v2, v3));
+    const float s = (fast_exp2((float)(v0 - m)) + fast_exp2((float)(v1 - m))) +
+                    (fast_exp2((float)(v2 - m)) + fast_exp2((float)(v3 - m)));
+    return m + (double)fast_log2(s);
 }
 
 // Reductions over the first WIDTH lanes of a wave (WIDTH = min(threads, 64)).
@@ -71,6 +80,45 @@ struct BcjrLayout {
     __host__ __device__ static size_t bytes_per_seq(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 4); }
 };
 
+// fp64 message buffer: a chunk = 4 consecutive groups = 32 bytes, stored as two 16-byte
+// halves in separate planes so that a wave's 16-byte accesses stay lane-contiguous.
+// Planes are P bytes apart inside blocks of 2P bytes, P <= 32 KiB, so the second half
+// is reached through the DS instruction's immediate offset.
+template <int L>
+struct BcjrLds {
+    static constexpr int NB = Trellis<L>::kButterflies;   // chunks per message vector
+    static constexpr int kPerBlock = NB < 2048 ? NB : 2048;
+    static constexpr int P = kPerBlock * 16;
+    static constexpr int kBytes = NB * 32;
+    __device__ static int addr(int g)   // g = swizzled chunk index
+    {
+        return (g / kPerBlock) * 2 * P + (g % kPerBlock) * 16;
+    }
+};
+
+// float -> double, emitted at every use: keeps the compiler from hoisting sixteen
+// widened copies (32 registers) out of the inner loops.
+__device__ __forceinline__ double widen(float f)
+{
+    double d;
+    asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(d) : "v"(f));
+    return d;
+}
+
+__device__ __forceinline__ void lds_read4(const char* base, int addr, int P, double (&v)[4])
+{
+    const double2 lo = *reinterpret_cast<const double2*>(base + addr);
+    const double2 hi = *reinterpret_cast<const double2*>(base + addr + P);
+    v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
+}
+
+__device__ __forceinline__ void lds_write4(char* base, int addr, int P, double v0, double v1,
+                                           double v2, double v3)
+{
+    *reinterpret_cast<double2*>(base + addr) = make_double2(v0, v1);
+    *reinterpret_cast<double2*>(base + addr + P) = make_double2(v2, v3);
+}
+
 inline size_t bcjr_bytes_per_seq(int T, int L)
 {
     switch (L) {
@@ -84,20 +132,21 @@ inline size_t bcjr_bytes_per_seq(int T, int L)
 }
 
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws points at the
-// chunk's workspace, bytes_per_seq(T) per sequence.
+// chunk's workspace, bytes_per_seq(T) per sequence.  kappa = log2(e) / tau.
 template <int L, int CODE, bool WEIGHTED>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
-           float sk, char* __restrict__ ws)
+           double kappa, char* __restrict__ ws)
 {
     using Tr = Trellis<L>;
     using Ly = BcjrLayout<L>;
-    constexpr int NB = Tr::kButterflies;
-    constexpr int M = Tr::kGroups;
+    using Ld = BcjrLds<L>;
     constexpr int NT = Tr::kThreads;
+    constexpr int M = Tr::kGroups;
     constexpr int kWaves = Ly::kWaves;
     constexpr int WID = NT < 64 ? NT : 64;
-    __shared__ float4 buf[2][Tr::kChunks];
+    constexpr int P = Ld::P;
+    __shared__ __align__(16) char buf[Ld::kBytes];
     __shared__ float wmax[2][kWaves];
     __shared__ float redm[kWaves], reds[kWaves];
 
@@ -112,177 +161,212 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
     float4* stash = reinterpret_cast<float4*>(base + Ly::off_stash(T));
 
-    float Cs[4][4][4];   // sqrt(kappa) * code value of state (a, c = 4 tid + r, x)
+    float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                Cs[a][r][x] = sk * code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
+                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
 
-    int rd[4], wr[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) rd[a] = lds_chunk(a * (NB / 4) + tid);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wr[r] = lds_chunk(4 * tid + r);
+    // byte addresses of the chunks (a, 4tid..4tid+3) and (4tid+r, 0..3), recomputed at
+    // each use (a few integer ops) rather than held in eight registers
+    auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + tid)); };
+    auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * tid + r)); };
+
+    auto energy = [&](float c, float sp, float wp) -> double {
+        const float d = c - sp;
+        float e = d * d;
+        if constexpr (WEIGHTED) e = wp * e;
+        return (double)e;
+    };
 
     // ---------------- forward ----------------
 #pragma unroll
-    for (int r = 0; r < 4; ++r) buf[0][wr[r]] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
     if (tid < kWaves) wmax[0][tid] = 0.f;
     __syncthreads();
 
     double G = 0.0;   // sum of g_0 .. g_{t-1}
-    int cur = 0;
+    int par = 0;
     for (int t = 1; t < T; ++t) {
-        float g = wmax[cur][0];
+        float g = wmax[par][0];
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q) g = __builtin_fmaxf(g, wmax[cur][q]);
-        G += (double)g;
-        if (tid == 0) gnorm[t - 1] = g;
-        const float sp = sk * s[t - 1];
-        const float wp = WEIGHTED ? w[t - 1] : 1.0f;
-        float u[4][4];
+        for (int q = 1; q < kWaves; ++q) g = __builtin_fmaxf(g, wmax[par][q]);
+        const double g64 = (double)g;
+        // Inputs of butterfly 4 tid + r: X_{t-1}[(a, 4 tid + r)], a = 0..3.  Each LSE's
+        // inputs are held relative to their own maximum (ref, exact in fp64): the
+        // dominant predecessor is represented exactly, only the (small) differences of
+        // the others are rounded to fp32.
+        float rel[4][4];    // [a][r]
+        double ref[4];      // [r] = max_a X - g
+        {
+            // two passes over the four input chunks (maximum, then differences) so that
+            // only one chunk of fp64 inputs is live at a time
+            double mx[4] = {-__builtin_inf(), -__builtin_inf(), -__builtin_inf(), -__builtin_inf()};
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            float4 v = buf[cur][rd[a]];
-            u[a][0] = v.x - g; u[a][1] = v.y - g; u[a][2] = v.z - g; u[a][3] = v.w - g;
+            for (int a = 0; a < 4; ++a) {
+                double xa[4];
+                lds_read4(buf, rd(a), P, xa);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx[r] = __builtin_fmax(mx[r], xa[r]);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                double xa[4];
+                lds_read4(buf, rd(a), P, xa);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rel[a][r] = (float)(xa[r] - mx[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ref[r] = mx[r] - g64;
         }
+        __syncthreads();   // every input read before any output overwrites it
+        G += g64;
+        if (tid == 0) gnorm[t - 1] = g;
+        const float sp = s[t - 1];
+        const float wp = WEIGHTED ? w[t - 1] : 1.0f;
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float o[4];
+            double o[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                float v[4];
+                double v[4];
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float d = Cs[a][r][x] - sp;
-                    v[a] = WEIGHTED ? __builtin_fmaf(-(wp * d), d, u[a][r]) : __builtin_fmaf(-d, d, u[a][r]);
-                }
-                o[x] = lse2_4(v[0], v[1], v[2], v[3]);
-                lmax = __builtin_fmaxf(lmax, o[x]);
+                for (int a = 0; a < 4; ++a)
+                    v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[a][r]));
+                o[x] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                lmax = __builtin_fmaxf(lmax, (float)o[x]);
             }
-            const float4 ov = make_float4(o[0], o[1], o[2], o[3]);
-            buf[cur ^ 1][wr[r]] = ov;
-            stash[((size_t)(t - 1) * 4 + r) * NT + tid] = ov;
+            lds_write4(buf, wr(r), P, o[0], o[1], o[2], o[3]);
+            stash[((size_t)(t - 1) * 4 + r) * NT + tid] =
+                make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
+            __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one butterfly at a time
         }
         lmax = wave_max<WID>(lmax);
-        if (lane == 0) wmax[cur ^ 1][wave] = lmax;
+        if (lane == 0) wmax[par ^ 1][wave] = lmax;
+        par ^= 1;
         __syncthreads();
-        cur ^= 1;
     }
 
-    // log2 Z = G_{T-1} + LSE2_j( X_{T-1}[j >> 2] - g_{T-1} - kappa e_{T-1}(j) )
-    float gl = wmax[cur][0];
+    // log2 Z = G_{T-1} + LSE2_j( X_{T-1}[j >> 2] - g_{T-1} - kappa e_{T-1}(j) ), in two
+    // passes (maximum, then the sum of powers) to keep registers low
+    float gl = wmax[par][0];
 #pragma unroll
-    for (int q = 1; q < kWaves; ++q) gl = __builtin_fmaxf(gl, wmax[cur][q]);
+    for (int q = 1; q < kWaves; ++q) gl = __builtin_fmaxf(gl, wmax[par][q]);
     G += (double)gl;
     if (tid == 0) gnorm[T - 1] = gl;
     double log2z;
     {
-        const float sp = sk * s[T - 1];
+        const float sp = s[T - 1];
         const float wp = WEIGHTED ? w[T - 1] : 1.0f;
-        float q[4][4][4];
-        float m = -__builtin_inff();
+        const double gl64 = (double)gl;
+        double m = -__builtin_inf();
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            float4 v = buf[cur][rd[a]];
-            float in[4] = {v.x - gl, v.y - gl, v.z - gl, v.w - gl};
+            double xa[4];
+            lds_read4(buf, rd(a), P, xa);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float d = Cs[a][r][x] - sp;
-                    q[a][r][x] = WEIGHTED ? __builtin_fmaf(-(wp * d), d, in[r]) : __builtin_fmaf(-d, d, in[r]);
-                    m = __builtin_fmaxf(m, q[a][r][x]);
-                }
+                for (int x = 0; x < 4; ++x)
+                    m = __builtin_fmax(m, __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64));
         }
-        float wm = wave_max<WID>(m);
+        float wm = wave_max<WID>((float)m);
         if (lane == 0) redm[wave] = wm;
         __syncthreads();
         float bm = redm[0];
 #pragma unroll
         for (int qq = 1; qq < kWaves; ++qq) bm = __builtin_fmaxf(bm, redm[qq]);
+        const double bm64 = (double)bm;
         float sum = 0.f;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+            double xa[4];
+            lds_read4(buf, rd(a), P, xa);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) sum += fast_exp2(q[a][r][x] - bm);
+                for (int x = 0; x < 4; ++x)
+                    sum += fast_exp2((float)(__builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64) - bm64));
+        }
         sum = wave_sum<WID>(sum);
         if (lane == 0) reds[wave] = sum;
-        __syncthreads();
+        __syncthreads();   // also: every read of X_{T-1} done before the buffer is reused
         float tot = 0.f;
 #pragma unroll
         for (int qq = 0; qq < kWaves; ++qq) tot += reds[qq];
-        log2z = G + (double)bm + (double)fast_log2(tot);
+        log2z = G + bm64 + (double)fast_log2(tot);
         if (tid == 0) l2z[0] = log2z;
     }
 
     // ---------------- backward + posterior ----------------
-    // Y_{T-1} = 0 in the buffer not holding X_{T-1}
-    int cb = cur ^ 1;
+    // Y_{T-1} = 0
 #pragma unroll
-    for (int a = 0; a < 4; ++a) buf[cb][rd[a]] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < kWaves) wmax[cb][tid] = 0.f;
+    for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
+    if (tid < kWaves) wmax[par][tid] = 0.f;
     __syncthreads();
 
-    double Gm = G;     // G_{t} at the top of iteration t (sum g_0..g_t)
+    double Gm = G;     // G_t at the top of iteration t
     double H = 0.0;    // H_{t+1} at the top of iteration t
-    for (int t = T - 1; t >= 0; --t) {
-        float h = wmax[cb][0];
+    // One backward step at t (t >= 1 produces Y_{t-1}); the posterior of step t is
+    // accumulated on the way.  At t = 0 only the posterior is formed (X_0 = 0).
+    auto bstep = [&](int t, bool produce) {
+        float h = wmax[par][0];
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[cb][q]);
-        H += (double)h;                        // H_t
-        Gm -= (double)gnorm[t];                // G_{t-1}
-        const float Ot = (float)(log2z - Gm - H);
-        // X_t[(a, 4 tid + r)] - O_t from the stash (X_0 = 0)
-        float xo[4][4];
-        if (t > 0) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int g = a * (NB / 4) + tid;      // logical chunk index
-                const float4 v = stash[((size_t)(t - 1) * 4 + (g & 3)) * NT + (g >> 2)];
-                xo[a][0] = v.x - Ot; xo[a][1] = v.y - Ot; xo[a][2] = v.z - Ot; xo[a][3] = v.w - Ot;
-            }
-        } else {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xo[a][r] = -Ot;
-        }
-        float u[4][4];
+        for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[par][q]);
+        const double h64 = (double)h;
+        // inputs Y_t[(4 tid + r, x)], x = 0..3, relative to their maximum (as forward)
+        float rel[4][4];    // [r][x]
+        double ref[4];      // [r] = max_x Y - h
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float4 v = buf[cb][wr[r]];
-            u[r][0] = v.x - h; u[r][1] = v.y - h; u[r][2] = v.z - h; u[r][3] = v.w - h;
+            double yv[4];
+            lds_read4(buf, wr(r), P, yv);
+            const double mx = __builtin_fmax(__builtin_fmax(yv[0], yv[1]), __builtin_fmax(yv[2], yv[3]));
+#pragma unroll
+            for (int x = 0; x < 4; ++x) rel[r][x] = (float)(yv[x] - mx);
+            ref[r] = mx - h64;
         }
-        const float sp = sk * s[t];
+        if (produce) __syncthreads();   // every input read before any output overwrites it
+        H += h64;                              // H_t
+        Gm -= (double)gnorm[t];                // G_{t-1}
+        const double Ot = log2z - Gm - H;
+        const float sp = s[t];
         const float wp = WEIGHTED ? w[t] : 1.0f;
         float pg = 0.f, pc = 0.f;
         float ymax = -__builtin_inff();
-        float yo[4][4];   // Y_{t-1}[(a, 4 tid + r)]
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            // X_t[(a, 4 tid + r)], r = 0..3, from the stash (X_0 = 0)
+            float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (produce) {
+                const int gch = a * NT + tid;      // logical chunk index
+                xs = stash[((size_t)(t - 1) * 4 + (gch & 3)) * NT + (gch >> 2)];
+            }
+            const float xsr[4] = {xs.x, xs.y, xs.z, xs.w};
+            double y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float v[4];
+                // posterior exponent = X_t - O_t + (Y_t - h_t) - kappa e_t
+                const double xo = ((double)xsr[r] - Ot) + ref[r];
+                double v[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const float d = Cs[a][r][x] - sp;
-                    v[x] = WEIGHTED ? __builtin_fmaf(-(wp * d), d, u[r][x]) : __builtin_fmaf(-d, d, u[r][x]);
-                    const float p = fast_exp2(xo[a][r] + v[x]);
+                    v[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[r][x]));
+                    const float p = fast_exp2((float)(xo + v[x]));
                     pg += p;
-                    pc = __builtin_fmaf(p, Cs[a][r][x], pc);
+                    pc = __builtin_fmaf(p, Cv[a][r][x], pc);
                 }
-                if (t > 0) {
-                    yo[a][r] = lse2_4(v[0], v[1], v[2], v[3]);
-                    ymax = __builtin_fmaxf(ymax, yo[a][r]);
+                if (produce) {
+                    y[r] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                    ymax = __builtin_fmaxf(ymax, (float)y[r]);
                 }
             }
+            if (produce) lds_write4(buf, rd(a), P, y[0], y[1], y[2], y[3]);
+            __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one a at a time
         }
         pg = wave_sum<WID>(pg);
         pc = wave_sum<WID>(pc);
@@ -290,21 +374,21 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             part[((size_t)t * kWaves + wave) * 2 + 0] = pg;
             part[((size_t)t * kWaves + wave) * 2 + 1] = pc;
         }
-        if (t == 0) break;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            buf[cb ^ 1][rd[a]] = make_float4(yo[a][0], yo[a][1], yo[a][2], yo[a][3]);
-        ymax = wave_max<WID>(ymax);
-        if (lane == 0) wmax[cb ^ 1][wave] = ymax;
-        __syncthreads();
-        cb ^= 1;
-    }
+        if (produce) {
+            ymax = wave_max<WID>(ymax);
+            if (lane == 0) wmax[par ^ 1][wave] = ymax;
+            par ^= 1;
+            __syncthreads();
+        }
+    };
+    for (int t = T - 1; t >= 1; --t) bstep(t, true);
+    bstep(0, false);
 }
 
-// soft[b][t] = (sum_waves pc) / (sum_waves pg) / sqrt(kappa); log_z = ln 2 * log2 Z.
+// soft[b][t] = (sum_waves pc) / (sum_waves pg); log_z = ln 2 * log2 Z.
 template <int L>
 __global__ void __launch_bounds__(256)
-bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0, float inv_sk,
+bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0,
               float* __restrict__ soft, float* __restrict__ logz)
 {
     using Ly = BcjrLayout<L>;
@@ -321,7 +405,7 @@ bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0, float i
         pg += part[((size_t)t * kWaves + q) * 2 + 0];
         pc += part[((size_t)t * kWaves + q) * 2 + 1];
     }
-    soft[(b0 + i) * T + t] = (pc / pg) * inv_sk;
+    soft[(b0 + i) * T + t] = pc / pg;
     if (logz && t == 0) {
         const double l2z = *reinterpret_cast<const double*>(base);
         logz[b0 + i] = (float)(l2z * 0.69314718055994530942);

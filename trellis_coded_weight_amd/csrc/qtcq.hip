@@ -137,19 +137,16 @@ qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float t
     using Tr = Trellis<L>;
     const size_t per = BcjrLayout<L>::bytes_per_seq(T);
     const int64_t per_chunk = (int64_t)(ws_bytes / per);
-    // kappa = log2(e) / tau; code values and targets are scaled by sqrt(kappa)
-    const double kappa = 1.4426950408889634074 / (double)temperature;
-    const float sk = (float)__builtin_sqrt(kappa);
-    const float inv_sk = (float)(1.0 / __builtin_sqrt(kappa));
+    const double kappa = 1.4426950408889634074 / (double)temperature;   // log2(e) / tau
     char* wsc = static_cast<char*>(ws);
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
         hipLaunchKernelGGL((bcjr_sweep<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0, st,
-                           seq, w, T, b0, sk, wsc);
+                           seq, w, T, b0, kappa, wsc);
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
         hipLaunchKernelGGL((bcjr_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
-                           wsc, T, n, b0, inv_sk, soft, log_z);
+                           wsc, T, n, b0, soft, log_z);
         rc = launch_status();
         if (rc != QTCQ_OK) return rc;
     }

@@ -53,6 +53,15 @@ __device__ __forceinline__ int lds_chunk(int g)
     return g ^ ((g >> 2) & 15);
 }
 
+// A wave-uniform value copied into a VGPR (opaque to the compiler, so it is not folded
+// back into an SGPR operand).
+__device__ __forceinline__ float to_vgpr(float x)
+{
+    float v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+    return v;
+}
+
 // word * 2 + (this lane's bit of mask): one v_addc_co_u32 with the lane mask as the
 // carry-in (the compiler would otherwise select, shift and OR).  All lanes of the wave
 // must be active.
@@ -107,14 +116,17 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     for (int r = 0; r < 4; ++r) mu[0][wr[r]] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
-    int cur = 0;
-    for (int t = 1; t < T; ++t) {
-        const float sp = s[t - 1];
-        const float wp = WEIGHTED ? w[t - 1] : 1.0f;
+    // one ACS step: group minima of step t-1 in `src` -> group minima of step t in `dst`
+    auto step = [&](int t, const float4* __restrict__ src, float4* __restrict__ dst) {
+        // the step's target (and weight) are wave-uniform; keeping them in VGPRs lets
+        // the sub/mul/add below issue as 2-operand VGPR ops, which gfx950 issues twice
+        // as fast as ops reading an SGPR
+        const float sp = to_vgpr(s[t - 1]);
+        const float wp = WEIGHTED ? to_vgpr(w[t - 1]) : 1.0f;
         float in[4][4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            float4 v = mu[cur][rd[a]];
+            float4 v = src[rd[a]];
             in[a][0] = v.x; in[a][1] = v.y; in[a][2] = v.z; in[a][3] = v.w;
         }
         uint32_t word = 0;
@@ -141,16 +153,27 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            mu[cur ^ 1][wr[r]] = make_float4(out[r][0], out[r][1], out[r][2], out[r][3]);
+            dst[wr[r]] = make_float4(out[r][0], out[r][1], out[r][2], out[r][3]);
         bp_seq[(int64_t)(t - 1) * Tr::kBpWords + tid] = word;
         __syncthreads();
-        cur ^= 1;
+    };
+
+    // unrolled by two so that both buffers' LDS addresses stay loop-invariant
+    int t = 1;
+    for (; t + 1 < T; t += 2) {
+        step(t, mu[0], mu[1]);
+        step(t + 1, mu[1], mu[0]);
+    }
+    int cur = 0;
+    if (t < T) {
+        step(t, mu[0], mu[1]);
+        cur = 1;
     }
 
     // final costs cost_{T-1}(i) = mu_{T-1}[i >> 2] + e_{T-1}(i); lowest i wins ties
     {
-        const float sp = s[T - 1];
-        const float wp = WEIGHTED ? w[T - 1] : 1.0f;
+        const float sp = to_vgpr(s[T - 1]);
+        const float wp = WEIGHTED ? to_vgpr(w[T - 1]) : 1.0f;
         float best = __builtin_inff();
         uint32_t bi = 0xFFFFFFFFu;
 #pragma unroll
