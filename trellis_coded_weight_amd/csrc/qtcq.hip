@@ -58,8 +58,8 @@ qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n
     uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
     uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
     float* fin_cost = reinterpret_cast<float*>(fin + n);
-    hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0, st,
-                       seq, w, T, b0, bp, fin, fin_cost, mse);
+    hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3((unsigned)((n + 1) / 2)), dim3(Tr::kThreads),
+                       0, st, seq, w, T, b0, n, bp, fin, fin_cost, mse);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     const int Wd = (int)stream_words(L, 2, T);

@@ -17,16 +17,23 @@
 // mu_{t-1}[i >> 2] + e_{t-1}(i) is rebuilt on the fly from the 2^(L-2) minima.
 //
 // Kernel layout (L = 16): one workgroup of 1024 threads (16 wave64) per sequence, one
-// sequence per CU.  Thread tau owns butterflies c = 4*tau + r (r = 0..3): its 64 code
-// values C[(a, c, x)] are computed once and live in VGPRs for the whole sequence.  The
-// group minima (64 KiB) live in LDS, double-buffered (128 KiB of the 160 KiB); one
-// barrier per step.  Reads are one ds_read_b128 per a (groups (a, 4*tau .. 4*tau+3)),
-// writes one ds_write_b128 per r (groups (c, 0..3)); an XOR swizzle of the 16-byte
-// chunk index keeps both patterns free of bank conflicts.  Each thread emits its 16
-// groups' 2-bit argmins as one uint32 per step (coalesced 4 KiB per step per sequence
-// to HBM).  Ties: strict comparisons keep the lowest a (the lowest predecessor), the
-// final argmin keeps the lowest state.  Arithmetic: fl(fl(C - s)^2) [* w], then
-// fl(mu + e) -- contraction is disabled at build time.
+// sequence per CU.  Thread tau owns butterflies c = tau + r*NT (r = 0..3, NT = 1024
+// threads): its 64 code values C[(a, c, x)] are computed once and live in VGPRs for the
+// whole sequence.  The group minima (64 KiB) live in LDS, double-buffered (128 KiB of
+// the 160 KiB); one barrier per step.  For each r the thread reads its four inputs
+// (a, c), a = 0..3, as lane-contiguous ds_read_b32 and writes its four outputs (c, x),
+// x = 0..3, as one lane-contiguous ds_write_b128 as soon as they are computed, so LDS
+// traffic overlaps the arithmetic and no access pattern has bank conflicts.  Each
+// thread emits its 16 groups' 2-bit argmins as one uint32 per step (coalesced 4 KiB
+// per step per sequence to HBM).  Ties: strict comparisons keep the lowest a (the
+// lowest predecessor), the final argmin keeps the lowest state.  Arithmetic:
+// fl(fl(C - s)^2) [* w], then fl(mu + e) -- contraction is disabled at build time.
+//
+// Issue-rate notes (gfx950, measured): v_add/v_sub/v_mul_f32 with VGPR or constant
+// operands issue at two wave64 instructions per CU cycle, while compares, min/min3,
+// add-with-carry and any instruction reading an SGPR issue at one; hence the per-step
+// target is copied into a VGPR and the argmin uses the fewest slow instructions
+// (min3 + min, three compares, two add-with-carry per group of four candidates).
 #pragma once
 
 #include "codes.hpp"
@@ -43,6 +50,12 @@ struct Trellis {
     static constexpr int kChunks = kGroups / 4;         // float4 chunks of a group vector
     // uint32 backpointer words per step: 16 groups x 2 bits per thread
     static constexpr int kBpWords = kThreads;
+    // backpointer field of group m = 4c + x, c = tau + r*kThreads: word tau, field 4r + x
+    __host__ __device__ static int bp_word(uint32_t m) { return (int)((m >> 2) % kThreads); }
+    __host__ __device__ static int bp_shift(uint32_t m)
+    {
+        return 30 - 2 * (int)(4 * ((m >> 2) / kThreads) + (m & 3));
+    }
 };
 
 // XOR swizzle of a float4 chunk index: bits [3:0] ^= bits [5:2].  Bijective; makes
@@ -73,29 +86,46 @@ __device__ __forceinline__ uint32_t shift_in_bit(uint32_t word, uint64_t mask)
     return out;
 }
 
-// Forward pass.  grid.x = number of sequences in the chunk, block = Trellis<L>::kThreads.
-//   seq, wts : [*][T] (rows b0 .. b0 + gridDim.x - 1 are processed)
-//   bp       : [gridDim.x][T-1][kBpWords] 2-bit argmins of each step
-//   fin      : [gridDim.x] final state (uint32) ; fin_cost [gridDim.x]
-//   mse      : [*] (row b0 + blockIdx.x) or nullptr
+// groups between a group's compares and the add-with-carry that packs its bits
+constexpr int kBitDelay = 1;
+
+// Forward pass over a pair of sequences per workgroup.
+//   grid.x = ceil(n / 2) for the n sequences of the chunk, block = Trellis<L>::kThreads.
+//   seq, wts : [*][T]; the workgroup takes rows b0 + 2*blockIdx.x (+1 if < b0 + n)
+//   bp       : [n][T-1][kBpWords] 2-bit argmins of each step
+//   fin      : [n] final state (uint32) ; fin_cost [n]
+//   mse      : [*] (row b0 + q) or nullptr
+// The two sequences A and B are interleaved so that LDS latency hides behind
+// arithmetic: each phase loads one sequence's inputs while it computes the other's
+// step, with one barrier per phase.  Each sequence has a single 64 KiB buffer of group
+// minima: a buffer is only written in the phase after every thread's reads of it have
+// completed (a barrier in between), and only read after the barrier that follows its
+// writes.  The code-value registers are shared by both sequences.
 template <int L, int CODE, bool WEIGHTED>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
-                uint32_t* __restrict__ bp, uint32_t* __restrict__ fin, float* __restrict__ fin_cost,
-                float* __restrict__ mse)
+                int64_t n, uint32_t* __restrict__ bp, uint32_t* __restrict__ fin,
+                float* __restrict__ fin_cost, float* __restrict__ mse)
 {
     using Tr = Trellis<L>;
     constexpr int NB = Tr::kButterflies;
     constexpr int M = Tr::kGroups;
-    __shared__ float4 mu[2][Tr::kChunks];
+    constexpr int NT = Tr::kThreads;
+    __shared__ float4 muA[Tr::kChunks];   // group minima of sequence A, M / 4 float4
+    __shared__ float4 muB[Tr::kChunks];   // and of sequence B
 
     const int tid = threadIdx.x;
-    const int64_t row = b0 + blockIdx.x;
-    const float* s = seq + row * T;
-    const float* w = WEIGHTED ? wts + row * T : nullptr;
-    uint32_t* bp_seq = bp + (int64_t)blockIdx.x * (T - 1) * Tr::kBpWords;
+    const int64_t qa = 2 * (int64_t)blockIdx.x;          // index within the chunk
+    const bool has_b = qa + 1 < n;                        // uniform over the workgroup
+    const int64_t qb = has_b ? qa + 1 : qa;
+    const float* sa = seq + (b0 + qa) * T;
+    const float* sb = seq + (b0 + qb) * T;
+    const float* wa = WEIGHTED ? wts + (b0 + qa) * T : nullptr;
+    const float* wb = WEIGHTED ? wts + (b0 + qb) * T : nullptr;
+    uint32_t* bpa = bp + qa * (T - 1) * Tr::kBpWords;
+    uint32_t* bpb = bp + qb * (T - 1) * Tr::kBpWords;
 
-    // this thread's code values: state (a, c, x) = a*M + 16*tid + 4*r + x
+    // this thread's code values: state (a, c, x) = a*M + 4*(tid + r*NT) + x
     float Cv[4][4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -103,42 +133,44 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
-
-    int rd[4], wr[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) rd[a] = lds_chunk(a * (NB / 4) + tid);   // groups (a, 4tid..4tid+3)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wr[r] = lds_chunk(4 * tid + r);          // groups (4tid+r, 0..3)
+                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x));
 
     // mu_0 = +0 everywhere, so cost_0 = fl(0 + e_0) = e_0
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mu[0][wr[r]] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 4; ++r) {
+        muA[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
+        muB[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();
 
-    // one ACS step: group minima of step t-1 in `src` -> group minima of step t in `dst`
-    auto step = [&](int t, const float4* __restrict__ src, float4* __restrict__ dst) {
-        // the step's target (and weight) are wave-uniform; keeping them in VGPRs lets
-        // the sub/mul/add below issue as 2-operand VGPR ops, which gfx950 issues twice
-        // as fast as ops reading an SGPR
-        const float sp = to_vgpr(s[t - 1]);
-        const float wp = WEIGHTED ? to_vgpr(w[t - 1]) : 1.0f;
-        float in[4][4];
+    // inputs of this thread's butterflies: in[r][a] = mu_{t-1}[(a, tid + r*NT)]
+    auto load_in = [&](const float4* src4, float (&in)[4][4]) {
+        const float* src = reinterpret_cast<const float*>(src4);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            float4 v = src[rd[a]];
-            in[a][0] = v.x; in[a][1] = v.y; in[a][2] = v.z; in[a][3] = v.w;
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) in[r][a] = src[a * NB + tid + r * NT];
+    };
+
+    // one ACS step from registers: writes mu_t[(c, 0..3)] for c = tid + r*NT and
+    // returns the 16 packed 2-bit argmins
+    // sp, wp: the step's target and weight, wave-uniform but held in VGPRs so that the
+    // sub/mul/add below issue as 2-operand VGPR ops
+    auto acs = [&](const float (&in)[4][4], float sp, float wp, float4* dst) -> uint32_t {
         uint32_t word = 0;
-        float out[4][4];
+        // a group's two argmin bits are shifted in two groups later, so the scalar mask
+        // logic between its compares and its add-with-carry has time to complete
+        uint64_t hi[16], lo[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            float out[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
+                const int g = 4 * r + x;
                 float v[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
-                    v[a] = in[a][r] + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
+                    v[a] = in[r][a] + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
                 const float m = __builtin_fminf(__builtin_fminf(v[0], v[1]), __builtin_fminf(v[2], v[3]));
                 // lowest a attaining the minimum: 0 if v0 == m, else 1 if v1 == m, else
                 // 2 if v2 == m, else 3.  The two bits are shifted in with add-with-carry
@@ -146,50 +178,102 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
                 const uint64_t n0 = __builtin_amdgcn_ballot_w64(v[0] != m);
                 const uint64_t e1 = __builtin_amdgcn_ballot_w64(v[1] == m);
                 const uint64_t n2 = __builtin_amdgcn_ballot_w64(v[2] != m);
-                word = shift_in_bit(word, n0 & ~e1);          // a >= 2
-                word = shift_in_bit(word, n0 & (e1 | n2));    // a odd
-                out[r][x] = m;
+                hi[g] = n0 & ~e1;            // a >= 2
+                lo[g] = n0 & (e1 | n2);      // a odd
+                if (g >= kBitDelay) {
+                    word = shift_in_bit(word, hi[g - kBitDelay]);
+                    word = shift_in_bit(word, lo[g - kBitDelay]);
+                }
+                out[x] = m;
             }
+            dst[tid + r * NT] = make_float4(out[0], out[1], out[2], out[3]);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dst[wr[r]] = make_float4(out[r][0], out[r][1], out[r][2], out[r][3]);
-        bp_seq[(int64_t)(t - 1) * Tr::kBpWords + tid] = word;
-        __syncthreads();
+        for (int g = 16 - kBitDelay; g < 16; ++g) {
+            word = shift_in_bit(word, hi[g]);
+            word = shift_in_bit(word, lo[g]);
+        }
+        return word;
     };
 
-    // unrolled by two so that both buffers' LDS addresses stay loop-invariant
-    int t = 1;
-    for (; t + 1 < T; t += 2) {
-        step(t, mu[0], mu[1]);
-        step(t + 1, mu[1], mu[0]);
-    }
-    int cur = 0;
-    if (t < T) {
-        step(t, mu[0], mu[1]);
-        cur = 1;
+    float inA[4][4], inB[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) inA[r][a] = 0.f;
+
+    // Targets (and weights) go through a small LDS ring of two 256-step chunks per
+    // sequence and are read one phase ahead with the input loads: a per-step scalar
+    // load would be waited on together with the LDS reads (one shared counter) and
+    // stall every phase.  Chunk k + 1 is loaded at the start of step 256 k into the
+    // slot chunk k - 1 used; every read of that chunk happened before step 256 k.
+    constexpr int kChunk = 256;
+    constexpr int kRing = WEIGHTED ? 4 : 2;    // sa, sb [, wa, wb]
+    __shared__ float ring[kRing][2][kChunk];
+    auto fill = [&](int k) {   // chunk k of every stream into slot k & 1
+        const int j = k * kChunk;
+        for (int i = tid; i < kChunk; i += NT) {
+            const bool ok = j + i < T;
+            ring[0][k & 1][i] = ok ? sa[j + i] : 0.f;
+            ring[1][k & 1][i] = ok ? sb[j + i] : 0.f;
+            if constexpr (WEIGHTED) {
+                ring[2][k & 1][i] = ok ? wa[j + i] : 0.f;
+                ring[3][k & 1][i] = ok ? wb[j + i] : 0.f;
+            }
+        }
+    };
+    auto ring_at = [&](int stream, int j) -> float {   // LDS read, lands in a VGPR
+        return ring[stream][(j / kChunk) & 1][j % kChunk];
+    };
+    fill(0);
+    if (T > kChunk) fill(1);
+    __syncthreads();
+
+    float spA = ring_at(0, 0), spB = 0.f;
+    float wpA = WEIGHTED ? ring_at(2, 0) : 1.0f, wpB = 1.0f;
+    for (int t = 1; t < T; ++t) {
+        if (t % kChunk == 0 && t + kChunk < T) fill(t / kChunk + 1);
+        // phase 1: fetch B's inputs and target, step A
+        load_in(muB, inB);
+        spB = ring_at(1, t - 1);
+        if constexpr (WEIGHTED) wpB = ring_at(3, t - 1);
+        const uint32_t wordA = acs(inA, spA, wpA, muA);
+        bpa[(int64_t)(t - 1) * Tr::kBpWords + tid] = wordA;
+        __syncthreads();
+        // phase 2: fetch A's next inputs and target, step B
+        if (t + 1 < T) {
+            load_in(muA, inA);
+            spA = ring_at(0, t);
+            if constexpr (WEIGHTED) wpA = ring_at(2, t);
+        }
+        if (has_b) {
+            const uint32_t wordB = acs(inB, spB, wpB, muB);
+            bpb[(int64_t)(t - 1) * Tr::kBpWords + tid] = wordB;
+        }
+        __syncthreads();
     }
 
     // final costs cost_{T-1}(i) = mu_{T-1}[i >> 2] + e_{T-1}(i); lowest i wins ties
-    {
+    auto finish = [&](const float4* mu4, const float* s, const float* w, int64_t q) {
+        const float* fin_mu = reinterpret_cast<const float*>(mu4);
         const float sp = to_vgpr(s[T - 1]);
         const float wp = WEIGHTED ? to_vgpr(w[T - 1]) : 1.0f;
         float best = __builtin_inff();
         uint32_t bi = 0xFFFFFFFFu;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            float4 v = mu[cur][rd[a]];
-            float in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
+                const float in = fin_mu[a * NB + tid + r * NT];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    float c = in[r] + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
+                    float c = in + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
                     if (c < best) {   // states visited in increasing order
                         best = c;
-                        bi = (uint32_t)(a * M + 16 * tid + 4 * r + x);
+                        bi = (uint32_t)(a * M + 4 * (tid + r * NT) + x);
                     }
                 }
+            }
         }
         // wave reduction of (best, bi), lexicographic, over the lanes that exist
         constexpr int kWidth = Tr::kThreads < 64 ? Tr::kThreads : 64;
@@ -206,16 +290,19 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
             if ((tid & 63) == 0) { wbest[tid >> 6] = best; wbi[tid >> 6] = bi; }
             __syncthreads();
             if (tid == 0) {
-                for (int q = 1; q < kWaves; ++q)
-                    if (wbest[q] < best || (wbest[q] == best && wbi[q] < bi)) { best = wbest[q]; bi = wbi[q]; }
+                for (int k = 1; k < kWaves; ++k)
+                    if (wbest[k] < best || (wbest[k] == best && wbi[k] < bi)) { best = wbest[k]; bi = wbi[k]; }
             }
+            __syncthreads();   // the slots are reused by the next call
         }
         if (tid == 0) {
-            fin[blockIdx.x] = bi;
-            fin_cost[blockIdx.x] = best;
-            if (mse) mse[row] = best / (float)T;
+            fin[q] = bi;
+            fin_cost[q] = best;
+            if (mse) mse[b0 + q] = best / (float)T;
         }
-    }
+    };
+    finish(muA, sa, wa, qa);
+    if (has_b) finish(muB, sb, wb, qb);
 }
 
 // Traceback and pack.  One thread per sequence of the chunk: walks the backpointers
@@ -245,8 +332,8 @@ viterbi_traceback(const uint32_t* __restrict__ bp, const uint32_t* __restrict__ 
         if (wi != curw) { out[curw] = acc; curw = wi; acc = 0; }
         acc |= (j & 3u) << (30 - (p & 31));
         const uint32_t m = j >> 2;                   // group of j's predecessors
-        const uint32_t word = bpq[(int64_t)(t - 1) * Tr::kBpWords + (m >> 4)];
-        const uint32_t a = (word >> (30 - 2 * (m & 15))) & 3u;
+        const uint32_t word = bpq[(int64_t)(t - 1) * Tr::kBpWords + Tr::bp_word(m)];
+        const uint32_t a = (word >> Tr::bp_shift(m)) & 3u;
         j = m | (a << (L - 2));
     }
     if (st) st[0] = j;
