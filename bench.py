@@ -58,7 +58,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
-    ap.add_argument("--cpu-seqs", type=int, default=48)
+    ap.add_argument("--cpu-seqs", type=int, default=1536)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
     ap.add_argument("--calib-copy", action="store_true",

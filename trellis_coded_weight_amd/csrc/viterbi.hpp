@@ -125,15 +125,18 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     uint32_t* bpa = bp + qa * (T - 1) * Tr::kBpWords;
     uint32_t* bpb = bp + qb * (T - 1) * Tr::kBpWords;
 
-    // this thread's code values: state (a, c, x) = a*M + 4*(tid + r*NT) + x
+    // this thread's code values: state (a, c, x) = a*M + 4*(tid + r*NT) + x, computed one
+    // at a time (scheduling barriers) so the fp64 divisions do not pile up registers
     float Cv[4][4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 4; ++x) {
                 Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 
     // mu_0 = +0 everywhere, so cost_0 = fl(0 + e_0) = e_0
 #pragma unroll
@@ -256,6 +259,10 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     // final costs cost_{T-1}(i) = mu_{T-1}[i >> 2] + e_{T-1}(i); lowest i wins ties
     auto finish = [&](const float4* mu4, const float* s, const float* w, int64_t q) {
         const float* fin_mu = reinterpret_cast<const float*>(mu4);
+        // the thread index through an opaque move: keeps the epilogue's address
+        // arithmetic from being hoisted above the step loop (where it would be spilled)
+        int tid = threadIdx.x;
+        asm volatile("v_mov_b32 %0, %0" : "+v"(tid));
         const float sp = to_vgpr(s[T - 1]);
         const float wp = WEIGHTED ? to_vgpr(w[T - 1]) : 1.0f;
         float best = __builtin_inff();
