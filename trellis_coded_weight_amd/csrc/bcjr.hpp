@@ -40,10 +40,19 @@ namespace qtcq {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// fp64 maximum of two values that are never NaN (plain v_max_f64, without the
+// canonicalising moves the compiler adds for IEEE maxnum on loaded values)
+__device__ __forceinline__ double max64(double a, double b)
+{
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // log2(2^v0 + 2^v1 + 2^v2 + 2^v3) with the max and the differences in fp64.
 __device__ __forceinline__ double lse2_4(double v0, double v1, double v2, double v3)
 {
-    const double m = __builtin_fmax(__builtin_fmax(v0, v1), __builtin_fmax(v2, v3));
+    const double m = max64(max64(v0, v1), max64(v2, v3));
     const float s = (fast_exp2((float)(v0 - m)) + fast_exp2((float)(v1 - m))) +
                     (fast_exp2((float)(v2 - m)) + fast_exp2((float)(v3 - m)));
     return m + (double)fast_log2(s);
@@ -95,6 +104,16 @@ struct BcjrLds {
         return (g / kPerBlock) * 2 * P + (g % kPerBlock) * 16;
     }
 };
+
+// A wave-uniform double kept in two SGPRs (the running normalisation sums would
+// otherwise occupy VGPR pairs for the whole sweep).
+__device__ __forceinline__ double uniform64(double x)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // float -> double, emitted at every use: keeps the compiler from hoisting sixteen
 // widened copies (32 registers) out of the inner loops.
@@ -161,19 +180,27 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
     float4* stash = reinterpret_cast<float4*>(base + Ly::off_stash(T));
 
-    float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x)
+    float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x), one at a time
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 4; ++x) {
                 Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 
     // byte addresses of the chunks (a, 4tid..4tid+3) and (4tid+r, 0..3), recomputed at
-    // each use (a few integer ops) rather than held in eight registers
-    auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + tid)); };
-    auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * tid + r)); };
+    // each use from an opaque copy of the thread index, so that the compiler cannot hoist
+    // eight loop-invariant addresses out of the step loops (they would be spilled)
+    auto opaque_tid = [&]() {
+        int v = tid;
+        asm volatile("v_mov_b32 %0, %0" : "+v"(v));
+        return v;
+    };
+    auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + opaque_tid())); };
+    auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * opaque_tid() + r)); };
 
     auto energy = [&](float c, float sp, float wp) -> double {
         const float d = c - sp;
@@ -210,8 +237,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 double xa[4];
                 lds_read4(buf, rd(a), P, xa);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx[r] = __builtin_fmax(mx[r], xa[r]);
+                for (int r = 0; r < 4; ++r) mx[r] = max64(mx[r], xa[r]);
             }
+            // keep the second pass's reads (the compiler would reuse the first pass's
+            // sixteen fp64 values, which is what the two passes avoid)
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 double xa[4];
@@ -223,27 +253,32 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             for (int r = 0; r < 4; ++r) ref[r] = mx[r] - g64;
         }
         __syncthreads();   // every input read before any output overwrites it
-        G += g64;
+        G = uniform64(G + g64);
         if (tid == 0) gnorm[t - 1] = g;
         const float sp = s[t - 1];
         const float wp = WEIGHTED ? w[t - 1] : 1.0f;
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            double o[4];
+            float of[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                double v[4];
+            for (int h = 0; h < 2; ++h) {        // output pairs x = 2h, 2h + 1
+                double o[2];
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[a][r]));
-                o[x] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
-                lmax = __builtin_fmaxf(lmax, (float)o[x]);
+                for (int xx = 0; xx < 2; ++xx) {
+                    const int x = 2 * h + xx;
+                    double v[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[a][r]));
+                    o[xx] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                    of[x] = (float)o[xx];
+                    lmax = __builtin_fmaxf(lmax, of[x]);
+                }
+                *reinterpret_cast<double2*>(buf + wr(r) + h * P) = make_double2(o[0], o[1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            lds_write4(buf, wr(r), P, o[0], o[1], o[2], o[3]);
-            stash[((size_t)(t - 1) * 4 + r) * NT + tid] =
-                make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
-            __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one butterfly at a time
+            stash[((size_t)(t - 1) * 4 + r) * NT + tid] = make_float4(of[0], of[1], of[2], of[3]);
         }
         lmax = wave_max<WID>(lmax);
         if (lane == 0) wmax[par ^ 1][wave] = lmax;
@@ -256,7 +291,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     float gl = wmax[par][0];
 #pragma unroll
     for (int q = 1; q < kWaves; ++q) gl = __builtin_fmaxf(gl, wmax[par][q]);
-    G += (double)gl;
+    G = uniform64(G + (double)gl);
     if (tid == 0) gnorm[T - 1] = gl;
     double log2z;
     {
@@ -272,7 +307,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
-                    m = __builtin_fmax(m, __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64));
+                    m = max64(m, __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64));
         }
         float wm = wave_max<WID>((float)m);
         if (lane == 0) redm[wave] = wm;
@@ -298,7 +333,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float tot = 0.f;
 #pragma unroll
         for (int qq = 0; qq < kWaves; ++qq) tot += reds[qq];
-        log2z = G + bm64 + (double)fast_log2(tot);
+        log2z = uniform64(G + bm64 + (double)fast_log2(tot));
         if (tid == 0) l2z[0] = log2z;
     }
 
@@ -325,48 +360,56 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         for (int r = 0; r < 4; ++r) {
             double yv[4];
             lds_read4(buf, wr(r), P, yv);
-            const double mx = __builtin_fmax(__builtin_fmax(yv[0], yv[1]), __builtin_fmax(yv[2], yv[3]));
+            const double mx = max64(max64(yv[0], yv[1]), max64(yv[2], yv[3]));
 #pragma unroll
             for (int x = 0; x < 4; ++x) rel[r][x] = (float)(yv[x] - mx);
             ref[r] = mx - h64;
         }
         if (produce) __syncthreads();   // every input read before any output overwrites it
-        H += h64;                              // H_t
-        Gm -= (double)gnorm[t];                // G_{t-1}
-        const double Ot = log2z - Gm - H;
+        H = uniform64(H + h64);                       // H_t
+        Gm = uniform64(Gm - (double)gnorm[t]);        // G_{t-1}
+        const double Ot = uniform64(log2z - Gm - H);
         const float sp = s[t];
         const float wp = WEIGHTED ? w[t] : 1.0f;
         float pg = 0.f, pc = 0.f;
         float ymax = -__builtin_inff();
+        // X_t[(a, 4 tid + r)], r = 0..3, from the stash (X_0 = 0), prefetched one a ahead
+        auto stash_at = [&](int a) -> float4 {
+            if (!produce) return make_float4(0.f, 0.f, 0.f, 0.f);
+            const int gch = a * NT + tid;      // logical chunk index
+            return stash[((size_t)(t - 1) * 4 + (gch & 3)) * NT + (gch >> 2)];
+        };
+        float4 xs_next = stash_at(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            // X_t[(a, 4 tid + r)], r = 0..3, from the stash (X_0 = 0)
-            float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (produce) {
-                const int gch = a * NT + tid;      // logical chunk index
-                xs = stash[((size_t)(t - 1) * 4 + (gch & 3)) * NT + (gch >> 2)];
-            }
+            const float4 xs = xs_next;
+            if (a < 3) xs_next = stash_at(a + 1);
+            asm volatile("" ::: "memory");    // no further hoisting of stash loads
             const float xsr[4] = {xs.x, xs.y, xs.z, xs.w};
-            double y[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // posterior exponent = X_t - O_t + (Y_t - h_t) - kappa e_t
-                const double xo = ((double)xsr[r] - Ot) + ref[r];
-                double v[4];
+            for (int h = 0; h < 2; ++h) {        // output pairs r = 2h, 2h + 1
+                double y[2];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    v[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[r][x]));
-                    const float p = fast_exp2((float)(xo + v[x]));
-                    pg += p;
-                    pc = __builtin_fmaf(p, Cv[a][r][x], pc);
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = 2 * h + rr;
+                    // posterior exponent = X_t - O_t + (Y_t - h_t) - kappa e_t
+                    const double xo = ((double)xsr[r] - Ot) + ref[r];
+                    double v[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        v[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[r][x]));
+                        const float p = fast_exp2((float)(xo + v[x]));
+                        pg += p;
+                        pc = __builtin_fmaf(p, Cv[a][r][x], pc);
+                    }
+                    if (produce) {
+                        y[rr] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                        ymax = __builtin_fmaxf(ymax, (float)y[rr]);
+                    }
                 }
-                if (produce) {
-                    y[r] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
-                    ymax = __builtin_fmaxf(ymax, (float)y[r]);
-                }
+                if (produce) *reinterpret_cast<double2*>(buf + rd(a) + h * P) = make_double2(y[0], y[1]);
+                __builtin_amdgcn_sched_barrier(0);   // bound live ranges
             }
-            if (produce) lds_write4(buf, rd(a), P, y[0], y[1], y[2], y[3]);
-            __builtin_amdgcn_sched_barrier(0);   // bound live ranges: one a at a time
         }
         pg = wave_sum<WID>(pg);
         pc = wave_sum<WID>(pc);
