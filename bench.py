@@ -143,9 +143,9 @@ def main() -> int:
     ops = acs_ops_per_sequence(T) * B
     achieved_tops = ops / enc_s / 1e12
     dec_s = float(np.mean(dec_ms)) / 1000.0
-    # decode: read 17 words + write 256 floats per sequence; the MSE pass reads the
-    # targets and the stream again
-    dec_bytes = B * (W * 4 + T * 4) + B * (W * 4 + T * 4 + 4)
+    # decode (one fused kernel): read 17 stream words and 256 targets, write 256
+    # reconstructed weights and the MSE, per sequence
+    dec_bytes = B * (W * 4 + T * 4 + T * 4 + 4)
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "viterbi_forward_traffic.json")

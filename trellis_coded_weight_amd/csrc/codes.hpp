@@ -5,8 +5,11 @@
 // state, then either the byte sum of the LCG output (1MAD) or an fp16 bit trick with
 // one fp16 add (3INST; XOR-Trellis explainer, "The sign at each junction has to be
 // cheap").  The final rescale is a binary64 division rounded once to binary32, so every
-// code value is a fixed bit pattern; the device computes it with native fp64 (IEEE
-// division on gfx950) and v_sad_u8 for the byte sum.
+// code value is a fixed bit pattern.  The device multiplies by the binary64 reciprocal
+// of the divisor instead of dividing: over the whole input domain of each code (byte
+// sums 0..1020; every finite fp16 value) the product rounds to the same binary32 value
+// as the quotient -- checked exhaustively on the host -- and it costs one fp64 multiply
+// instead of an IEEE division sequence.  v_sad_u8 forms the byte sum.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,7 +33,8 @@ __device__ __forceinline__ uint32_t byte_sum(uint32_t u)
 // 1MAD for a byte sum S in [0, 1020]: (S - 510) / 147.8 in binary64, then binary32.
 __device__ __forceinline__ float mad_value_from_bytesum(uint32_t S)
 {
-    double q = (double)((int)S - 510) / 147.8;
+    constexpr double kInv = 1.0 / 147.8;   // binary64 reciprocal of the binary64 divisor
+    double q = (double)((int)S - 510) * kInv;
     return (float)q;
 }
 
@@ -50,7 +54,8 @@ __device__ __forceinline__ _Float16 code_3inst_raw(uint32_t x)
 
 __device__ __forceinline__ float code_3inst(uint32_t x)
 {
-    double q = (double)(float)code_3inst_raw(x) / 1.244;
+    constexpr double kInv = 1.0 / 1.244;
+    double q = (double)(float)code_3inst_raw(x) * kInv;
     return (float)q;
 }
 

@@ -2,64 +2,119 @@
 //
 // QTIP blog, "The trellis: a stateful codebook": the state at weight t is the L-bit
 // window of the MSB-first stream starting at bit t*k, so every weight decodes on its
-// own, with no graph and no serial walk.  One thread per weight: a 64-bit funnel of
-// the two stream words the window can touch, a shift and a mask, then the code.
+// own, with no graph and no serial walk.
 //
-// The path cost of the reconstruction (the encoder's mse) must be summed in t order to
-// reproduce the encoder bit for bit, so it runs as its own kernel with one thread per
-// sequence that slides the window along the stream.
+// One workgroup decodes a tile of SB whole sequences (SB*T <= 4096 weights): the tile's
+// stream words are staged in LDS (one coalesced read), then every thread decodes weights
+// of the tile in flattened order -- a 64-bit funnel of the two words the window can
+// touch, a shift and a mask, then the code -- and writes them coalesced.  When the MSE
+// is wanted the same thread forms the step error against the (coalesced) target and
+// leaves it in LDS; the path cost must be summed in t order to reproduce the encoder
+// bit for bit, so after a barrier one thread per sequence adds its row sequentially.
 #pragma once
 
 #include "codes.hpp"
 
 namespace qtcq {
 
-template <int L, int CODE>
-__global__ void __launch_bounds__(256)
-window_decode(const uint32_t* __restrict__ bits, int64_t total, int T, int W,
-              float* __restrict__ recon)
-{
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    const int64_t b = idx / T;
-    const int t = (int)(idx - b * T);
-    const int p = 2 * t;                 // first stream bit of the window (k = 2)
-    const int wi = p >> 5;
-    const uint32_t* row = bits + b * W;
-    const uint64_t hi = row[wi];
-    const uint64_t lo = (wi + 1 < W) ? row[wi + 1] : 0u;
-    const uint64_t f = (hi << 32) | lo;
-    const uint32_t win = (uint32_t)(f >> (64 - (p & 31) - L)) & ((1u << L) - 1u);
-    recon[idx] = code_value<CODE>(win);
-}
-
-// One thread per sequence: walks its stream's windows in t order (each new window is
-// the previous one shifted left by 2 with the next 2 stream bits entering at the
-// bottom) and sums the binary32 path cost against seq (and weights), divided by T.
-template <int L, int CODE, bool WEIGHTED>
-__global__ void __launch_bounds__(256)
-decode_path_mse(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
-                const float* __restrict__ wts, int64_t B, int T, int W, float* __restrict__ mse)
-{
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    const uint32_t* row = bits + b * W;
-    const float* s = seq + b * T;
-    const float* w = WEIGHTED ? wts + b * T : nullptr;
-    uint32_t word = row[0];
-    uint32_t win = word >> (32 - L);
-    int p = L;                                 // next unread stream bit
-    float acc = 0.0f;
-    for (int t = 0; t < T; ++t) {
-        if (t > 0) {
-            if ((p & 31) == 0) word = row[p >> 5];
-            const uint32_t nb = (word >> (30 - (p & 31))) & 3u;
-            win = ((win << 2) | nb) & ((1u << L) - 1u);
-            p += 2;
-        }
-        acc = acc + step_err<WEIGHTED>(code_value<CODE>(win), s[t], WEIGHTED ? w[t] : 1.0f);
+// Tile geometry, shared by the kernel and its launcher.
+struct DecodeTile {
+    static constexpr int kThreads = 256;
+    static constexpr int kMaxWeights = 4096;     // SB * T
+    static constexpr int kBitsWords = 1024;      // bound on SB * W (L <= 16, T <= 4096)
+    static constexpr int kErrFloats = 5888;      // bound on SB * err_stride(T)
+    // sequences per tile: SB*T <= 4096 and one summing thread per sequence
+    static int seqs(int T)
+    {
+        const int sb = kMaxWeights / T;
+        return sb < 1 ? 1 : (sb > kThreads ? kThreads : sb);
     }
-    mse[b] = acc / (float)T;
+    // row stride of the step errors: a multiple of 4 (16-byte reads), offset by 4 words
+    // per row so that the summing threads' reads fall in different banks
+    __host__ __device__ static int err_stride(int T) { return ((T + 3) & ~3) + 4; }
+    static size_t lds_bytes(int T, int W, bool with_mse)
+    {
+        const int sb = seqs(T);
+        return 4 * (size_t)((with_mse ? sb * err_stride(T) : 0) + sb * W);
+    }
+};
+
+// grid.x = ceil(B / SB), block = 256.  recon may be NULL (MSE only); mse may be NULL
+// (decode only, MSE_ = false).
+template <int L, int CODE, bool MSE_, bool WEIGHTED>
+__global__ void __launch_bounds__(DecodeTile::kThreads)
+decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
+            const float* __restrict__ wts, int64_t B, int T, int W, int SB,
+            float* __restrict__ recon, float* __restrict__ mse)
+{
+    constexpr int NT = DecodeTile::kThreads;
+    // dynamic LDS, DecodeTile::lds_bytes: step errors [SB][err_stride] (MSE only), then
+    // the tile's stream words [SB][W]
+    extern __shared__ __align__(16) char dyn_lds[];
+    float* lerr = reinterpret_cast<float*>(dyn_lds);
+    uint32_t* lbits = reinterpret_cast<uint32_t*>(dyn_lds) + (MSE_ ? SB * DecodeTile::err_stride(T) : 0);
+
+    const int tid = threadIdx.x;
+    const int64_t b0 = (int64_t)blockIdx.x * SB;
+    const int n = (int)((B - b0) < SB ? (B - b0) : SB);
+    const int total = n * T;                  // <= kMaxWeights: at most U per thread
+    const int64_t base = b0 * T;
+    constexpr int U = DecodeTile::kMaxWeights / NT;
+
+    // every target (and weight) this thread needs, in flight before the staging barrier
+    float sv[U], wv[U];
+    if constexpr (MSE_) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = tid + u * NT;
+            sv[u] = i < total ? seq[base + i] : 0.0f;
+            wv[u] = (WEIGHTED && i < total) ? wts[base + i] : 1.0f;
+        }
+    }
+    const int nw = n * W;
+    const uint32_t* gb = bits + b0 * W;
+    for (int i = tid; i < nw; i += NT) lbits[i] = gb[i];
+    __syncthreads();
+
+    const int ES = DecodeTile::err_stride(T);
+    // flattened element i = r * T + t, advanced by NT per iteration without a division
+    int r = tid / T, t = tid - r * T;
+    const int dr = NT / T, dt = NT - dr * T;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = tid + u * NT;
+        if (i >= total) break;
+        const int p = 2 * t;                  // first stream bit of the window (k = 2)
+        const int wi = p >> 5;
+        const uint32_t hi = lbits[r * W + wi];
+        const uint32_t lo = (wi + 1 < W) ? lbits[r * W + wi + 1] : 0u;
+        // bits [p, p + 32) of the stream, then the top L of them
+        const uint32_t top = __builtin_amdgcn_alignbit(hi, lo, (32 - (p & 31)) & 31);
+        const uint32_t win = ((p & 31) ? top : hi) >> (32 - L);
+        const float c = code_value<CODE>(win);
+        if (recon) recon[base + i] = c;
+        if constexpr (MSE_) lerr[r * ES + t] = step_err<WEIGHTED>(c, sv[u], wv[u]);
+        r += dr;
+        t += dt;
+        if (t >= T) { t -= T; ++r; }
+    }
+    if constexpr (MSE_) {
+        __syncthreads();
+        if (tid < n) {
+            const float* e = lerr + tid * ES;
+            float acc = 0.0f;
+            int u = 0;
+            for (; u + 4 <= T; u += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(e + u);
+                acc = acc + q.x;
+                acc = acc + q.y;
+                acc = acc + q.z;
+                acc = acc + q.w;
+            }
+            for (; u < T; ++u) acc = acc + e[u];
+            mse[b0 + tid] = acc / (float)T;
+        }
+    }
 }
 
 // Code table: out[x] = code(x) for x < n.

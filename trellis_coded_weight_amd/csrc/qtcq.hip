@@ -101,23 +101,21 @@ qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, co
                         const float* w, float* mse, hipStream_t st)
 {
     const int Wd = (int)stream_words(L, 2, T);
-    if (recon) {
-        const int64_t total = B * T;
-        hipLaunchKernelGGL((window_decode<L, CODE>), dim3(blocks_for(total, 256)), dim3(256), 0, st,
-                           bits, total, T, Wd, recon);
-        qtcq_status rc = launch_status();
-        if (rc != QTCQ_OK) return rc;
-    }
-    if (mse) {
-        if (w)
-            hipLaunchKernelGGL((decode_path_mse<L, CODE, true>), dim3(blocks_for(B, 256)), dim3(256),
-                               0, st, bits, seq, w, B, T, Wd, mse);
-        else
-            hipLaunchKernelGGL((decode_path_mse<L, CODE, false>), dim3(blocks_for(B, 256)), dim3(256),
-                               0, st, bits, seq, w, B, T, Wd, mse);
-        return launch_status();
-    }
-    return QTCQ_OK;
+    const int SB = DecodeTile::seqs(T);
+    if (SB * Wd > DecodeTile::kBitsWords || SB * DecodeTile::err_stride(T) > DecodeTile::kErrFloats)
+        return QTCQ_ERR_UNSUPPORTED;      // not reachable for T <= 4096, L <= 16
+    const dim3 grid(blocks_for(B, SB)), block(DecodeTile::kThreads);
+    const size_t lds = DecodeTile::lds_bytes(T, Wd, mse != nullptr);
+    if (!mse)
+        hipLaunchKernelGGL((decode_tile<L, CODE, false, false>), grid, block, lds, st, bits, seq,
+                           w, B, T, Wd, SB, recon, mse);
+    else if (w)
+        hipLaunchKernelGGL((decode_tile<L, CODE, true, true>), grid, block, lds, st, bits, seq, w,
+                           B, T, Wd, SB, recon, mse);
+    else
+        hipLaunchKernelGGL((decode_tile<L, CODE, true, false>), grid, block, lds, st, bits, seq,
+                           w, B, T, Wd, SB, recon, mse);
+    return launch_status();
 }
 
 template <int L>
