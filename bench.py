@@ -10,6 +10,8 @@ Extra objects on the line:
   roofline      -- the dominant kernel (the ACS forward pass) against the VALU peak,
                    from algorithmic ops / HIP-event-timed duration of the encode call
   cpu_baseline  -- the CPU oracle on a bounded sample, on this host's cores
+  tailbiting    -- the tail-biting encode (two searches per sequence) of a 4096x4096
+                   matrix
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
   decode        -- the decode kernels' own time and algorithmic HBM bytes
 """
@@ -58,6 +60,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
+    ap.add_argument("--no-tb", action="store_true", help="skip the tail-biting encode")
     ap.add_argument("--cpu-seqs", type=int, default=1536)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
@@ -188,6 +191,39 @@ def main() -> int:
         "mse_mean": float(mse.mean().item()),
     }
     del ws
+
+    if not args.no_tb:
+        # tail-biting encode of the same matrix: two forward searches per sequence
+        tname = "tb4096x4096_1mad"
+        st_host, _, _ = inputs.workload(tname, B=args.seqs or None)
+        stb = torch.from_numpy(st_host).to(dev)
+        Bt = stb.shape[0]
+        tws = api.tailbiting_workspace(Bt, T, L, K, max_bytes=64 << 30)
+        tbits = torch.empty((Bt, api.tailbiting_words(L, K, T)), dtype=torch.int32, device=dev)
+        tmse = torch.empty(Bt, dtype=torch.float32, device=dev)
+
+        def tb_encode():
+            nat.qtcq_tailbiting_encode(stb.data_ptr(), None, Bt, T, L, K, nat.QTCQ_CODE_1MAD,
+                                       tbits.data_ptr(), tmse.data_ptr(), None, tws.data_ptr(),
+                                       tws.numel(), sptr)
+        tb_encode()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 2
+        e0.record(stream)
+        for _ in range(reps):
+            tb_encode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tsec = e0.elapsed_time(e1) / 1000.0 / reps
+        tops = 2 * acs_ops_per_sequence(T) * Bt / tsec / 1e12
+        out["tailbiting"] = {"workload": "tail-biting encode (two searches), 4096x4096 = %d "
+                                         "sequences x T=256, N(0,1) seed 6, L=16, 1MAD" % Bt,
+                             "ms": tsec * 1000.0, "weights_per_s": Bt * T / tsec,
+                             "mse_mean": float(tmse.mean().item()),
+                             "achieved": tops, "unit": "Top/s", "frac": tops / PEAK_VALU_TOPS}
+        print("[bench] tail-biting %.2f ms" % (tsec * 1000.0), file=sys.stderr, flush=True)
+        del tws
 
     if not args.no_bcjr:
         bname = "bcjr4096x4096_1mad"

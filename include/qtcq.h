@@ -9,7 +9,8 @@
  *         (blog) -- "The trellis: a stateful codebook" (bitshift trellis, window
  *         decode, Viterbi with shift-computed predecessors), "The codebook is
  *         computed" (1MAD, 3INST), "Tail-biting is worth its complexity" (a plain
- *         trellis stores its L-k start bits).
+ *         trellis stores its L-k start bits; the tail-biting trellis and its
+ *         two-search encoder).
  *  [XOR]  "XOR-Trellis -- Trellis-coded quantization vs VQ codebooks -- What does it
  *         mean?" (explainer) -- "Cliff edges: weighting errors instead of rotating
  *         them" (per-weight error weights in the path cost), "The sign at each junction
@@ -146,6 +147,53 @@ qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, in
 qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
                            int code, float temperature, float* soft, float* log_z,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Tail-biting trellis [QTIP "Tail-biting is worth its complexity"] ------------
+ * A tail-biting walk is cyclic: the low L-k bits of its last state equal the high L-k
+ * bits of its first, so the stream needs no start state and is exactly k*T bits.
+ * Layout: state st[t] contributes its k high bits at stream bits [t*k, t*k + k), most
+ * significant first, in the word layout above; weight t reads the window of stream
+ * bits t*k, ..., t*k + L - 1 taken modulo k*T (the last L/k - 1 windows wrap round to
+ * the start).  Requires k*T >= L (the stream is at least one window long). */
+
+/* Words per sequence of a tail-biting stream: ceil(k*T / 32) -- 16 at (16, 2, 256),
+ * word-aligned whenever k*T is a multiple of 32.  Returns -1 for arguments outside
+ * 1 <= k <= L <= 32, T >= 1, k*T >= L. */
+int64_t qtcq_tailbiting_words(int L, int k, int T);
+
+/* Workspace bytes qtcq_tailbiting_encode needs for `B` sequences in one pass (the
+ * encode layout plus one overlap word per sequence).  Smaller workspaces that hold one
+ * sequence are used in chunks.  Returns 0 for unsupported arguments. */
+size_t qtcq_tailbiting_workspace_bytes(int64_t B, int T, int L, int k);
+
+/* Tail-biting encode with two searches per sequence (the page's summary of QTIP's
+ * Algorithm 4): (1) the free-start Viterbi search of qtcq_viterbi_encode over the
+ * targets rotated by r = floor(T/2), s'[t] = seq[b][(t + r) mod T] (weights likewise),
+ * so that the sequence's two ends meet in the middle; (2) the overlap o = the high
+ * L-k bits of the state that search assigns to original position 0; (3) the search
+ * over the original targets with the start restricted to states whose high L-k bits
+ * are o and the end to states whose low L-k bits are o (ties as in
+ * qtcq_viterbi_encode: lowest predecessor, then lowest allowed final state).  The
+ * result is a valid tail-biting walk, not always the cheapest one (the exact optimum
+ * needs 2^(L-k) pinned searches).
+ *   seq, err_w, B, T, L, k, code : as qtcq_viterbi_encode; k*T >= L
+ *   bits   [B][qtcq_tailbiting_words(L,k,T)] uint32 (out), the tail-biting layout
+ *   mse    [B] float32 (out) = the binary32 path cost of step (3) / T, or NULL
+ *   states [B][T] uint32 (out), or NULL
+ *   workspace: 16-byte aligned, >= qtcq_tailbiting_workspace_bytes(1, T, L, k)
+ * Errors: QTCQ_ERR_INVALID_ARG (also k*T < L), QTCQ_ERR_UNSUPPORTED,
+ * QTCQ_ERR_WORKSPACE, QTCQ_ERR_DEVICE. */
+qtcq_status qtcq_tailbiting_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
+                                   int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Window decode of tail-biting streams (cyclic windows, layout above); arguments,
+ * outputs and errors as qtcq_decode, with bits [B][qtcq_tailbiting_words(L,k,T)] and
+ * k*T >= L.  Decoding qtcq_tailbiting_encode's output with the same seq/err_w
+ * reproduces its mse bit for bit. */
+qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+                                   float* recon, const float* seq, const float* err_w, float* mse,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,21 @@ def lib() -> ctypes.CDLL:
                                              i64p]),
             "oracle_brute_bcjr": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, c_dbl, f64p,
                                           f64p]),
+            "oracle_tb_stream_bits": (c_i64, [c_int, c_int, c_int]),
+            "oracle_tb_stream_words": (c_i64, [c_int, c_int, c_int]),
+            "oracle_viterbi_pinned": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, c_u32,
+                                              u32p, f32p]),
+            "oracle_tailbiting_exact": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, u32p,
+                                                f32p]),
+            "oracle_tailbiting_alg4": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, u32p, f32p,
+                                               u32p]),
+            "oracle_tailbiting_alg4_batch": (c_int, [f32p, f32p, f32p, c_i64, c_int, c_int, c_int,
+                                                     u32p, f32p, f32p]),
+            "oracle_tb_pack_batch": (c_int, [u32p, c_i64, c_int, c_int, c_int, u32p]),
+            "oracle_tb_decode_batch": (c_int, [u32p, c_i64, c_int, c_int, c_int, f32p, u32p,
+                                               f32p]),
+            "oracle_brute_tailbiting": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, f32p,
+                                                i64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -249,3 +264,126 @@ def brute_bcjr(C, s, tau, w=None, L=6, k=2):
                                    _p(soft, ctypes.c_double), _p(logz, ctypes.c_double)),
            "brute_bcjr")
     return soft, logz[0]
+
+
+# ---------------------------------------------------------------------------------
+# tail-biting trellis
+# ---------------------------------------------------------------------------------
+
+def tb_stream_bits(L, k, T) -> int:
+    return lib().oracle_tb_stream_bits(L, k, T)
+
+
+def tb_stream_words(L, k, T) -> int:
+    return lib().oracle_tb_stream_words(L, k, T)
+
+
+def viterbi_pinned(C, s, o, w=None, L=16, k=2):
+    """One sequence, both ends pinned to overlap o.  Returns (states u32 [T], cost f32)."""
+    C = _f32(C)
+    s = _f32(s)
+    w = _f32(w)
+    T = s.shape[-1]
+    st = np.empty(T, dtype=np.uint32)
+    cost = np.empty(1, dtype=np.float32)
+    _check(lib().oracle_viterbi_pinned(_p(C, ctypes.c_float), _p(s, ctypes.c_float),
+                                       _p(w, ctypes.c_float), T, L, k, int(o),
+                                       _p(st, ctypes.c_uint32), _p(cost, ctypes.c_float)),
+           "viterbi_pinned")
+    return st, cost[0]
+
+
+def tailbiting_exact(C, s, w=None, L=12, k=2):
+    """Exact tail-biting optimum of one sequence (2^(L-k) pinned searches).
+    Returns (states u32 [T], cost f32)."""
+    C = _f32(C)
+    s = _f32(s)
+    w = _f32(w)
+    T = s.shape[-1]
+    st = np.empty(T, dtype=np.uint32)
+    cost = np.empty(1, dtype=np.float32)
+    _check(lib().oracle_tailbiting_exact(_p(C, ctypes.c_float), _p(s, ctypes.c_float),
+                                         _p(w, ctypes.c_float), T, L, k,
+                                         _p(st, ctypes.c_uint32), _p(cost, ctypes.c_float)),
+           "tailbiting_exact")
+    return st, cost[0]
+
+
+def tailbiting_overlap(C, s, w=None, L=16, k=2) -> int:
+    """The overlap the two-search encoder pins the ends to, for one sequence."""
+    C = _f32(C)
+    s = _f32(s)
+    w = _f32(w)
+    T = s.shape[-1]
+    st = np.empty(T, dtype=np.uint32)
+    cost = np.empty(1, dtype=np.float32)
+    o = np.empty(1, dtype=np.uint32)
+    _check(lib().oracle_tailbiting_alg4(_p(C, ctypes.c_float), _p(s, ctypes.c_float),
+                                        _p(w, ctypes.c_float), T, L, k, _p(st, ctypes.c_uint32),
+                                        _p(cost, ctypes.c_float), _p(o, ctypes.c_uint32)),
+           "tailbiting_alg4")
+    return int(o[0])
+
+
+def tailbiting(C, s, w=None, L=16, k=2):
+    """Batch two-search tail-biting encode.  Returns (states u32, cost f32, mse f32)."""
+    C = _f32(C)
+    s = _f32(s)
+    one = s.ndim == 1
+    s2 = s.reshape(1, -1) if one else s
+    B, T = s2.shape
+    w2 = None if w is None else _f32(w).reshape(B, T)
+    st = np.empty((B, T), dtype=np.uint32)
+    cost = np.empty(B, dtype=np.float32)
+    mse = np.empty(B, dtype=np.float32)
+    _check(lib().oracle_tailbiting_alg4_batch(_p(C, ctypes.c_float), _p(s2, ctypes.c_float),
+                                              _p(w2, ctypes.c_float), B, T, L, k,
+                                              _p(st, ctypes.c_uint32), _p(cost, ctypes.c_float),
+                                              _p(mse, ctypes.c_float)), "tailbiting")
+    if one:
+        return st[0], cost[0], mse[0]
+    return st, cost, mse
+
+
+def tb_pack(states, L=16, k=2):
+    st = np.ascontiguousarray(states, dtype=np.uint32)
+    one = st.ndim == 1
+    st2 = st.reshape(1, -1) if one else st
+    B, T = st2.shape
+    W = tb_stream_words(L, k, T)
+    words = np.empty((B, W), dtype=np.uint32)
+    _check(lib().oracle_tb_pack_batch(_p(st2, ctypes.c_uint32), B, T, L, k,
+                                      _p(words, ctypes.c_uint32)), "tb_pack")
+    return words[0] if one else words
+
+
+def tb_decode(words, T, C, L=16, k=2):
+    """Cyclic window decode.  Returns (windows u32 [B][T], recon f32 [B][T])."""
+    C = _f32(C)
+    wd = np.ascontiguousarray(words, dtype=np.uint32)
+    one = wd.ndim == 1
+    wd2 = wd.reshape(1, -1) if one else wd
+    B = wd2.shape[0]
+    assert wd2.shape[1] == tb_stream_words(L, k, T)
+    win = np.empty((B, T), dtype=np.uint32)
+    rec = np.empty((B, T), dtype=np.float32)
+    _check(lib().oracle_tb_decode_batch(_p(wd2, ctypes.c_uint32), B, T, L, k,
+                                        _p(C, ctypes.c_float), _p(win, ctypes.c_uint32),
+                                        _p(rec, ctypes.c_float)), "tb_decode")
+    if one:
+        return win[0], rec[0]
+    return win, rec
+
+
+def brute_tailbiting(C, s, w=None, L=6, k=2):
+    """Returns (min cost over every cyclic walk f32, #walks attaining it)."""
+    C = _f32(C)
+    s = _f32(s)
+    w = _f32(w)
+    T = s.shape[-1]
+    best = np.empty(1, dtype=np.float32)
+    n = np.empty(1, dtype=np.int64)
+    _check(lib().oracle_brute_tailbiting(_p(C, ctypes.c_float), _p(s, ctypes.c_float),
+                                         _p(w, ctypes.c_float), T, L, k, _p(best, ctypes.c_float),
+                                         _p(n, ctypes.c_int64)), "brute_tailbiting")
+    return best[0], int(n[0])

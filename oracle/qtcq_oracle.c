@@ -564,3 +564,234 @@ int oracle_brute_bcjr(const float* C, const float* s, const float* w, int T, int
     free(st); free(E);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------ */
+/* Tail-biting trellis  ([QTIP] "Tail-biting is worth its complexity")               */
+/* ------------------------------------------------------------------------------ */
+
+/* A tail-biting walk is cyclic: the low L-k bits of the last state equal the high L-k
+ * bits of the first, so the stream is exactly k*T bits and weight t's state is the
+ * L-bit window starting at bit t*k read cyclically.  That needs k*T >= L (a stream at
+ * least one window long). */
+static int check_tailbiting(int T, int L, int k)
+{
+    return check_trellis(T, L, k) && (int64_t)k * T >= L;
+}
+
+int64_t oracle_tb_stream_bits(int L, int k, int T) { (void)L; return (int64_t)k * T; }
+int64_t oracle_tb_stream_words(int L, int k, int T) { return (oracle_tb_stream_bits(L, k, T) + 31) / 32; }
+
+/* Viterbi with both ends pinned to an overlap value o (an (L-k)-bit integer): the walk
+ * must start in a state whose high L-k bits are o and end in a state whose low L-k
+ * bits are o.  Exactly the plain search (same arithmetic, same tie rules) with the
+ * forbidden start states given cost +infinity and the final minimum taken over the
+ * allowed end states only (the lowest allowed state wins a tie). */
+int oracle_viterbi_pinned(const float* C, const float* s, const float* w, int T, int L, int k,
+                          uint32_t o, uint32_t* st, float* cost_out)
+{
+    if (!C || !s || !st || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    const uint32_t N = 1u << L;
+    const uint32_t K = 1u << k;
+    const uint32_t low_mask = (1u << (L - k)) - 1u;
+    if (o > low_mask) return ORC_EINVAL;
+    float* cost = (float*)malloc(sizeof(float) * N);
+    float* next = (float*)malloc(sizeof(float) * N);
+    uint32_t* back = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)T * N);
+    if (!cost || !next || !back) {
+        free(cost); free(next); free(back);
+        return ORC_ENOMEM;
+    }
+
+    for (uint32_t j = 0; j < N; ++j)
+        cost[j] = ((j >> k) == o) ? step_error(C[j], s[0], w, 0) : INFINITY;
+
+    for (int t = 1; t < T; ++t) {
+        for (uint32_t j = 0; j < N; ++j) {
+            uint32_t best_i = j >> k;
+            float best = cost[best_i];
+            for (uint32_t a = 1; a < K; ++a) {
+                uint32_t i = (j >> k) | (a << (L - k));
+                if (cost[i] < best) {
+                    best = cost[i];
+                    best_i = i;
+                }
+            }
+            back[(size_t)t * N + j] = best_i;
+            next[j] = best + step_error(C[j], s[t], w, t);
+        }
+        float* tmp = cost; cost = next; next = tmp;
+    }
+
+    /* allowed end states: j with (j & low_mask) == o, i.e. j = o + a * 2^(L-k) */
+    uint32_t jstar = o;
+    for (uint32_t a = 1; a < K; ++a) {
+        uint32_t j = o | (a << (L - k));
+        if (cost[j] < cost[jstar]) jstar = j;
+    }
+    *cost_out = cost[jstar];
+
+    st[T - 1] = jstar;
+    for (int t = T - 1; t > 0; --t)
+        st[t - 1] = back[(size_t)t * N + st[t]];
+
+    free(cost); free(next); free(back);
+    return ORC_OK;
+}
+
+/* Exact tail-biting optimum: one pinned search per overlap value, 2^(L-k) of them; the
+ * cheapest wins (the lowest overlap on a tie).  Practical for L <= 12. */
+int oracle_tailbiting_exact(const float* C, const float* s, const float* w, int T, int L, int k,
+                            uint32_t* st, float* cost_out)
+{
+    if (!C || !s || !st || !cost_out || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    uint32_t* cand = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    if (!cand) return ORC_ENOMEM;
+    float best = INFINITY;
+    const uint32_t n_over = 1u << (L - k);
+    for (uint32_t o = 0; o < n_over; ++o) {
+        float c;
+        int rc = oracle_viterbi_pinned(C, s, w, T, L, k, o, cand, &c);
+        if (rc) { free(cand); return rc; }
+        if (c < best) {
+            best = c;
+            memcpy(st, cand, sizeof(uint32_t) * T);
+        }
+    }
+    *cost_out = best;
+    free(cand);
+    return ORC_OK;
+}
+
+/* Two-search tail-biting (the page's Algorithm 4 summary): rotate the sequence by
+ * r = floor(T/2) so that its ends meet in the middle, run the free-start search on the
+ * rotated sequence, take the overlap from the state the rotated walk assigns to the
+ * original position 0 (its high L-k bits, which by the trellis rule also equal the
+ * low L-k bits of the state before it, the original position T-1), then search the
+ * original sequence with both ends pinned to that overlap.
+ * Rotated sequence: s'[t] = s[(t + r) mod T] (weights likewise); original position 0
+ * sits at rotated position (T - r) mod T.  *overlap_out (may be NULL) = the overlap. */
+int oracle_tailbiting_alg4(const float* C, const float* s, const float* w, int T, int L, int k,
+                           uint32_t* st, float* cost_out, uint32_t* overlap_out)
+{
+    if (!C || !s || !st || !cost_out || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    const int r = T / 2;
+    float* sr = (float*)malloc(sizeof(float) * T);
+    float* wr = w ? (float*)malloc(sizeof(float) * T) : NULL;
+    uint32_t* str = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    if (!sr || !str || (w && !wr)) { free(sr); free(wr); free(str); return ORC_ENOMEM; }
+    for (int t = 0; t < T; ++t) {
+        sr[t] = s[(t + r) % T];
+        if (w) wr[t] = w[(t + r) % T];
+    }
+    float c1;
+    int rc = oracle_viterbi(C, sr, wr, T, L, k, str, &c1);
+    if (!rc) {
+        const uint32_t o = str[(T - r) % T] >> k;
+        if (overlap_out) *overlap_out = o;
+        rc = oracle_viterbi_pinned(C, s, w, T, L, k, o, st, cost_out);
+    }
+    free(sr); free(wr); free(str);
+    return rc;
+}
+
+/* Batch driver for the two-search encoder: st[B][T], cost[B], mse[B] (cost, mse may
+ * be NULL). */
+int oracle_tailbiting_alg4_batch(const float* C, const float* s, const float* w, int64_t B,
+                                 int T, int L, int k, uint32_t* st, float* cost, float* mse)
+{
+    if (B < 0) return ORC_EINVAL;
+    for (int64_t b = 0; b < B; ++b) {
+        float c;
+        int rc = oracle_tailbiting_alg4(C, s + b * T, w ? w + b * T : NULL, T, L, k,
+                                        st + b * T, &c, NULL);
+        if (rc) return rc;
+        if (cost) cost[b] = c;
+        if (mse) mse[b] = mse_of(c, T);
+    }
+    return ORC_OK;
+}
+
+/* Tail-biting pack: each state contributes its k high bits, state t at stream bits
+ * [t*k, t*k + k) (MSB first); the window rule then reproduces every state, the ones
+ * near the end wrapping round to the start of the stream.  Pad bits = 0. */
+int oracle_tb_pack(const uint32_t* st, int T, int L, int k, uint32_t* words)
+{
+    if (!st || !words || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    int64_t nw = oracle_tb_stream_words(L, k, T);
+    memset(words, 0, sizeof(uint32_t) * (size_t)nw);
+    for (int t = 0; t < T; ++t) {
+        uint32_t top = st[t] >> (L - k);
+        for (int b = 0; b < k; ++b)
+            put_bit(words, (int64_t)t * k + b, (top >> (k - 1 - b)) & 1u);
+    }
+    return ORC_OK;
+}
+
+int oracle_tb_pack_batch(const uint32_t* st, int64_t B, int T, int L, int k, uint32_t* words)
+{
+    int64_t nw = oracle_tb_stream_words(L, k, T);
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_tb_pack(st + b * T, T, L, k, words + b * nw);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* Tail-biting window decode: weight t reads stream bits t*k, t*k + 1, ..., t*k + L - 1,
+ * every position taken modulo the stream length k*T. */
+int oracle_tb_decode(const uint32_t* words, int T, int L, int k, const float* C,
+                     uint32_t* windows, float* recon)
+{
+    if (!words || !C || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    const int64_t nbits = oracle_tb_stream_bits(L, k, T);
+    for (int t = 0; t < T; ++t) {
+        uint32_t win = 0;
+        for (int b = 0; b < L; ++b)
+            win = (win << 1) | get_bit(words, ((int64_t)t * k + b) % nbits);
+        if (windows) windows[t] = win;
+        if (recon) recon[t] = C[win];
+    }
+    return ORC_OK;
+}
+
+int oracle_tb_decode_batch(const uint32_t* words, int64_t B, int T, int L, int k, const float* C,
+                           uint32_t* windows, float* recon)
+{
+    int64_t nw = oracle_tb_stream_words(L, k, T);
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_tb_decode(words + b * nw, T, L, k, C, windows ? windows + b * T : NULL,
+                                  recon ? recon + b * T : NULL);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* Brute force over every tail-biting walk: all 2^(k*T) cyclic streams, each walk's
+ * cost summed sequentially in binary32.  *best_cost = the minimum; *n_optimal = how
+ * many walks attain it. */
+int oracle_brute_tailbiting(const float* C, const float* s, const float* w, int T, int L, int k,
+                            float* best_cost, int64_t* n_optimal)
+{
+    if (!C || !s || !best_cost || !check_tailbiting(T, L, k)) return ORC_EINVAL;
+    const int nbits = k * T;
+    if (nbits > 24) return ORC_EINVAL;
+    const uint32_t mask = (1u << L) - 1u;
+    float best = INFINITY;
+    int64_t count = 0;
+    for (uint64_t n = 0; n < (1ull << nbits); ++n) {
+        float acc = 0.0f;
+        for (int t = 0; t < T; ++t) {
+            uint32_t win = 0;
+            for (int b = 0; b < L; ++b) {
+                int p = (t * k + b) % nbits;              /* stream bit p, MSB first */
+                win = (win << 1) | (uint32_t)((n >> (nbits - 1 - p)) & 1u);
+            }
+            acc = acc + step_error(C[win & mask], s[t], w, t);
+        }
+        if (acc < best) { best = acc; count = 1; }
+        else if (acc == best) ++count;
+    }
+    *best_cost = best;
+    if (n_optimal) *n_optimal = count;
+    return ORC_OK;
+}

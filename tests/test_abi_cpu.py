@@ -112,6 +112,38 @@ def test_bcjr_validation(nat):
     assert st(None, None, 0, 256, 16, 2, 0, 1.0, None, None, None, 0, None) == nat.QTCQ_OK
 
 
+def test_tailbiting_sizes(nat):
+    assert nat.qtcq_tailbiting_words(16, 2, 256) == 16     # exactly 2T bits, word-aligned
+    assert nat.qtcq_tailbiting_words(16, 2, 8) == 1
+    assert nat.qtcq_tailbiting_words(16, 2, 7) == -1       # 14 bits < one 16-bit window
+    assert nat.qtcq_tailbiting_words(6, 2, 3) == 1
+    assert nat.qtcq_tailbiting_words(16, 2, 17) == 2
+    per = nat.qtcq_tailbiting_workspace_bytes(1, 256, 16, 2)
+    assert per == nat.qtcq_encode_workspace_bytes(1, 256, 16, 2) + 4
+    assert nat.qtcq_tailbiting_workspace_bytes(5, 256, 16, 2) == 5 * per
+    assert nat.qtcq_tailbiting_workspace_bytes(1, 7, 16, 2) == 0
+    assert nat.qtcq_tailbiting_workspace_bytes(1, 256, 9, 2) == 0
+
+
+def test_tailbiting_validation(nat):
+    enc = lambda *a: nat.raw_status("qtcq_tailbiting_encode", *a)
+    ws = nat.qtcq_tailbiting_workspace_bytes(1, 256, 16, 2)
+    # seq, w, B, T, L, k, code, bits, mse, states, ws, wsb, stream
+    assert enc(FAKE, None, 4, 7, 16, 2, 0, FAKE, None, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert enc(FAKE, None, 4, 256, 16, 2, 7, FAKE, None, None, FAKE, ws, None) == nat.QTCQ_ERR_UNSUPPORTED
+    assert enc(FAKE, None, 4, 256, 16, 2, 0, None, None, None, FAKE, ws, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert enc(FAKE, None, 4, 256, 16, 2, 0, FAKE, None, None, FAKE, ws - 1, None) == nat.QTCQ_ERR_WORKSPACE
+    assert enc(FAKE, None, 4, 256, 16, 2, 0, FAKE, None, None, FAKE + 8, ws, None) == nat.QTCQ_ERR_WORKSPACE
+    assert enc(None, None, 0, 256, 16, 2, 0, None, None, None, None, 0, None) == nat.QTCQ_OK
+    dec = lambda *a: nat.raw_status("qtcq_tailbiting_decode", *a)
+    # bits, B, T, L, k, code, recon, seq, w, mse, stream
+    assert dec(FAKE, 4, 7, 16, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert dec(FAKE, 4, 256, 16, 2, 0, None, None, None, None, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert dec(FAKE, 4, 256, 16, 2, 0, None, None, None, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert dec(FAKE, 4, 256, 11, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_ERR_UNSUPPORTED
+    assert dec(None, 0, 256, 16, 2, 0, FAKE, None, None, None, None) == nat.QTCQ_OK
+
+
 def test_code_table_validation(nat):
     assert nat.raw_status("qtcq_code_table", 0, 16, None, None) == nat.QTCQ_ERR_INVALID_ARG
     assert nat.raw_status("qtcq_code_table", 0, 25, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG

@@ -53,6 +53,12 @@ _SIGS = {
     "qtcq_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "qtcq_bcjr_soft": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp,
                               _vp, _sz, _vp]),
+    "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
+    "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
+    "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]),
+    "qtcq_tailbiting_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+                                      _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -111,6 +117,29 @@ def qtcq_bcjr_soft(seq: int, err_w, B: int, T: int, L: int, k: int, code: int,
     _check(_lib.qtcq_bcjr_soft(_ptr(seq), _ptr(err_w), B, T, L, k, code, float(temperature),
                                _ptr(soft), _ptr(log_z), _ptr(workspace), workspace_bytes,
                                _ptr(stream)), "qtcq_bcjr_soft")
+
+
+def qtcq_tailbiting_words(L: int, k: int, T: int) -> int:
+    return _lib.qtcq_tailbiting_words(L, k, T)
+
+
+def qtcq_tailbiting_workspace_bytes(B: int, T: int, L: int, k: int) -> int:
+    return _lib.qtcq_tailbiting_workspace_bytes(B, T, L, k)
+
+
+def qtcq_tailbiting_encode(seq: int, err_w, B: int, T: int, L: int, k: int, code: int,
+                           bits: int, mse, states, workspace: int, workspace_bytes: int,
+                           stream: int = 0) -> None:
+    _check(_lib.qtcq_tailbiting_encode(_ptr(seq), _ptr(err_w), B, T, L, k, code, _ptr(bits),
+                                       _ptr(mse), _ptr(states), _ptr(workspace), workspace_bytes,
+                                       _ptr(stream)), "qtcq_tailbiting_encode")
+
+
+def qtcq_tailbiting_decode(bits: int, B: int, T: int, L: int, k: int, code: int, recon, seq,
+                           err_w, mse, stream: int = 0) -> None:
+    _check(_lib.qtcq_tailbiting_decode(_ptr(bits), B, T, L, k, code, _ptr(recon), _ptr(seq),
+                                       _ptr(err_w), _ptr(mse), _ptr(stream)),
+           "qtcq_tailbiting_decode")
 
 
 def raw_status(name: str, *args) -> int:

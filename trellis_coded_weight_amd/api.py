@@ -104,3 +104,58 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
                        _code(code), temperature, soft.data_ptr(), logz.data_ptr(),
                        workspace.data_ptr(), workspace.numel(), _stream())
     return soft, logz
+
+
+def tailbiting_words(L: int = 16, k: int = 2, T: int = 256) -> int:
+    return nat.qtcq_tailbiting_words(L, k, T)
+
+
+def tailbiting_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
+                         max_bytes: int | None = None) -> torch.Tensor:
+    need = nat.qtcq_tailbiting_workspace_bytes(B, T, L, k)
+    if max_bytes is not None:
+        per = nat.qtcq_tailbiting_workspace_bytes(1, T, L, k)
+        need = max(per, min(need, max_bytes // per * per))
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def tailbiting_encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16,
+                      k: int = 2, code="1mad", want_states: bool = False,
+                      workspace: torch.Tensor | None = None):
+    """Tail-biting encode (two searches per sequence) of [B][T] targets.  Returns
+    (bits [B][ceil(kT/32)] int32 view of uint32 words, mse [B], states [B][T] or None)."""
+    _dev_f32(seq, "seq")
+    B, T = seq.shape
+    if weights is not None:
+        _dev_f32(weights, "weights")
+        if weights.shape != seq.shape:
+            raise ValueError("weights must have the shape of seq")
+    W = nat.qtcq_tailbiting_words(L, k, T)
+    if W < 0:
+        raise ValueError("tail-biting needs k*T >= L")
+    bits = torch.empty((B, W), dtype=torch.int32, device=seq.device)
+    mse = torch.empty(B, dtype=torch.float32, device=seq.device)
+    states = torch.empty((B, T), dtype=torch.int32, device=seq.device) if want_states else None
+    if workspace is None:
+        workspace = tailbiting_workspace(B, T, L, k)
+    nat.qtcq_tailbiting_encode(seq.data_ptr(), None if weights is None else weights.data_ptr(), B,
+                               T, L, k, _code(code), bits.data_ptr(), mse.data_ptr(),
+                               None if states is None else states.data_ptr(),
+                               workspace.data_ptr(), workspace.numel(), _stream())
+    return bits, mse, states
+
+
+def tailbiting_decode(bits: torch.Tensor, T: int, L: int = 16, k: int = 2, code="1mad",
+                      seq: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+                      want_recon: bool = True, want_mse: bool = False):
+    """Cyclic window decode of [B][W] tail-biting streams.  Returns (recon or None,
+    mse or None)."""
+    B = bits.shape[0]
+    recon = torch.empty((B, T), dtype=torch.float32, device=bits.device) if want_recon else None
+    mse = torch.empty(B, dtype=torch.float32, device=bits.device) if want_mse else None
+    nat.qtcq_tailbiting_decode(bits.data_ptr(), B, T, L, k, _code(code),
+                               None if recon is None else recon.data_ptr(),
+                               None if seq is None else seq.data_ptr(),
+                               None if weights is None else weights.data_ptr(),
+                               None if mse is None else mse.data_ptr(), _stream())
+    return recon, mse

@@ -40,8 +40,10 @@ struct DecodeTile {
 };
 
 // grid.x = ceil(B / SB), block = 256.  recon may be NULL (MSE only); mse may be NULL
-// (decode only, MSE_ = false).
-template <int L, int CODE, bool MSE_, bool WEIGHTED>
+// (decode only, MSE_ = false).  TB: tail-biting streams of exactly 2T bits, whose
+// windows are read cyclically (a window running past the end continues at bit 0;
+// 2T >= L, so it wraps at most once).
+template <int L, int CODE, bool MSE_, bool WEIGHTED, bool TB = false>
 __global__ void __launch_bounds__(DecodeTile::kThreads)
 decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
             const float* __restrict__ wts, int64_t B, int T, int W, int SB,
@@ -90,7 +92,14 @@ decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
         const uint32_t lo = (wi + 1 < W) ? lbits[r * W + wi + 1] : 0u;
         // bits [p, p + 32) of the stream, then the top L of them
         const uint32_t top = __builtin_amdgcn_alignbit(hi, lo, (32 - (p & 31)) & 31);
-        const uint32_t win = ((p & 31) ? top : hi) >> (32 - L);
+        uint32_t win = ((p & 31) ? top : hi) >> (32 - L);
+        if constexpr (TB) {
+            const int nf = 2 * T - p;          // stream bits left from p
+            if (nf < L) {                      // the first nf bits, then L - nf from bit 0
+                const uint32_t head = lbits[r * W];
+                win = ((((p & 31) ? top : hi) >> (32 - nf)) << (L - nf)) | (head >> (32 - (L - nf)));
+            }
+        }
         const float c = code_value<CODE>(win);
         if (recon) recon[base + i] = c;
         if constexpr (MSE_) lerr[r * ES + t] = step_err<WEIGHTED>(c, sv[u], wv[u]);

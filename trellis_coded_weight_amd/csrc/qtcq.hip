@@ -30,6 +30,10 @@ int64_t stream_words(int L, int k, int T)
     return ((int64_t)L + (int64_t)k * (T - 1) + 31) / 32;
 }
 
+// tail-biting: exactly k*T bits, and at least one window long
+bool tailbiting_ok(int L, int k, int T) { return (int64_t)k * T >= L; }
+int64_t tb_stream_words(int k, int T) { return ((int64_t)k * T + 31) / 32; }
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -59,7 +63,7 @@ qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n
     uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
     float* fin_cost = reinterpret_cast<float*>(fin + n);
     hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3((unsigned)((n + 1) / 2)), dim3(Tr::kThreads),
-                       0, st, seq, w, T, b0, n, bp, fin, fin_cost, mse);
+                       0, st, seq, w, T, b0, n, 0, nullptr, bp, fin, fin_cost, mse);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     const int Wd = (int)stream_words(L, 2, T);
@@ -82,6 +86,69 @@ qtcq_status encode_all(const float* seq, const float* w, int64_t B, int T, uint3
     return QTCQ_OK;
 }
 
+// ---- tail-biting encode -------------------------------------------------------------
+// Two searches per sequence: the free-start search over the targets rotated by T/2, the
+// seam (the overlap read off the state of original position 0), then the search over
+// the original targets with both ends pinned to the overlap, traced back and packed
+// as a 2T-bit cyclic stream.  Workspace per sequence: the encode layout plus the
+// overlap word.
+
+size_t tb_bytes_per_seq(int T, int L) { return encode_bytes_per_seq(T, L) + 4; }
+
+template <int L, int CODE, bool W>
+qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, int T,
+                     uint32_t* bits, float* mse, uint32_t* states, char* ws, hipStream_t st)
+{
+    using Tr = Trellis<L>;
+    uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
+    float* fin_cost = reinterpret_cast<float*>(fin + n);
+    uint32_t* overlap = reinterpret_cast<uint32_t*>(fin_cost + n);
+    const dim3 grid((unsigned)((n + 1) / 2)), block(Tr::kThreads);
+    const int rot = T / 2;
+    hipLaunchKernelGGL((viterbi_forward<L, CODE, W, false>), grid, block, 0, st, seq, w, T, b0, n,
+                       rot, nullptr, bp, fin, fin_cost, nullptr);
+    qtcq_status rc = launch_status();
+    if (rc != QTCQ_OK) return rc;
+    hipLaunchKernelGGL((viterbi_seam<L>), dim3(blocks_for(n, 256)), dim3(256), 0, st, bp, fin, T, n,
+                       (T - rot) % T, overlap);
+    rc = launch_status();
+    if (rc != QTCQ_OK) return rc;
+    hipLaunchKernelGGL((viterbi_forward<L, CODE, W, true>), grid, block, 0, st, seq, w, T, b0, n, 0,
+                       overlap, bp, fin, fin_cost, mse);
+    rc = launch_status();
+    if (rc != QTCQ_OK) return rc;
+    hipLaunchKernelGGL((viterbi_traceback<L, true>), dim3(blocks_for(n, 256)), dim3(256), 0, st,
+                       bp, fin, T, n, b0, (int)tb_stream_words(2, T), bits, states);
+    return launch_status();
+}
+
+template <int L, int CODE, bool W>
+qtcq_status tb_all(const float* seq, const float* w, int64_t B, int T, uint32_t* bits,
+                   float* mse, uint32_t* states, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t per_chunk = (int64_t)(ws_bytes / tb_bytes_per_seq(T, L));
+    for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
+        const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
+        qtcq_status rc = tb_chunk<L, CODE, W>(seq, w, b0, n, T, bits, mse, states,
+                                              static_cast<char*>(ws), st);
+        if (rc != QTCQ_OK) return rc;
+    }
+    return QTCQ_OK;
+}
+
+template <int L>
+qtcq_status tb_dispatch_code(int code, bool weighted, const float* seq, const float* w,
+                             int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
+                             void* ws, size_t wsb, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return weighted ? tb_all<L, kCode1Mad, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
+                        : tb_all<L, kCode1Mad, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
+    return weighted ? tb_all<L, kCode3Inst, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
+                    : tb_all<L, kCode3Inst, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
+}
+
 template <int L>
 qtcq_status encode_dispatch_code(int code, bool weighted, const float* seq, const float* w,
                                  int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
@@ -96,34 +163,38 @@ qtcq_status encode_dispatch_code(int code, bool weighted, const float* seq, cons
 
 // ---- decode ------------------------------------------------------------------------
 
-template <int L, int CODE>
+template <int L, int CODE, bool TB>
 qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, const float* seq,
                         const float* w, float* mse, hipStream_t st)
 {
-    const int Wd = (int)stream_words(L, 2, T);
+    const int Wd = (int)(TB ? tb_stream_words(2, T) : stream_words(L, 2, T));
     const int SB = DecodeTile::seqs(T);
     if (SB * Wd > DecodeTile::kBitsWords || SB * DecodeTile::err_stride(T) > DecodeTile::kErrFloats)
         return QTCQ_ERR_UNSUPPORTED;      // not reachable for T <= 4096, L <= 16
     const dim3 grid(blocks_for(B, SB)), block(DecodeTile::kThreads);
     const size_t lds = DecodeTile::lds_bytes(T, Wd, mse != nullptr);
     if (!mse)
-        hipLaunchKernelGGL((decode_tile<L, CODE, false, false>), grid, block, lds, st, bits, seq,
-                           w, B, T, Wd, SB, recon, mse);
+        hipLaunchKernelGGL((decode_tile<L, CODE, false, false, TB>), grid, block, lds, st, bits,
+                           seq, w, B, T, Wd, SB, recon, mse);
     else if (w)
-        hipLaunchKernelGGL((decode_tile<L, CODE, true, true>), grid, block, lds, st, bits, seq, w,
-                           B, T, Wd, SB, recon, mse);
-    else
-        hipLaunchKernelGGL((decode_tile<L, CODE, true, false>), grid, block, lds, st, bits, seq,
+        hipLaunchKernelGGL((decode_tile<L, CODE, true, true, TB>), grid, block, lds, st, bits, seq,
                            w, B, T, Wd, SB, recon, mse);
+    else
+        hipLaunchKernelGGL((decode_tile<L, CODE, true, false, TB>), grid, block, lds, st, bits,
+                           seq, w, B, T, Wd, SB, recon, mse);
     return launch_status();
 }
 
 template <int L>
-qtcq_status decode_dispatch_code(int code, const uint32_t* bits, int64_t B, int T, float* recon,
-                                 const float* seq, const float* w, float* mse, hipStream_t st)
+qtcq_status decode_dispatch_code(int code, bool tb, const uint32_t* bits, int64_t B, int T,
+                                 float* recon, const float* seq, const float* w, float* mse,
+                                 hipStream_t st)
 {
-    if (code == QTCQ_CODE_1MAD) return decode_impl<L, kCode1Mad>(bits, B, T, recon, seq, w, mse, st);
-    return decode_impl<L, kCode3Inst>(bits, B, T, recon, seq, w, mse, st);
+    if (code == QTCQ_CODE_1MAD)
+        return tb ? decode_impl<L, kCode1Mad, true>(bits, B, T, recon, seq, w, mse, st)
+                  : decode_impl<L, kCode1Mad, false>(bits, B, T, recon, seq, w, mse, st);
+    return tb ? decode_impl<L, kCode3Inst, true>(bits, B, T, recon, seq, w, mse, st)
+              : decode_impl<L, kCode3Inst, false>(bits, B, T, recon, seq, w, mse, st);
 }
 
 // ---- bcjr --------------------------------------------------------------------------
@@ -182,6 +253,11 @@ template <int L>
 struct EncodeF {
     template <typename... A>
     static qtcq_status run(A... a) { return encode_dispatch_code<L>(a...); }
+};
+template <int L>
+struct TailBitingF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return tb_dispatch_code<L>(a...); }
 };
 template <int L>
 struct DecodeF {
@@ -266,7 +342,49 @@ qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, in
     if (mse && !seq) return QTCQ_ERR_INVALID_ARG;
     if (B == 0) return QTCQ_OK;
     if (!bits) return QTCQ_ERR_INVALID_ARG;
-    return by_L<DecodeF>(L, code, bits, B, T, recon, seq, err_w, mse, as_stream(stream));
+    return by_L<DecodeF>(L, code, false, bits, B, T, recon, seq, err_w, mse, as_stream(stream));
+}
+
+int64_t qtcq_tailbiting_words(int L, int k, int T)
+{
+    if (k < 1 || L < k || L > 32 || T < 1 || !tailbiting_ok(L, k, T)) return -1;
+    return tb_stream_words(k, T);
+}
+
+size_t qtcq_tailbiting_workspace_bytes(int64_t B, int T, int L, int k)
+{
+    if (!supported_trellis(L, k) || T < 1 || T > kMaxT || B < 0 || !tailbiting_ok(L, k, T))
+        return 0;
+    return (size_t)(B > 0 ? B : 1) * tb_bytes_per_seq(T, L);
+}
+
+qtcq_status qtcq_tailbiting_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
+                                   int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (!tailbiting_ok(L, k, T)) return QTCQ_ERR_INVALID_ARG;
+    if (B == 0) return QTCQ_OK;
+    if (!seq || !bits) return QTCQ_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < tb_bytes_per_seq(T, L))
+        return QTCQ_ERR_WORKSPACE;
+    return by_L<TailBitingF>(L, code, err_w != nullptr, seq, err_w, B, T, bits, mse, states,
+                             workspace, workspace_bytes, as_stream(stream));
+}
+
+qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+                                   float* recon, const float* seq, const float* err_w, float* mse,
+                                   void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (!tailbiting_ok(L, k, T)) return QTCQ_ERR_INVALID_ARG;
+    if (!recon && !mse) return QTCQ_ERR_INVALID_ARG;
+    if (mse && !seq) return QTCQ_ERR_INVALID_ARG;
+    if (B == 0) return QTCQ_OK;
+    if (!bits) return QTCQ_ERR_INVALID_ARG;
+    return by_L<DecodeF>(L, code, true, bits, B, T, recon, seq, err_w, mse, as_stream(stream));
 }
 
 qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int T, int L, int k,

@@ -92,6 +92,12 @@ constexpr int kBitDelay = 1;
 // Forward pass over a pair of sequences per workgroup.
 //   grid.x = ceil(n / 2) for the n sequences of the chunk, block = Trellis<L>::kThreads.
 //   seq, wts : [*][T]; the workgroup takes rows b0 + 2*blockIdx.x (+1 if < b0 + n)
+//   rot      : the search runs over the rotated targets s'[t] = s[(t + rot) mod T]
+//              (0 <= rot < T; the tail-biting encoder's first search uses T/2)
+//   pin      : PINNED only -- [n] overlap o per sequence (an (L-2)-bit value): the walk
+//              must start in a state whose high L-2 bits are o (group o, so mu_0 = +inf
+//              outside group o) and end in a state whose low L-2 bits are o (the final
+//              minimum runs over the four states a*2^(L-2) + o)
 //   bp       : [n][T-1][kBpWords] 2-bit argmins of each step
 //   fin      : [n] final state (uint32) ; fin_cost [n]
 //   mse      : [*] (row b0 + q) or nullptr
@@ -101,11 +107,11 @@ constexpr int kBitDelay = 1;
 // minima: a buffer is only written in the phase after every thread's reads of it have
 // completed (a barrier in between), and only read after the barrier that follows its
 // writes.  The code-value registers are shared by both sequences.
-template <int L, int CODE, bool WEIGHTED>
+template <int L, int CODE, bool WEIGHTED, bool PINNED = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
-                int64_t n, uint32_t* __restrict__ bp, uint32_t* __restrict__ fin,
-                float* __restrict__ fin_cost, float* __restrict__ mse)
+                int64_t n, int rot, const uint32_t* __restrict__ pin, uint32_t* __restrict__ bp,
+                uint32_t* __restrict__ fin, float* __restrict__ fin_cost, float* __restrict__ mse)
 {
     using Tr = Trellis<L>;
     constexpr int NB = Tr::kButterflies;
@@ -138,11 +144,25 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
                 __builtin_amdgcn_sched_barrier(0);
             }
 
-    // mu_0 = +0 everywhere, so cost_0 = fl(0 + e_0) = e_0
+    // mu_0 = +0 everywhere, so cost_0 = fl(0 + e_0) = e_0; pinned: +inf outside group o,
+    // so cost_0 = +inf for every start state outside the allowed four
+    if constexpr (PINNED) {
+        const uint32_t oA = pin[qa], oB = pin[qb];
+        const float inf = __builtin_inff();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        muA[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
-        muB[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t g = 4u * (uint32_t)(tid + r * NT);
+            muA[tid + r * NT] = make_float4(g == oA ? 0.f : inf, g + 1 == oA ? 0.f : inf,
+                                            g + 2 == oA ? 0.f : inf, g + 3 == oA ? 0.f : inf);
+            muB[tid + r * NT] = make_float4(g == oB ? 0.f : inf, g + 1 == oB ? 0.f : inf,
+                                            g + 2 == oB ? 0.f : inf, g + 3 == oB ? 0.f : inf);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            muA[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
+            muB[tid + r * NT] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     __syncthreads();
 
@@ -199,11 +219,16 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         return word;
     };
 
+    // A's first inputs: mu_0 (all +0 unless pinned, so no LDS read is needed then)
     float inA[4][4], inB[4][4];
+    if constexpr (PINNED) {
+        load_in(muA, inA);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) inA[r][a] = 0.f;
+            for (int a = 0; a < 4; ++a) inA[r][a] = 0.f;
+    }
 
     // Targets (and weights) go through a small LDS ring of two 256-step chunks per
     // sequence and are read one phase ahead with the input loads: a per-step scalar
@@ -217,11 +242,13 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         const int j = k * kChunk;
         for (int i = tid; i < kChunk; i += NT) {
             const bool ok = j + i < T;
-            ring[0][k & 1][i] = ok ? sa[j + i] : 0.f;
-            ring[1][k & 1][i] = ok ? sb[j + i] : 0.f;
+            int src = j + i + rot;             // rotated step index, < 2T
+            if (src >= T) src -= T;
+            ring[0][k & 1][i] = ok ? sa[src] : 0.f;
+            ring[1][k & 1][i] = ok ? sb[src] : 0.f;
             if constexpr (WEIGHTED) {
-                ring[2][k & 1][i] = ok ? wa[j + i] : 0.f;
-                ring[3][k & 1][i] = ok ? wb[j + i] : 0.f;
+                ring[2][k & 1][i] = ok ? wa[src] : 0.f;
+                ring[3][k & 1][i] = ok ? wb[src] : 0.f;
             }
         }
     };
@@ -257,14 +284,16 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     }
 
     // final costs cost_{T-1}(i) = mu_{T-1}[i >> 2] + e_{T-1}(i); lowest i wins ties
+    const int last = (T - 1 + rot) % T;    // the last step's target index
     auto finish = [&](const float4* mu4, const float* s, const float* w, int64_t q) {
         const float* fin_mu = reinterpret_cast<const float*>(mu4);
         // the thread index through an opaque move: keeps the epilogue's address
         // arithmetic from being hoisted above the step loop (where it would be spilled)
         int tid = threadIdx.x;
         asm volatile("v_mov_b32 %0, %0" : "+v"(tid));
-        const float sp = to_vgpr(s[T - 1]);
-        const float wp = WEIGHTED ? to_vgpr(w[T - 1]) : 1.0f;
+        const float sp = to_vgpr(s[last]);
+        const float wp = WEIGHTED ? to_vgpr(w[last]) : 1.0f;
+        const uint32_t o = PINNED ? pin[q] : 0u;
         float best = __builtin_inff();
         uint32_t bi = 0xFFFFFFFFu;
 #pragma unroll
@@ -275,6 +304,8 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     float c = in + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
+                    // pinned: only the end states whose low L-2 bits are o take part
+                    if (PINNED && (uint32_t)(4 * (tid + r * NT) + x) != o) continue;
                     if (c < best) {   // states visited in increasing order
                         best = c;
                         bi = (uint32_t)(a * M + 4 * (tid + r * NT) + x);
@@ -313,9 +344,12 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
 }
 
 // Traceback and pack.  One thread per sequence of the chunk: walks the backpointers
-// from the final state to t = 0 and writes the stream (start state's L bits, then the
-// 2 new bits of every later state, MSB first) and optionally the states.
-template <int L>
+// from the final state to t = 0 and writes the stream and optionally the states.
+//   plain (TB = false): the start state's L bits, then the 2 new bits of every later
+//     state, MSB first -- L + 2(T-1) bits;
+//   tail-biting (TB = true): the 2 high bits of every state st[t] at stream bits
+//     [2t, 2t + 2) -- exactly 2T bits; the cyclic window rule restores every state.
+template <int L, bool TB = false>
 __global__ void __launch_bounds__(256)
 viterbi_traceback(const uint32_t* __restrict__ bp, const uint32_t* __restrict__ fin, int T,
                   int64_t n, int64_t b0, int W, uint32_t* __restrict__ bits,
@@ -329,15 +363,17 @@ viterbi_traceback(const uint32_t* __restrict__ bp, const uint32_t* __restrict__ 
     uint32_t* st = states ? states + (b0 + i) * (int64_t)T : nullptr;
 
     uint32_t j = fin[i];
-    const int nbits = L + 2 * (T - 1);
+    const int nbits = TB ? 2 * T : L + 2 * (T - 1);
     int curw = (nbits - 1) >> 5;
     uint32_t acc = 0;
     for (int t = T - 1; t >= 1; --t) {
         if (st) st[t] = j;
-        const int p = L + 2 * (t - 1);              // stream position of st[t]'s new bits
+        // stream position of the 2 bits st[t] contributes: its high bits (tail-biting)
+        // or the bits that entered its window (plain)
+        const int p = TB ? 2 * t : L + 2 * (t - 1);
         const int wi = p >> 5;
         if (wi != curw) { out[curw] = acc; curw = wi; acc = 0; }
-        acc |= (j & 3u) << (30 - (p & 31));
+        acc |= ((TB ? j >> (L - 2) : j) & 3u) << (30 - (p & 31));
         const uint32_t m = j >> 2;                   // group of j's predecessors
         const uint32_t word = bpq[(int64_t)(t - 1) * Tr::kBpWords + Tr::bp_word(m)];
         const uint32_t a = (word >> Tr::bp_shift(m)) & 3u;
@@ -345,8 +381,29 @@ viterbi_traceback(const uint32_t* __restrict__ bp, const uint32_t* __restrict__ 
     }
     if (st) st[0] = j;
     if (curw != 0) { out[curw] = acc; acc = 0; }
-    acc |= j << (32 - L);
+    acc |= TB ? (j >> (L - 2)) << 30 : j << (32 - L);
     out[0] = acc;
+}
+
+// Seam of the tail-biting encoder's first (rotated) search: walks back from the final
+// state to step pos and stores the high L-2 bits of that state (the overlap the second
+// search pins both ends to).  One thread per sequence of the chunk; 0 <= pos < T.
+template <int L>
+__global__ void __launch_bounds__(256)
+viterbi_seam(const uint32_t* __restrict__ bp, const uint32_t* __restrict__ fin, int T,
+             int64_t n, int pos, uint32_t* __restrict__ overlap)
+{
+    using Tr = Trellis<L>;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t* bpq = bp + i * (int64_t)(T - 1) * Tr::kBpWords;
+    uint32_t j = fin[i];
+    for (int t = T - 1; t > pos; --t) {
+        const uint32_t m = j >> 2;
+        const uint32_t word = bpq[(int64_t)(t - 1) * Tr::kBpWords + Tr::bp_word(m)];
+        j = m | (((word >> Tr::bp_shift(m)) & 3u) << (L - 2));
+    }
+    overlap[i] = j >> 2;
 }
 
 }  // namespace qtcq

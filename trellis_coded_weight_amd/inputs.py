@@ -25,6 +25,8 @@ WORKLOADS = {
     "enc4096x14336_3inst": dict(B=229376, code="3inst", weighted=False, seed=3),
     "enc4096x4096_1mad_weighted": dict(B=65536, code="1mad", weighted=True, seed=4, wseed=40),
     "bcjr4096x4096_1mad": dict(B=65536, code="1mad", weighted=False, seed=5),
+    "tb4096x4096_1mad": dict(B=65536, code="1mad", weighted=False, seed=6),
+    "tb4096x14336_3inst": dict(B=229376, code="3inst", weighted=False, seed=7),
 }
 
 
