@@ -33,6 +33,13 @@
  * the magic constant is the fp16 nearest 0.922, the halves are added in fp16 (RNE)
  * and the sum is divided by the printed raw sigma 1.244.  BCJR energy = the Viterbi
  * path cost (a sum), path weight exp(-E / tau), uniform start prior, binary64.
+ * Tail-biting: the walk is cyclic (low L-k bits of the last state = high L-k bits of
+ * the first) and needs k*T >= L; the stream holds each state's k high bits at bits
+ * [t*k, t*k + k) and windows are read modulo k*T; the two-search encoder rotates by
+ * floor(T/2) with s'[t] = s[(t + r) mod T], takes the overlap from the high L-k bits
+ * of the rotated walk's state at original position 0, and pins the start to states
+ * with those high bits and the end to states with those low bits; the exact solver's
+ * ties go to the lowest overlap.
  *
  * PARITY UNPINNED: the LCG inside 3INST.  The page names no LCG for 3INST; every
  * other 3INST choice above is pinned by the printed raw sigma, the LCG choice is not
