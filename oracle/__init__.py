@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
                                              i64p]),
             "oracle_brute_bcjr": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, c_dbl, f64p,
                                           f64p]),
+            "oracle_bcjr_vjp_batch": (c_int, [f32p, f32p, f32p, c_i64, c_int, c_int, c_int, c_dbl,
+                                              f64p, f64p, f64p]),
+            "oracle_brute_bcjr_vjp": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, c_dbl, f64p,
+                                              f64p]),
             "oracle_tb_stream_bits": (c_i64, [c_int, c_int, c_int]),
             "oracle_tb_stream_words": (c_i64, [c_int, c_int, c_int]),
             "oracle_viterbi_pinned": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, c_u32,
@@ -222,6 +226,41 @@ def bcjr(C, s, tau, w=None, L=16, k=2):
     if one:
         return soft[0], logz[0]
     return soft, logz
+
+
+def bcjr_vjp(C, s, tau, g, w=None, L=16, k=2):
+    """Batch fp64 vector-Jacobian product of the soft codeword w.r.t. the targets.
+    g: upstream gradient, shape of s.  Returns (grad f64 [B][T], soft f64 [B][T])."""
+    C = _f32(C)
+    s = _f32(s)
+    one = s.ndim == 1
+    s2 = s.reshape(1, -1) if one else s
+    B, T = s2.shape
+    w2 = None if w is None else _f32(w).reshape(B, T)
+    g2 = np.ascontiguousarray(g, dtype=np.float64).reshape(B, T)
+    grad = np.empty((B, T), dtype=np.float64)
+    soft = np.empty((B, T), dtype=np.float64)
+    _check(lib().oracle_bcjr_vjp_batch(_p(C, ctypes.c_float), _p(s2, ctypes.c_float),
+                                       _p(w2, ctypes.c_float), B, T, L, k, float(tau),
+                                       _p(g2, ctypes.c_double), _p(grad, ctypes.c_double),
+                                       _p(soft, ctypes.c_double)), "bcjr_vjp")
+    if one:
+        return grad[0], soft[0]
+    return grad, soft
+
+
+def brute_bcjr_vjp(C, s, tau, g, w=None, L=6, k=2):
+    C = _f32(C)
+    s = _f32(s)
+    w = _f32(w)
+    T = s.shape[-1]
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    grad = np.empty(T, dtype=np.float64)
+    _check(lib().oracle_brute_bcjr_vjp(_p(C, ctypes.c_float), _p(s, ctypes.c_float),
+                                       _p(w, ctypes.c_float), T, L, k, float(tau),
+                                       _p(g, ctypes.c_double), _p(grad, ctypes.c_double)),
+           "brute_bcjr_vjp")
+    return grad
 
 
 def minsum_marginals(C, s, w=None, L=16, k=2) -> np.ndarray:

@@ -802,3 +802,199 @@ int oracle_brute_tailbiting(const float* C, const float* s, const float* w, int 
     if (n_optimal) *n_optimal = count;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------ */
+/* Gradient of the soft codeword  ([BCJR] abstract: the relaxation is exactly       */
+/* differentiable)                                                                  */
+/* ------------------------------------------------------------------------------ */
+
+/* Vector-Jacobian product of the BCJR soft codeword with respect to the targets.
+ * With p(walk) proportional to exp(-E/tau) and dE/ds_u = -2 w_u (C(state_u) - s_u),
+ *     d soft_t / d s_u = (2 w_u / tau) Cov_p( C(state_t), C(state_u) ),
+ * so for an upstream gradient g (g_t = dLoss/dsoft_t)
+ *     grad_u = sum_t g_t d soft_t / d s_u = (2 w_u / tau) Cov_p( F, C(state_u) ),
+ *     F = sum_t g_t C(state_t).
+ * The covariance uses the Markov structure of p: given state_u = j the walk's past and
+ * future are independent, so E[F | state_u = j] = Phi_u(j) + g_u C_j + Psi_u(j) with
+ *     Phi_0(j) = 0,      Phi_t(j) = sum_{i in pred(j)} P(i | j) (Phi_{t-1}(i) + g_{t-1} C_i),
+ *                        P(i | j) proportional to exp(la_{t-1}(i))
+ *     Psi_{T-1}(i) = 0,  Psi_t(i) = sum_{x in succ(i)} P(x | i) (g_{t+1} C_x + Psi_{t+1}(x)),
+ *                        P(x | i) proportional to exp(lb_{t+1}(x) - e_{t+1}(x)/tau)
+ * (la, lb the forward and backward log messages of oracle_bcjr), and
+ *     Cov_p(F, C_u) = sum_j gamma_u(j) (C_j - soft_u) (E[F | j] - E[F]) / sum_j gamma_u(j).
+ * Binary64 throughout.  grad[0..T) out; soft (may be NULL) receives the soft codeword. */
+int oracle_bcjr_vjp(const float* C, const float* s, const float* w, int T, int L, int k,
+                    double tau, const double* g, double* grad, double* soft)
+{
+    if (!C || !s || !g || !grad || !check_trellis(T, L, k) || !(tau > 0.0) || !isfinite(tau))
+        return ORC_EINVAL;
+    const uint32_t N = 1u << L;
+    const uint32_t K = 1u << k;
+    double* la = (double*)malloc(sizeof(double) * (size_t)T * N);
+    double* lb = (double*)malloc(sizeof(double) * (size_t)T * N);
+    double* psi = (double*)malloc(sizeof(double) * (size_t)T * N);
+    double* phi = (double*)malloc(sizeof(double) * N);
+    double* phi_next = (double*)malloc(sizeof(double) * N);
+    double* terms = (double*)malloc(sizeof(double) * K);
+    if (!la || !lb || !psi || !phi || !phi_next || !terms) {
+        free(la); free(lb); free(psi); free(phi); free(phi_next); free(terms);
+        return ORC_ENOMEM;
+    }
+
+    /* forward and backward log messages, every step kept */
+    for (uint32_t j = 0; j < N; ++j)
+        la[j] = -energy64(C, s, w, 0, j) / tau;
+    for (int t = 1; t < T; ++t) {
+        const double* prev = la + (size_t)(t - 1) * N;
+        double* cur = la + (size_t)t * N;
+        for (uint32_t j = 0; j < N; ++j) {
+            for (uint32_t a = 0; a < K; ++a)
+                terms[a] = prev[(j >> k) | (a << (L - k))];
+            cur[j] = logsumexp(terms, (int)K) - energy64(C, s, w, t, j) / tau;
+        }
+    }
+    const double lz = logsumexp(la + (size_t)(T - 1) * N, (int)N);
+    for (uint32_t i = 0; i < N; ++i)
+        lb[(size_t)(T - 1) * N + i] = 0.0;
+    for (int t = T - 1; t >= 1; --t) {
+        for (uint32_t i = 0; i < N; ++i) {
+            for (uint32_t b = 0; b < K; ++b) {
+                uint32_t x = ((i << k) | b) & (N - 1);
+                terms[b] = lb[(size_t)t * N + x] - energy64(C, s, w, t, x) / tau;
+            }
+            lb[(size_t)(t - 1) * N + i] = logsumexp(terms, (int)K);
+        }
+    }
+
+    /* Psi backward, every step kept */
+    for (uint32_t i = 0; i < N; ++i)
+        psi[(size_t)(T - 1) * N + i] = 0.0;
+    for (int t = T - 2; t >= 0; --t) {
+        for (uint32_t i = 0; i < N; ++i) {
+            for (uint32_t b = 0; b < K; ++b) {
+                uint32_t x = ((i << k) | b) & (N - 1);
+                terms[b] = lb[(size_t)(t + 1) * N + x] - energy64(C, s, w, t + 1, x) / tau;
+            }
+            double m = logsumexp(terms, (int)K);
+            double acc = 0.0;
+            for (uint32_t b = 0; b < K; ++b) {
+                uint32_t x = ((i << k) | b) & (N - 1);
+                double q = exp(terms[b] - m);
+                acc += q * (g[t + 1] * (double)C[x] + psi[(size_t)(t + 1) * N + x]);
+            }
+            psi[(size_t)t * N + i] = acc;
+        }
+    }
+
+    /* Phi forward, combined with Psi step by step */
+    for (uint32_t j = 0; j < N; ++j)
+        phi[j] = 0.0;
+    for (int u = 0; u < T; ++u) {
+        if (u > 0) {
+            const double* prev = la + (size_t)(u - 1) * N;
+            for (uint32_t j = 0; j < N; ++j) {
+                for (uint32_t a = 0; a < K; ++a)
+                    terms[a] = prev[(j >> k) | (a << (L - k))];
+                double m = logsumexp(terms, (int)K);
+                double acc = 0.0;
+                for (uint32_t a = 0; a < K; ++a) {
+                    uint32_t i = (j >> k) | (a << (L - k));
+                    acc += exp(terms[a] - m) * (phi[i] + g[u - 1] * (double)C[i]);
+                }
+                phi_next[j] = acc;
+            }
+            double* tmp = phi; phi = phi_next; phi_next = tmp;
+        }
+        const double* cur = la + (size_t)u * N;
+        const double* bk = lb + (size_t)u * N;
+        const double* ps = psi + (size_t)u * N;
+        double den = 0.0, num_c = 0.0, num_f = 0.0;
+        for (uint32_t j = 0; j < N; ++j) {
+            double gm = exp(cur[j] + bk[j] - lz);
+            den += gm;
+            num_c += gm * (double)C[j];
+            num_f += gm * (phi[j] + g[u] * (double)C[j] + ps[j]);
+        }
+        const double su = num_c / den, fbar = num_f / den;
+        double cov = 0.0;
+        for (uint32_t j = 0; j < N; ++j) {
+            double gm = exp(cur[j] + bk[j] - lz);
+            double ef = phi[j] + g[u] * (double)C[j] + ps[j];
+            cov += gm * ((double)C[j] - su) * (ef - fbar);
+        }
+        cov /= den;
+        grad[u] = 2.0 * (w ? (double)w[u] : 1.0) / tau * cov;
+        if (soft) soft[u] = su;
+    }
+
+    free(la); free(lb); free(psi); free(phi); free(phi_next); free(terms);
+    return ORC_OK;
+}
+
+int oracle_bcjr_vjp_batch(const float* C, const float* s, const float* w, int64_t B, int T, int L,
+                          int k, double tau, const double* g, double* grad, double* soft)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        int rc = oracle_bcjr_vjp(C, s + b * T, w ? w + b * T : NULL, T, L, k, tau, g + b * T,
+                                 grad + b * T, soft ? soft + b * T : NULL);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* The same vector-Jacobian product by explicit enumeration of every walk: the
+ * Boltzmann probabilities, then Cov(F, C(state_u)) with both factors centred.
+ * Binary64; L + k(T-1) <= 22. */
+int oracle_brute_bcjr_vjp(const float* C, const float* s, const float* w, int T, int L, int k,
+                          double tau, const double* g, double* grad)
+{
+    if (!C || !s || !g || !grad || !check_trellis(T, L, k) || !(tau > 0.0)) return ORC_EINVAL;
+    int nbits = L + k * (T - 1);
+    if (nbits > 22) return ORC_EINVAL;
+    uint64_t nwalks = 1ull << nbits;
+    uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * T);
+    double* E = (double*)malloc(sizeof(double) * nwalks);
+    double* cbar = (double*)malloc(sizeof(double) * T);
+    if (!st || !E || !cbar) { free(st); free(E); free(cbar); return ORC_ENOMEM; }
+    double emin = INFINITY;
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        walk_states(n, T, L, k, st);
+        double e = 0.0;
+        for (int t = 0; t < T; ++t)
+            e += energy64(C, s, w, t, st[t]);
+        E[n] = e;
+        if (e < emin) emin = e;
+    }
+    double z = 0.0, fbar = 0.0;
+    for (int t = 0; t < T; ++t)
+        cbar[t] = 0.0;
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        double p = exp(-(E[n] - emin) / tau);
+        walk_states(n, T, L, k, st);
+        double f = 0.0;
+        for (int t = 0; t < T; ++t) {
+            f += g[t] * (double)C[st[t]];
+            cbar[t] += p * (double)C[st[t]];
+        }
+        fbar += p * f;
+        z += p;
+    }
+    fbar /= z;
+    for (int t = 0; t < T; ++t) {
+        cbar[t] /= z;
+        grad[t] = 0.0;
+    }
+    for (uint64_t n = 0; n < nwalks; ++n) {
+        double p = exp(-(E[n] - emin) / tau) / z;
+        walk_states(n, T, L, k, st);
+        double f = 0.0;
+        for (int t = 0; t < T; ++t)
+            f += g[t] * (double)C[st[t]];
+        for (int u = 0; u < T; ++u)
+            grad[u] += p * (f - fbar) * ((double)C[st[u]] - cbar[u]);
+    }
+    for (int u = 0; u < T; ++u)
+        grad[u] *= 2.0 * (w ? (double)w[u] : 1.0) / tau;
+    free(st); free(E); free(cbar);
+    return ORC_OK;
+}

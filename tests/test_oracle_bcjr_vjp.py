@@ -1,0 +1,143 @@
+"""Pins for the oracle's binary64 BCJR gradient (vector-Jacobian product).  CPU only.
+
+Source: BCJR-QAT abstract -- the soft relaxation is exactly differentiable.  With the
+Boltzmann walk distribution p ~ exp(-E / tau) of the soft codeword and E the weighted
+path cost, d soft_t / d s_u = (2 w_u / tau) Cov_p(C(state_t), C(state_u)); the oracle
+computes the product with an upstream gradient g by expectation messages.
+
+Pins (none of them retypes the oracle's recursion):
+* explicit enumeration of every walk at L = 6, k = 2, T <= 6, both codes, weighted;
+* central differences of sum_t g_t soft_t(s) through the (separately pinned) BCJR
+  oracle, unweighted and weighted, L = 8;
+* T = 1 closed form: grad = (2 w / tau) g Var(C) under softmax(-e_0 / tau);
+* a constant code has zero covariance, so zero gradient;
+* symmetry and positive semi-definiteness of the covariance matrix built from the
+  columns g = e_t (w_t J[t][u] = w_u J[u][t]);
+* tau -> infinity: walks become uniform, so (tau / 2) J[t][u] -> the uniform-walk
+  covariance, Var(C) on the diagonal and 0 once |t - u| >= L / k (no shared bits).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from trellis_coded_weight_amd import inputs
+
+
+def _g(T, seed):
+    return np.random.default_rng(seed).standard_normal(T)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 6])
+@pytest.mark.parametrize("tau", [1.0, 0.1])
+def test_bruteforce_L6(T, tau):
+    L, k = 6, 2
+    C = oracle.code_table("1mad", L)
+    for seed in range(2):
+        s = inputs.targets(1, T, 500 + seed)[0]
+        g = _g(T, 600 + seed)
+        grad, soft = oracle.bcjr_vjp(C, s, tau, g, L=L, k=k)
+        ref = oracle.brute_bcjr_vjp(C, s, tau, g, L=L, k=k)
+        bsoft, _ = oracle.brute_bcjr(C, s, tau, L=L, k=k)
+        scale = np.abs(ref).max() + 1e-300
+        assert np.allclose(grad, ref, rtol=1e-10, atol=1e-10 * scale)
+        assert np.allclose(soft, bsoft, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [3, 5])
+def test_bruteforce_weighted_3inst_L6(T):
+    L, k = 6, 2
+    C = oracle.code_table("3inst", L)
+    s = inputs.targets(1, T, 27)[0]
+    w = inputs.weights(1, T, 28)[0]
+    g = _g(T, 29)
+    grad, _ = oracle.bcjr_vjp(C, s, 0.3, g, w, L=L, k=k)
+    ref = oracle.brute_bcjr_vjp(C, s, 0.3, g, w, L=L, k=k)
+    assert np.allclose(grad, ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_central_differences(weighted):
+    L, k, T, tau = 8, 2, 20, 0.5
+    C = oracle.code_table("1mad", L)
+    s = inputs.targets(1, T, 31)[0]
+    w = inputs.weights(1, T, 32)[0] if weighted else None
+    g = _g(T, 33)
+    grad, _ = oracle.bcjr_vjp(C, s, tau, g, w, L=L, k=k)
+    h = np.float32(2.0 ** -12)
+    for u in (0, 5, 11, T - 1):
+        sp = s.copy(); sp[u] += h
+        sm = s.copy(); sm[u] -= h
+        assert sp[u] - s[u] == h and s[u] - sm[u] == h      # exact perturbations
+        fp, _ = oracle.bcjr(C, sp, tau, w, L=L, k=k)
+        fm, _ = oracle.bcjr(C, sm, tau, w, L=L, k=k)
+        fd = (g @ fp - g @ fm) / (2.0 * float(h))
+        assert abs(fd - grad[u]) <= 1e-5 * max(1.0, np.abs(grad).max())
+
+
+def test_single_step_closed_form():
+    L, tau = 8, 0.3
+    C = oracle.code_table("3inst", L).astype(np.float64)
+    s = inputs.targets(1, 1, 41)[0]
+    w = inputs.weights(1, 1, 42)[0]
+    for wt in (None, w):
+        ww = 1.0 if wt is None else float(wt[0])
+        e = ww * (C - float(s[0])) ** 2
+        p = np.exp(-(e - e.min()) / tau)
+        p /= p.sum()
+        mean = p @ C
+        var = p @ (C - mean) ** 2
+        grad, soft = oracle.bcjr_vjp(C.astype(np.float32), s, tau, np.array([1.7]), wt, L=L)
+        assert abs(soft[0] - mean) <= 1e-12
+        assert abs(grad[0] - 2.0 * ww / tau * 1.7 * var) <= 1e-12 * max(1.0, abs(grad[0]))
+
+
+def test_constant_code_has_zero_gradient():
+    L, T = 8, 16
+    ones = np.full(1 << L, 0.75, dtype=np.float32)
+    s = inputs.targets(1, T, 43)[0]
+    grad, soft = oracle.bcjr_vjp(ones, s, 0.2, _g(T, 44), L=L)
+    assert np.allclose(soft, 0.75, atol=1e-13)
+    assert np.abs(grad).max() <= 1e-12
+
+
+def _jacobian(C, s, tau, w, L):
+    T = s.shape[-1]
+    J = np.empty((T, T))
+    for t in range(T):
+        g = np.zeros(T)
+        g[t] = 1.0
+        J[t], _ = oracle.bcjr_vjp(C, s, tau, g, w, L=L)    # row t: d soft_t / d s_u
+    return J
+
+
+def test_covariance_symmetric_and_psd():
+    L, T, tau = 8, 14, 0.4
+    C = oracle.code_table("1mad", L)
+    s = inputs.targets(1, T, 45)[0]
+    w = inputs.weights(1, T, 46)[0].astype(np.float64)
+    J = _jacobian(C, s, tau, w.astype(np.float32), L)
+    K = J * tau / (2.0 * w[None, :])                     # Cov(C_t, C_u)
+    assert np.allclose(K, K.T, rtol=1e-9, atol=1e-12)
+    ev = np.linalg.eigvalsh(0.5 * (K + K.T))
+    assert ev.min() >= -1e-10 * ev.max()
+    assert np.all(np.diag(K) > 0)
+
+
+def test_high_temperature_uniform_covariance():
+    L, k, T, tau = 8, 2, 20, 1e7
+    C = oracle.code_table("1mad", L).astype(np.float64)
+    s = inputs.targets(1, T, 47)[0]
+    J = _jacobian(C.astype(np.float32), s, tau, None, L)
+    K = J * tau / 2.0
+    var = C.var()
+    assert np.allclose(np.diag(K), var, rtol=1e-5)
+    far = np.abs(np.subtract.outer(np.arange(T), np.arange(T))) >= L // k
+    assert np.abs(K[far]).max() <= 1e-5 * var
+    # one step apart a state shares L-k bits with the next: uniform-walk covariance of
+    # C(x) and C(y) with y = (x << k | b) mod 2^L, b uniform
+    N = 1 << L
+    x = np.arange(N)
+    mean = C.mean()
+    cov1 = np.mean([(C[x] - mean) @ (C[((x << k) | b) & (N - 1)] - mean) / N
+                    for b in range(1 << k)])
+    assert np.allclose(np.diag(K, 1), cov1, rtol=1e-4, atol=1e-5 * var)
