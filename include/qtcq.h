@@ -148,6 +148,35 @@ qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int 
                            int code, float temperature, float* soft, float* log_z,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Gradient of the soft codeword [BCJR abstract: the relaxation is exactly
+ * differentiable] -------------------------------------------------------------------
+ * With p(walk) ~ exp(-E / temperature) and E the path cost of qtcq_bcjr_soft,
+ *     d soft[b][t] / d seq[b][u] = (2 w_u / temperature) Cov_p( C(st[t]), C(st[u]) ),
+ * (w_u = err_w[b][u], or 1), so for an upstream gradient g = dLoss/dsoft the
+ * vector-Jacobian product is
+ *     grad_seq[b][u] = (2 w_u / temperature) Cov_p( sum_t g[b][t] C(st[t]), C(st[u]) ),
+ * computed exactly by one more forward-backward pass with expectation messages. */
+
+/* Workspace bytes qtcq_bcjr_vjp needs for `B` sequences in one pass (both message
+ * directions of every step, in fixed point, plus the expectation messages of the
+ * forward direction).  Smaller workspaces that hold one sequence are used in chunks.
+ * Returns 0 for unsupported arguments. */
+size_t qtcq_bcjr_vjp_workspace_bytes(int64_t B, int T, int L, int k);
+
+/* Vector-Jacobian product of the BCJR soft codeword with respect to the targets.
+ *   seq, err_w, B, T, L, k, code, temperature : as qtcq_bcjr_soft
+ *   grad_soft [B][T] float32 (in): the upstream gradient g
+ *   grad_seq  [B][T] float32 (out): the product above
+ *   soft      [B][T] float32 (out) or NULL: the soft codeword (as qtcq_bcjr_soft)
+ *   log_z     [B] float32 (out) or NULL
+ *   workspace: 16-byte aligned, >= qtcq_bcjr_vjp_workspace_bytes(1, T, L, k)
+ * Errors: QTCQ_ERR_INVALID_ARG (also grad_soft or grad_seq NULL), QTCQ_ERR_UNSUPPORTED,
+ * QTCQ_ERR_WORKSPACE, QTCQ_ERR_DEVICE. */
+qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
+                          int code, float temperature, const float* grad_soft, float* grad_seq,
+                          float* soft, float* log_z, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* ---- Tail-biting trellis [QTIP "Tail-biting is worth its complexity"] ------------
  * A tail-biting walk is cyclic: the low L-k bits of its last state equal the high L-k
  * bits of its first, so the stream needs no start state and is exactly k*T bits.

@@ -64,6 +64,24 @@ def oracle_bcjr_par(C, s, tau, w=None, L=16, k=2):
     return soft, logz
 
 
+def oracle_vjp_par(C, s, tau, g, w=None, L=16, k=2):
+    """Oracle BCJR gradient over rows of s, fanned out over threads (one row per job:
+    the binary64 oracle keeps every step's messages, 3 x T x 2^L doubles per row)."""
+    B, T = s.shape
+    grad = np.empty((B, T))
+    soft = np.empty((B, T))
+    workers = N_WORKERS if L < 16 else max(1, min(N_WORKERS, 8))
+
+    def job(b):
+        gr, so = oracle.bcjr_vjp(C, s[b:b + 1], tau, g[b:b + 1], None if w is None else w[b:b + 1],
+                                 L=L, k=k)
+        grad[b], soft[b] = gr, so
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(job, range(B)))
+    return grad, soft
+
+
 def bcjr_err(soft_gpu, soft_ref):
     """Per sequence: max_t |soft_gpu - soft_ref| / RMS_t(soft_ref)."""
     soft_gpu = np.asarray(soft_gpu, dtype=np.float64)

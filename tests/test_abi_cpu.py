@@ -112,6 +112,37 @@ def test_bcjr_validation(nat):
     assert st(None, None, 0, 256, 16, 2, 0, 1.0, None, None, None, 0, None) == nat.QTCQ_OK
 
 
+def test_bcjr_vjp_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_bcjr_vjp", *a)
+    ws = nat.qtcq_bcjr_vjp_workspace_bytes(1, 256, 16, 2)
+    assert ws > nat.qtcq_bcjr_workspace_bytes(1, 256, 16, 2)
+    assert nat.qtcq_bcjr_vjp_workspace_bytes(4, 256, 16, 2) == 4 * ws
+    assert nat.qtcq_bcjr_vjp_workspace_bytes(1, 256, 9, 2) == 0
+    # seq, w, B, T, L, k, code, tau, grad_soft, grad_seq, soft, logz, ws, wsb, stream
+    ok = [FAKE, None, 4, 256, 16, 2, 0, 0.5, FAKE, FAKE, None, None, FAKE, ws, None]
+    names = ["seq", "w", "B", "T", "L", "k", "code", "tau", "g", "grad", "soft", "logz", "ws",
+             "wsb", "stream"]
+
+    def call(**kw):
+        a = list(ok)
+        for kk, v in kw.items():
+            a[names.index(kk)] = v
+        return st(*a)
+
+    assert call(tau=0.0) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(tau=float("nan")) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(T=0) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(L=9) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(code=3) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(g=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(grad=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(seq=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(ws=None) == nat.QTCQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == nat.QTCQ_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == nat.QTCQ_ERR_WORKSPACE
+    assert call(B=0, seq=None, g=None, grad=None, ws=None, wsb=0) == nat.QTCQ_OK
+
+
 def test_tailbiting_sizes(nat):
     assert nat.qtcq_tailbiting_words(16, 2, 256) == 16     # exactly 2T bits, word-aligned
     assert nat.qtcq_tailbiting_words(16, 2, 8) == 1

@@ -53,6 +53,9 @@ _SIGS = {
     "qtcq_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "qtcq_bcjr_soft": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp,
                               _vp, _sz, _vp]),
+    "qtcq_bcjr_vjp_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
+    "qtcq_bcjr_vjp": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp,
+                             _vp, _vp, _sz, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
     "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
@@ -117,6 +120,18 @@ def qtcq_bcjr_soft(seq: int, err_w, B: int, T: int, L: int, k: int, code: int,
     _check(_lib.qtcq_bcjr_soft(_ptr(seq), _ptr(err_w), B, T, L, k, code, float(temperature),
                                _ptr(soft), _ptr(log_z), _ptr(workspace), workspace_bytes,
                                _ptr(stream)), "qtcq_bcjr_soft")
+
+
+def qtcq_bcjr_vjp_workspace_bytes(B: int, T: int, L: int, k: int) -> int:
+    return _lib.qtcq_bcjr_vjp_workspace_bytes(B, T, L, k)
+
+
+def qtcq_bcjr_vjp(seq: int, err_w, B: int, T: int, L: int, k: int, code: int,
+                  temperature: float, grad_soft: int, grad_seq: int, soft, log_z, workspace: int,
+                  workspace_bytes: int, stream: int = 0) -> None:
+    _check(_lib.qtcq_bcjr_vjp(_ptr(seq), _ptr(err_w), B, T, L, k, code, float(temperature),
+                              _ptr(grad_soft), _ptr(grad_seq), _ptr(soft), _ptr(log_z),
+                              _ptr(workspace), workspace_bytes, _ptr(stream)), "qtcq_bcjr_vjp")
 
 
 def qtcq_tailbiting_words(L: int, k: int, T: int) -> int:

@@ -106,6 +106,38 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
     return soft, logz
 
 
+def bcjr_vjp_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
+                       max_bytes: int | None = None) -> torch.Tensor:
+    need = nat.qtcq_bcjr_vjp_workspace_bytes(B, T, L, k)
+    if max_bytes is not None:
+        per = nat.qtcq_bcjr_vjp_workspace_bytes(1, T, L, k)
+        need = max(per, min(need, max_bytes // per * per))
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def bcjr_vjp(seq: torch.Tensor, temperature: float, grad_soft: torch.Tensor,
+             weights: torch.Tensor | None = None, L: int = 16, k: int = 2, code="1mad",
+             want_soft: bool = False, workspace: torch.Tensor | None = None):
+    """Gradient of sum_t grad_soft[b][t] * soft[b][t] with respect to seq.  Returns
+    (grad_seq [B][T] float32, soft [B][T] or None, log_z [B] or None)."""
+    _dev_f32(seq, "seq")
+    _dev_f32(grad_soft, "grad_soft")
+    B, T = seq.shape
+    if grad_soft.shape != seq.shape:
+        raise ValueError("grad_soft must have the shape of seq")
+    grad = torch.empty((B, T), dtype=torch.float32, device=seq.device)
+    soft = torch.empty((B, T), dtype=torch.float32, device=seq.device) if want_soft else None
+    logz = torch.empty(B, dtype=torch.float32, device=seq.device) if want_soft else None
+    if workspace is None:
+        workspace = bcjr_vjp_workspace(B, T, L, k, max_bytes=8 << 30)
+    nat.qtcq_bcjr_vjp(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
+                      _code(code), temperature, grad_soft.data_ptr(), grad.data_ptr(),
+                      None if soft is None else soft.data_ptr(),
+                      None if logz is None else logz.data_ptr(), workspace.data_ptr(),
+                      workspace.numel(), _stream())
+    return grad, soft, logz
+
+
 def tailbiting_words(L: int = 16, k: int = 2, T: int = 256) -> int:
     return nat.qtcq_tailbiting_words(L, k, T)
 

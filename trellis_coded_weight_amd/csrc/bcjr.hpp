@@ -17,19 +17,26 @@
 // Precision.  A message accumulates one rounding per step; in fp32 at tau = 0.01 the
 // per-step increments (kappa e ~ 10 log2 units) make those roundings ~1e-6 each, which
 // over ~250 steps shifts competing walks' weights by ~1e-5.  So messages are stored and
-// combined in fp64: the energy is computed in fp32 (d = C - s, e = d*d [* w]) and
-// widened exactly, each LSE's four inputs are held as an fp64 reference (their maximum)
+// combined in fp64: the energy is the exact binary64 value of (C - s)^2 [* w] from the
+// binary32 inputs, each LSE's four inputs are held as an fp64 reference (their maximum)
 // plus fp32 differences (the dominant input is then exact), the LSE's max and
 // differences are fp64, and only exp2 / log2 of small arguments run in fp32.
 // Messages live in one fp64 LDS buffer (128 KiB at L = 16): each step reads all its
 // inputs, barrier, writes all outputs, barrier.
 // Normalisation: stored X_t = A_t - G_{t-1}; the next step subtracts g_t = max X_t
 // (from per-wave maxima) and G accumulates the g's, likewise h/H for the backward.
-// Every X_t also goes to an fp32 HBM stash (rounding there does not accumulate).
+// Stash: while step t + 1 reads X_t it also writes Xn_t = X_t - g_t = A_t - G_t (every
+// value <= 0 up to rounding, the maximum at 0) to HBM in 32 bits (to_fix): fixed point
+// with a uniform 2.4e-7 log2 resolution down to -1024, fp32 below.  Plain fp32 would
+// lose precision on the moderately negative values that still matter once the
+// backward message is added.
 // Posterior at t: gamma_t(j) = 2^( la_t(j) + lb_t(j) - log2 Z ), computed in the backward
-// sweep from the stash value X_t[(a, c)], the backward input Y_t[(c, x)] and the step
-// energy, with the exact offset O_t = log2 Z - G_{t-1} - H_t.  soft_t = sum gamma C /
-// sum gamma: per-wave partial sums per step go to the workspace, a small kernel divides.
+// sweep from the stashed Xn_t[(a, c)], the normalised backward input Yn_t[(c, x)] =
+// Y_t - h_t and the step energy, with the exact offset O_t = log2 Z - G_t - H_t.
+// soft_t = sum gamma C / sum gamma: per-wave partial sums per step go to the
+// workspace, a small kernel divides.
+// VJP mode (for the gradient kernel, bcjr_vjp.hpp) also stashes Yn_t in the same
+// fixed point and O_t in binary64.
 #pragma once
 
 #include "codes.hpp"
@@ -75,18 +82,76 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// Stash values (normalised messages, <= 0 up to the rounding of the normaliser) in 32
+// bits: v >= -1024 as int32 units of 2^-21 log2 (codes below 2^30), v < -1024 as the
+// binary32 bit pattern of -v, whose codes are >= 0x44800000 (= 1024.0f).  Near the
+// maximum, where a posterior term depends on them, values keep a uniform 2.4e-7
+// resolution; far below it they keep fp32's relative precision, so that at low
+// temperature a state whose forward message is far below the step's maximum but whose
+// backward message lifts it still gets the right (finite) posterior exponent.
+constexpr double kFixScale = 2097152.0;
+__device__ __forceinline__ int to_fix(double v)
+{
+    if (v >= -1024.0) return (int)__builtin_rint(v * kFixScale);
+    return (int)__builtin_bit_cast(uint32_t, (float)(-v));
+}
+__device__ __forceinline__ double from_fix(int q)
+{
+    if (q < 0x40000000) return (double)q * (1.0 / kFixScale);
+    return -(double)__builtin_bit_cast(float, (uint32_t)q);
+}
+
+// Forward stash Xn_t[(a, 4 tid + r)], t = 1..T-1, at step index i = t - 1.  The soft pass
+// keeps [i][a][tid] int4 (r = 0..3); in VJP mode the layout is [i][a][h][tid] int2
+// (r = 2h, 2h + 1) so that the gradient kernel, which works on one half of a thread's
+// butterflies at a time, reads it lane-contiguously.
+template <int NT, bool VJP>
+__device__ __forceinline__ void xn_store(int* st, size_t i, int a, int tid, int4 v)
+{
+    if constexpr (VJP) {
+        int2* p = reinterpret_cast<int2*>(st);
+        p[((i * 4 + a) * 2 + 0) * NT + tid] = make_int2(v.x, v.y);
+        p[((i * 4 + a) * 2 + 1) * NT + tid] = make_int2(v.z, v.w);
+    } else {
+        reinterpret_cast<int4*>(st)[(i * 4 + a) * NT + tid] = v;
+    }
+}
+
+template <int NT, bool VJP>
+__device__ __forceinline__ int4 xn_load(const int* st, size_t i, int a, int tid)
+{
+    if constexpr (VJP) {
+        const int2* p = reinterpret_cast<const int2*>(st);
+        const int2 lo = p[((i * 4 + a) * 2 + 0) * NT + tid];
+        const int2 hi = p[((i * 4 + a) * 2 + 1) * NT + tid];
+        return make_int4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        return reinterpret_cast<const int4*>(st)[(i * 4 + a) * NT + tid];
+    }
+}
+
 template <int L>
 struct BcjrLayout {
     using Tr = Trellis<L>;
     static constexpr int kWaves = (Tr::kThreads + 63) / 64;
     // Per-sequence workspace, each part 256-byte aligned:
     //   log2 Z (double) | g_0..g_{T-1} (float) | posterior partial sums [T][kWaves][2]
-    //   | stash X_1..X_{T-1} ([T-1][4][kThreads] float4: chunk 4*tau + r at [r][tau])
+    //   | stash Xn_1..Xn_{T-1} (groups (a, 4 tau + r): see xn_store)
+    // and in VJP mode, after those:
+    //   | Yn_0..Yn_{T-1} ([T][4][kThreads] int4: groups (4 tau + r, x), x = 0..3, at
+    //     [r][tau]) | O_0..O_{T-1} (double) | Phi_0..Phi_{T-1} ([T][4][2][kThreads]
+    //     float2: groups (a, 4 tau + 2h + i), i = 0, 1, at [a][h][tau]) | gradient
+    //     partial sums [T][kWaves][4] (float)
     __host__ __device__ static size_t up(size_t b) { return (b + 255) / 256 * 256; }
     __host__ __device__ static size_t off_g() { return 256; }
     __host__ __device__ static size_t off_part(int T) { return off_g() + up((size_t)T * 4); }
     __host__ __device__ static size_t off_stash(int T) { return off_part(T) + up((size_t)T * kWaves * 8); }
     __host__ __device__ static size_t bytes_per_seq(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 4); }
+    __host__ __device__ static size_t off_ystash(int T) { return bytes_per_seq(T); }
+    __host__ __device__ static size_t off_ofs(int T) { return off_ystash(T) + up((size_t)T * Tr::kGroups * 4); }
+    __host__ __device__ static size_t off_phi(int T) { return off_ofs(T) + up((size_t)T * 8); }
+    __host__ __device__ static size_t off_vpart(int T) { return off_phi(T) + up((size_t)T * Tr::kGroups * 4); }
+    __host__ __device__ static size_t bytes_per_seq_vjp(int T) { return off_vpart(T) + up((size_t)T * kWaves * 16); }
 };
 
 // fp64 message buffer: a chunk = 4 consecutive groups = 32 bytes, stored as two 16-byte
@@ -138,21 +203,22 @@ __device__ __forceinline__ void lds_write4(char* base, int addr, int P, double v
     *reinterpret_cast<double2*>(base + addr + P) = make_double2(v2, v3);
 }
 
-inline size_t bcjr_bytes_per_seq(int T, int L)
+inline size_t bcjr_bytes_per_seq(int T, int L, bool vjp = false)
 {
     switch (L) {
-    case 6: return BcjrLayout<6>::bytes_per_seq(T);
-    case 8: return BcjrLayout<8>::bytes_per_seq(T);
-    case 10: return BcjrLayout<10>::bytes_per_seq(T);
-    case 12: return BcjrLayout<12>::bytes_per_seq(T);
-    case 14: return BcjrLayout<14>::bytes_per_seq(T);
-    default: return BcjrLayout<16>::bytes_per_seq(T);
+    case 6: return vjp ? BcjrLayout<6>::bytes_per_seq_vjp(T) : BcjrLayout<6>::bytes_per_seq(T);
+    case 8: return vjp ? BcjrLayout<8>::bytes_per_seq_vjp(T) : BcjrLayout<8>::bytes_per_seq(T);
+    case 10: return vjp ? BcjrLayout<10>::bytes_per_seq_vjp(T) : BcjrLayout<10>::bytes_per_seq(T);
+    case 12: return vjp ? BcjrLayout<12>::bytes_per_seq_vjp(T) : BcjrLayout<12>::bytes_per_seq(T);
+    case 14: return vjp ? BcjrLayout<14>::bytes_per_seq_vjp(T) : BcjrLayout<14>::bytes_per_seq(T);
+    default: return vjp ? BcjrLayout<16>::bytes_per_seq_vjp(T) : BcjrLayout<16>::bytes_per_seq(T);
     }
 }
 
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws points at the
-// chunk's workspace, bytes_per_seq(T) per sequence.  kappa = log2(e) / tau.
-template <int L, int CODE, bool WEIGHTED>
+// chunk's workspace, bytes_per_seq(T) (VJP: bytes_per_seq_vjp(T)) per sequence.
+// kappa = log2(e) / tau.
+template <int L, int CODE, bool WEIGHTED, bool VJP = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
            double kappa, char* __restrict__ ws)
@@ -174,11 +240,13 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     const int64_t row = b0 + blockIdx.x;
     const float* s = seq + row * T;
     const float* w = WEIGHTED ? wts + row * T : nullptr;
-    char* base = ws + (size_t)blockIdx.x * Ly::bytes_per_seq(T);
+    char* base = ws + (size_t)blockIdx.x * (VJP ? Ly::bytes_per_seq_vjp(T) : Ly::bytes_per_seq(T));
     double* l2z = reinterpret_cast<double*>(base);
     float* gnorm = reinterpret_cast<float*>(base + Ly::off_g());
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
-    float4* stash = reinterpret_cast<float4*>(base + Ly::off_stash(T));
+    int* stash = reinterpret_cast<int*>(base + Ly::off_stash(T));
+    int4* ystash = reinterpret_cast<int4*>(base + Ly::off_ystash(T));     // VJP only
+    double* ofs = reinterpret_cast<double*>(base + Ly::off_ofs(T));        // VJP only
 
     float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x), one at a time
 #pragma unroll
@@ -202,11 +270,12 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + opaque_tid())); };
     auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * opaque_tid() + r)); };
 
-    auto energy = [&](float c, float sp, float wp) -> double {
-        const float d = c - sp;
-        float e = d * d;
+    // exact binary64 energy (C - s)^2 [* w] of binary32 inputs; sp, wp already widened
+    auto energy = [&](float c, double sp, double wp) -> double {
+        const double d = widen(c) - sp;
+        double e = d * d;
         if constexpr (WEIGHTED) e = wp * e;
-        return (double)e;
+        return e;
     };
 
     // ---------------- forward ----------------
@@ -248,6 +317,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 lds_read4(buf, rd(a), P, xa);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) rel[a][r] = (float)(xa[r] - mx[r]);
+                // Xn_{t-1}[(a, 4 tid + r)] (Xn_0 = 0 is not stored)
+                if (t >= 2)
+                    xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
+                                      make_int4(to_fix(xa[0] - g64), to_fix(xa[1] - g64),
+                                                to_fix(xa[2] - g64), to_fix(xa[3] - g64)));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) ref[r] = mx[r] - g64;
@@ -255,12 +329,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         __syncthreads();   // every input read before any output overwrites it
         G = uniform64(G + g64);
         if (tid == 0) gnorm[t - 1] = g;
-        const float sp = s[t - 1];
-        const float wp = WEIGHTED ? w[t - 1] : 1.0f;
+        const double sp = (double)s[t - 1];
+        const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float of[4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs x = 2h, 2h + 1
                 double o[2];
@@ -272,13 +345,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     for (int a = 0; a < 4; ++a)
                         v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[a][r]));
                     o[xx] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
-                    of[x] = (float)o[xx];
-                    lmax = __builtin_fmaxf(lmax, of[x]);
+                    lmax = __builtin_fmaxf(lmax, (float)o[xx]);
                 }
                 *reinterpret_cast<double2*>(buf + wr(r) + h * P) = make_double2(o[0], o[1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            stash[((size_t)(t - 1) * 4 + r) * NT + tid] = make_float4(of[0], of[1], of[2], of[3]);
         }
         lmax = wave_max<WID>(lmax);
         if (lane == 0) wmax[par ^ 1][wave] = lmax;
@@ -295,14 +366,18 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     if (tid == 0) gnorm[T - 1] = gl;
     double log2z;
     {
-        const float sp = s[T - 1];
-        const float wp = WEIGHTED ? w[T - 1] : 1.0f;
+        const double sp = (double)s[T - 1];
+        const double wp = WEIGHTED ? (double)w[T - 1] : 1.0;
         const double gl64 = (double)gl;
         double m = -__builtin_inf();
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             double xa[4];
             lds_read4(buf, rd(a), P, xa);
+            if (T >= 2)   // Xn_{T-1}
+                xn_store<NT, VJP>(stash, (size_t)(T - 2), a, tid,
+                                  make_int4(to_fix(xa[0] - gl64), to_fix(xa[1] - gl64),
+                                            to_fix(xa[2] - gl64), to_fix(xa[3] - gl64)));
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -364,28 +439,32 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
             for (int x = 0; x < 4; ++x) rel[r][x] = (float)(yv[x] - mx);
             ref[r] = mx - h64;
+            if constexpr (VJP)   // Yn_t[(4 tid + r, x)]
+                ystash[((size_t)t * 4 + r) * NT + tid] =
+                    make_int4(to_fix(yv[0] - h64), to_fix(yv[1] - h64), to_fix(yv[2] - h64),
+                              to_fix(yv[3] - h64));
         }
         if (produce) __syncthreads();   // every input read before any output overwrites it
         H = uniform64(H + h64);                       // H_t
+        const double Ot = uniform64(log2z - Gm - H);  // log2 Z - G_t - H_t
+        if (VJP && tid == 0) ofs[t] = Ot;
         Gm = uniform64(Gm - (double)gnorm[t]);        // G_{t-1}
-        const double Ot = uniform64(log2z - Gm - H);
-        const float sp = s[t];
-        const float wp = WEIGHTED ? w[t] : 1.0f;
+        const double sp = (double)s[t];
+        const double wp = WEIGHTED ? (double)w[t] : 1.0;
         float pg = 0.f, pc = 0.f;
         float ymax = -__builtin_inff();
-        // X_t[(a, 4 tid + r)], r = 0..3, from the stash (X_0 = 0), prefetched one a ahead
-        auto stash_at = [&](int a) -> float4 {
-            if (!produce) return make_float4(0.f, 0.f, 0.f, 0.f);
-            const int gch = a * NT + tid;      // logical chunk index
-            return stash[((size_t)(t - 1) * 4 + (gch & 3)) * NT + (gch >> 2)];
+        // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a ahead
+        auto stash_at = [&](int a) -> int4 {
+            if (!produce) return make_int4(0, 0, 0, 0);
+            return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
         };
-        float4 xs_next = stash_at(0);
+        int4 xs_next = stash_at(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const float4 xs = xs_next;
+            const int4 xs = xs_next;
             if (a < 3) xs_next = stash_at(a + 1);
             asm volatile("" ::: "memory");    // no further hoisting of stash loads
-            const float xsr[4] = {xs.x, xs.y, xs.z, xs.w};
+            const int xsr[4] = {xs.x, xs.y, xs.z, xs.w};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs r = 2h, 2h + 1
                 double y[2];
@@ -393,7 +472,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 for (int rr = 0; rr < 2; ++rr) {
                     const int r = 2 * h + rr;
                     // posterior exponent = X_t - O_t + (Y_t - h_t) - kappa e_t
-                    const double xo = ((double)xsr[r] - Ot) + ref[r];
+                    const double xo = (from_fix(xsr[r]) - Ot) + ref[r];
                     double v[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
@@ -428,10 +507,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     bstep(0, false);
 }
 
-// soft[b][t] = (sum_waves pc) / (sum_waves pg); log_z = ln 2 * log2 Z.
+// soft[b][t] = (sum_waves pc) / (sum_waves pg); log_z = ln 2 * log2 Z.  stride: the
+// workspace bytes per sequence (bytes_per_seq or bytes_per_seq_vjp).
 template <int L>
 __global__ void __launch_bounds__(256)
-bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0,
+bcjr_finalize(const char* __restrict__ ws, size_t stride, int T, int64_t n, int64_t b0,
               float* __restrict__ soft, float* __restrict__ logz)
 {
     using Ly = BcjrLayout<L>;
@@ -440,7 +520,7 @@ bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0,
     if (idx >= n * T) return;
     const int64_t i = idx / T;
     const int t = (int)(idx - i * T);
-    const char* base = ws + (size_t)i * Ly::bytes_per_seq(T);
+    const char* base = ws + (size_t)i * stride;
     const float* part = reinterpret_cast<const float*>(base + Ly::off_part(T));
     float pg = 0.f, pc = 0.f;
 #pragma unroll
@@ -448,7 +528,7 @@ bcjr_finalize(const char* __restrict__ ws, int T, int64_t n, int64_t b0,
         pg += part[((size_t)t * kWaves + q) * 2 + 0];
         pc += part[((size_t)t * kWaves + q) * 2 + 1];
     }
-    soft[(b0 + i) * T + t] = pc / pg;
+    if (soft) soft[(b0 + i) * T + t] = pc / pg;
     if (logz && t == 0) {
         const double l2z = *reinterpret_cast<const double*>(base);
         logz[b0 + i] = (float)(l2z * 0.69314718055994530942);

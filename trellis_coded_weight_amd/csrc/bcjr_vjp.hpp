@@ -1,0 +1,275 @@
+// bcjr_vjp.hpp -- vector-Jacobian product of the BCJR soft codeword, gfx950.
+//
+// BCJR-QAT abstract: the soft codeword is the Boltzmann expectation of the
+// reconstruction over trellis walks at temperature tau, and the relaxation is exactly
+// differentiable.  With p(walk) ~ exp(-E / tau) and dE/ds_u = -2 w_u (C(state_u) - s_u),
+//     d soft_t / d s_u = (2 w_u / tau) Cov( C(state_t), C(state_u) ),
+// so for an upstream gradient g (g_t = dLoss / dsoft_t)
+//     grad_u = (2 w_u / tau) Cov( F, C(state_u) ),   F = sum_t g_t C(state_t).
+// Given state_u = j the walk's past and future are independent, so
+//     E[F | state_u = j] - Fbar = Phi_u(j >> 2) + g_u (C_j - soft_u) + Psi_u(j mod M)
+// with Fbar = sum_t g_t soft_t and two linear recursions over the same trellis groups as
+// the soft pass, centred on soft (which keeps their values O(1) and fp32 adequate):
+//     Phi_0 = 0,  Phi_t[(c, x)] = sum_a P_a (Phi_{t-1}[(a, c)] + g_{t-1} (C_(a,c,x) - soft_{t-1}))
+//                 P_a ~ 2^( Xn_{t-1}[(a, c)] - kappa e_{t-1}((a, c, x)) )
+//     Psi_{T-1} = 0,  Psi_{u-1}[(a, c)] = sum_x Q_x (g_u (C_(a,c,x) - soft_u) + Psi_u[(c, x)])
+//                 Q_x ~ 2^( Yn_u[(c, x)] - kappa e_u((a, c, x)) )
+// where Xn, Yn are the soft pass's normalised forward / backward messages (32-bit
+// stash, to_fix) and kappa = log2(e) / tau.  At every u the posterior gamma_u(j) =
+// 2^(Xn_u + Yn_u - kappa e_u - O_u) gives the four sums S0 = sum gamma, S1 = sum gamma c,
+// S2 = sum gamma f, S3 = sum gamma c f (c = C_j - soft_u, f = the bracket above), and
+//     Cov = S3 / S0 - (S1 / S0)(S2 / S0).
+// Kernel: one workgroup per sequence, thread tau owns butterflies c = 4 tau + r as in
+// the soft pass, handled in two halves (r = 2h, 2h + 1) so that only half of the
+// messages are live at once.  Phi / Psi live in a double-buffered fp32 LDS buffer (one
+// barrier per step).  While step t + 1 reads Phi_t it also stores it to HBM
+// ([t][a][h][tau] float2, lane-contiguous) for the backward; per-wave partial sums per
+// step go to the workspace and bcjr_vjp_finalize forms the gradient.
+#pragma once
+
+#include <type_traits>
+
+#include "bcjr.hpp"
+
+namespace qtcq {
+
+// grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws: the chunk's VJP
+// workspace as left by bcjr_sweep<..., VJP = true> (bytes_per_seq_vjp(T) per sequence).
+// gup: [*][T] upstream gradient; row b0 + blockIdx.x.
+template <int L, int CODE, bool WEIGHTED>
+__global__ void __launch_bounds__(Trellis<L>::kThreads)
+bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
+               const float* __restrict__ gup, int T, int64_t b0, double kappa,
+               char* __restrict__ ws)
+{
+    using Tr = Trellis<L>;
+    using Ly = BcjrLayout<L>;
+    constexpr int NT = Tr::kThreads;
+    constexpr int NB = Tr::kButterflies;
+    constexpr int M = Tr::kGroups;
+    constexpr int kWaves = Ly::kWaves;
+    constexpr int WID = NT < 64 ? NT : 64;
+    __shared__ float4 buf[2][NB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t row = b0 + blockIdx.x;
+    const float* s = seq + row * T;
+    const float* w = WEIGHTED ? wts + row * T : nullptr;
+    const float* gu = gup + row * T;
+    char* base = ws + (size_t)blockIdx.x * Ly::bytes_per_seq_vjp(T);
+    const float* part = reinterpret_cast<const float*>(base + Ly::off_part(T));
+    const int2* xst = reinterpret_cast<const int2*>(base + Ly::off_stash(T));    // [t-1][a][h][tau]
+    const int4* yst = reinterpret_cast<const int4*>(base + Ly::off_ystash(T));   // [t][r][tau]
+    const double* ofs = reinterpret_cast<const double*>(base + Ly::off_ofs(T));
+    float2* phs = reinterpret_cast<float2*>(base + Ly::off_phi(T));              // [t][a][h][tau]
+    float* vpart = reinterpret_cast<float*>(base + Ly::off_vpart(T));
+
+    float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+    auto opaque_tid = [&]() {
+        int v = tid;
+        asm volatile("v_mov_b32 %0, %0" : "+v"(v));
+        return v;
+    };
+    auto rd = [&](int a) { return lds_chunk(a * NT + opaque_tid()); };   // groups (a, 4tid + r)
+    auto wr = [&](int r) { return lds_chunk(4 * opaque_tid() + r); };   // groups (4tid + r, x)
+    auto half = [&](int cur, int chunk, int h) -> float2& {
+        return reinterpret_cast<float2*>(&buf[cur][chunk])[h];
+    };
+    // soft_t as the soft pass's finalize forms it
+    auto soft_at = [&](int t) -> float {
+        float pg = 0.f, pc = 0.f;
+#pragma unroll
+        for (int q = 0; q < kWaves; ++q) {
+            pg += part[((size_t)t * kWaves + q) * 2 + 0];
+            pc += part[((size_t)t * kWaves + q) * 2 + 1];
+        }
+        return pc / pg;
+    };
+    // the soft pass's exact binary64 energy
+    auto energy = [&](float c, double sp, double wp) -> double {
+        const double d = widen(c) - sp;
+        double e = d * d;
+        if constexpr (WEIGHTED) e = wp * e;
+        return e;
+    };
+    auto phi_slot = [&](int t, int a, int h) -> size_t {
+        return (((size_t)t * 4 + a) * 2 + h) * NT + tid;
+    };
+
+    // ---------------- forward: Phi ----------------
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buf[0][wr(r)] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    int cur = 0;
+    for (int t = 1; t < T; ++t) {
+        const double sp = (double)s[t - 1];
+        const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
+        const float gp = gu[t - 1];
+        const float sft = soft_at(t - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float ph[4][2];   // Phi_{t-1}[(a, 4 tid + 2h + i)]
+            int xq[4][2];     // Xn_{t-1}[(a, 4 tid + 2h + i)]
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float2 v = half(cur, rd(a), h);
+                phs[phi_slot(t - 1, a, h)] = v;
+                ph[a][0] = v.x; ph[a][1] = v.y;
+                int2 q = make_int2(0, 0);
+                if (t >= 2) q = xst[(((size_t)(t - 2) * 4 + a) * 2 + h) * NT + tid];
+                xq[a][0] = q.x; xq[a][1] = q.y;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 2 * h + i;
+                float out[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    double lw[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        lw[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(xq[a][i]));
+                    const double m = max64(max64(lw[0], lw[1]), max64(lw[2], lw[3]));
+                    float num = 0.f, den = 0.f;
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float p = fast_exp2((float)(lw[a] - m));
+                        den += p;
+                        num += p * (ph[a][i] + gp * (Cv[a][r][x] - sft));
+                    }
+                    out[x] = num * __builtin_amdgcn_rcpf(den);   // den >= 1: its largest term is 2^0
+                }
+                buf[cur ^ 1][wr(r)] = make_float4(out[0], out[1], out[2], out[3]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        cur ^= 1;
+        __syncthreads();
+    }
+    // Phi_{T-1}
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) phs[phi_slot(T - 1, a, h)] = half(cur, rd(a), h);
+
+    // ---------------- backward: Psi and the covariance sums ----------------
+    // Psi_{T-1} = 0 (the buffer not read by the last forward step)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buf[cur ^ 1][wr(r)] = make_float4(0.f, 0.f, 0.f, 0.f);
+    cur ^= 1;
+    __syncthreads();   // also orders this workgroup's Phi stores before their reads
+    // One backward step at u: the covariance sums of step u and, if PRODUCE (u >= 1),
+    // Psi_{u-1}.  The step with u = 0 is peeled so that the loop body has no branches.
+    auto bstep = [&](int u, auto produce_tag) {
+        constexpr bool PRODUCE = decltype(produce_tag)::value;
+        const double sp = (double)s[u];
+        const double wp = WEIGHTED ? (double)w[u] : 1.0;
+        const float gp = gu[u];
+        const float sft = soft_at(u);
+        const double Ou = ofs[u];
+        float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float ps[2][4];   // Psi_u[(4 tid + 2h + i, x)]
+            int yq[2][4];     // Yn_u[(4 tid + 2h + i, x)]
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float4 v = buf[cur][wr(2 * h + i)];
+                ps[i][0] = v.x; ps[i][1] = v.y; ps[i][2] = v.z; ps[i][3] = v.w;
+                const int4 q = yst[((size_t)u * 4 + 2 * h + i) * NT + tid];
+                yq[i][0] = q.x; yq[i][1] = q.y; yq[i][2] = q.z; yq[i][3] = q.w;
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                int2 xq = make_int2(0, 0);   // Xn_0 = 0
+                if constexpr (PRODUCE) xq = xst[(((size_t)(u - 1) * 4 + a) * 2 + h) * NT + tid];
+                const float2 ph = phs[phi_slot(u, a, h)];
+                const int xqi[2] = {xq.x, xq.y};
+                const float phi[2] = {ph.x, ph.y};
+                float outp[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = 2 * h + i;
+                    const double xo = from_fix(xqi[i]) - Ou;
+                    double lq[4];
+                    float cj[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        lq[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(yq[i][x]));
+                        cj[x] = Cv[a][r][x] - sft;
+                        const float gm = fast_exp2((float)(xo + lq[x]));
+                        const float f = phi[i] + gp * cj[x] + ps[i][x];
+                        S0 += gm;
+                        S1 += gm * cj[x];
+                        S2 += gm * f;
+                        S3 += gm * (cj[x] * f);
+                    }
+                    if constexpr (PRODUCE) {
+                        const double m = max64(max64(lq[0], lq[1]), max64(lq[2], lq[3]));
+                        float num = 0.f, den = 0.f;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const float q = fast_exp2((float)(lq[x] - m));
+                            den += q;
+                            num += q * (gp * cj[x] + ps[i][x]);
+                        }
+                        outp[i] = num * __builtin_amdgcn_rcpf(den);
+                    }
+                }
+                if constexpr (PRODUCE) half(cur ^ 1, rd(a), h) = make_float2(outp[0], outp[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        S0 = wave_sum<WID>(S0);
+        S1 = wave_sum<WID>(S1);
+        S2 = wave_sum<WID>(S2);
+        S3 = wave_sum<WID>(S3);
+        if (lane == 0) {
+            float* vp = vpart + ((size_t)u * kWaves + wave) * 4;
+            vp[0] = S0; vp[1] = S1; vp[2] = S2; vp[3] = S3;
+        }
+        if constexpr (PRODUCE) {
+            cur ^= 1;
+            __syncthreads();
+        }
+    };
+    for (int u = T - 1; u >= 1; --u) bstep(u, std::true_type{});
+    bstep(0, std::false_type{});
+}
+
+// grad[b][u] = (2 w_u / tau) (S3 / S0 - (S1 / S0)(S2 / S0)), the S's summed over waves.
+template <int L>
+__global__ void __launch_bounds__(256)
+bcjr_vjp_finalize(const char* __restrict__ ws, const float* __restrict__ wts, int T, int64_t n,
+                  int64_t b0, double two_over_tau, float* __restrict__ grad)
+{
+    using Ly = BcjrLayout<L>;
+    constexpr int kWaves = Ly::kWaves;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n * T) return;
+    const int64_t i = idx / T;
+    const int u = (int)(idx - i * T);
+    const char* base = ws + (size_t)i * Ly::bytes_per_seq_vjp(T);
+    const float* vp = reinterpret_cast<const float*>(base + Ly::off_vpart(T));
+    double S[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) S[k] += (double)vp[((size_t)u * kWaves + q) * 4 + k];
+    const double cov = S[3] / S[0] - (S[1] / S[0]) * (S[2] / S[0]);
+    const double wu = wts ? (double)wts[(b0 + i) * T + u] : 1.0;
+    grad[(b0 + i) * T + u] = (float)(two_over_tau * wu * cov);
+}
+
+}  // namespace qtcq

@@ -11,6 +11,7 @@
 #include "viterbi.hpp"
 #include "decode.hpp"
 #include "bcjr.hpp"
+#include "bcjr_vjp.hpp"
 
 namespace {
 
@@ -215,11 +216,61 @@ qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float t
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
         hipLaunchKernelGGL((bcjr_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
-                           wsc, T, n, b0, soft, log_z);
+                           wsc, per, T, n, b0, soft, log_z);
         rc = launch_status();
         if (rc != QTCQ_OK) return rc;
     }
     return QTCQ_OK;
+}
+
+// ---- BCJR gradient (vector-Jacobian product) ------------------------------------------
+// Per chunk: the soft pass in VJP mode (stashes both message directions and the posterior
+// offsets), its finalize when soft / log Z are wanted, the Phi / Psi sweep, the gradient.
+template <int L, int CODE, bool W>
+qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t B, int T,
+                    float temperature, float* grad, float* soft, float* log_z, void* ws,
+                    size_t ws_bytes, hipStream_t st)
+{
+    using Tr = Trellis<L>;
+    const size_t per = BcjrLayout<L>::bytes_per_seq_vjp(T);
+    const int64_t per_chunk = (int64_t)(ws_bytes / per);
+    const double kappa = 1.4426950408889634074 / (double)temperature;
+    const double two_over_tau = 2.0 / (double)temperature;
+    char* wsc = static_cast<char*>(ws);
+    for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
+        const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
+        hipLaunchKernelGGL((bcjr_sweep<L, CODE, W, true>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
+                           st, seq, w, T, b0, kappa, wsc);
+        qtcq_status rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+        if (soft || log_z) {
+            hipLaunchKernelGGL((bcjr_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
+                               wsc, per, T, n, b0, soft, log_z);
+            rc = launch_status();
+            if (rc != QTCQ_OK) return rc;
+        }
+        hipLaunchKernelGGL((bcjr_vjp_sweep<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
+                           st, seq, w, gup, T, b0, kappa, wsc);
+        rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+        hipLaunchKernelGGL((bcjr_vjp_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
+                           wsc, w, T, n, b0, two_over_tau, grad);
+        rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+    }
+    return QTCQ_OK;
+}
+
+template <int L>
+qtcq_status vjp_dispatch_code(int code, bool weighted, const float* seq, const float* w,
+                              const float* gup, int64_t B, int T, float temperature, float* grad,
+                              float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return weighted ? vjp_all<L, kCode1Mad, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)
+                        : vjp_all<L, kCode1Mad, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st);
+    return weighted ? vjp_all<L, kCode3Inst, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)
+                    : vjp_all<L, kCode3Inst, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st);
 }
 
 template <int L>
@@ -265,6 +316,11 @@ struct DecodeF {
     static qtcq_status run(A... a) { return decode_dispatch_code<L>(a...); }
 };
 template <int L>
+struct VjpF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return vjp_dispatch_code<L>(a...); }
+};
+template <int L>
 struct BcjrF {
     template <typename... A>
     static qtcq_status run(A... a) { return bcjr_dispatch_code<L>(a...); }
@@ -302,6 +358,12 @@ size_t qtcq_bcjr_workspace_bytes(int64_t B, int T, int L, int k)
 {
     if (!supported_trellis(L, k) || T < 1 || T > kMaxT || B < 0) return 0;
     return (size_t)(B > 0 ? B : 1) * bcjr_bytes_per_seq(T, L);
+}
+
+size_t qtcq_bcjr_vjp_workspace_bytes(int64_t B, int T, int L, int k)
+{
+    if (!supported_trellis(L, k) || T < 1 || T > kMaxT || B < 0) return 0;
+    return (size_t)(B > 0 ? B : 1) * bcjr_bytes_per_seq(T, L, true);
 }
 
 qtcq_status qtcq_code_table(int code, int L, float* out, void* stream)
@@ -400,6 +462,22 @@ qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int 
         return QTCQ_ERR_WORKSPACE;
     return by_L<BcjrF>(L, code, err_w != nullptr, seq, err_w, B, T, temperature, soft, log_z,
                        workspace, workspace_bytes, as_stream(stream));
+}
+
+qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
+                          int code, float temperature, const float* grad_soft, float* grad_seq,
+                          float* soft, float* log_z, void* workspace, size_t workspace_bytes,
+                          void* stream)
+{
+    if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
+    if (!(temperature > 0.0f) || !__builtin_isfinite(temperature)) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (B == 0) return QTCQ_OK;
+    if (!seq || !grad_soft || !grad_seq) return QTCQ_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < bcjr_bytes_per_seq(T, L, true))
+        return QTCQ_ERR_WORKSPACE;
+    return by_L<VjpF>(L, code, err_w != nullptr, seq, err_w, grad_soft, B, T, temperature,
+                      grad_seq, soft, log_z, workspace, workspace_bytes, as_stream(stream));
 }
 
 }  // extern "C"
