@@ -13,6 +13,7 @@ Extra objects on the line:
   tailbiting    -- the tail-biting encode (two searches per sequence) of a 4096x4096
                    matrix
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
+  bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
 """
 from __future__ import annotations
@@ -61,7 +62,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
     ap.add_argument("--no-tb", action="store_true", help="skip the tail-biting encode")
-    ap.add_argument("--cpu-seqs", type=int, default=1536)
+    ap.add_argument("--cpu-seqs", type=int, default=4096)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
     ap.add_argument("--calib-copy", action="store_true",
@@ -229,7 +230,7 @@ def main() -> int:
         bname = "bcjr4096x4096_1mad"
         sb_host, _, _ = inputs.workload(bname)
         sb = torch.from_numpy(sb_host).to(dev)
-        bws = api.bcjr_workspace(sb.shape[0], T, L, K, max_bytes=16 << 30)
+        bws = api.bcjr_workspace(sb.shape[0], T, L, K)
         api.bcjr_soft(sb[:256], 0.1, workspace=bws)      # warm-up
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -242,7 +243,26 @@ def main() -> int:
                        "seconds": bsec, "seq_per_s": sb.shape[0] / bsec,
                        "weights_per_s": sb.shape[0] * T / bsec}
         print("[bench] bcjr %.3f s" % bsec, file=sys.stderr, flush=True)
-        del bws
+        del bws, soft, logz
+
+        # gradient of the soft codeword (soft pass in VJP mode + expectation messages)
+        g = torch.from_numpy(np.random.default_rng(9).standard_normal(sb.shape, dtype=np.float32)).to(dev)
+        vws = api.bcjr_vjp_workspace(sb.shape[0], T, L, K)
+        api.bcjr_vjp(sb[:256], 0.1, g[:256], workspace=vws)      # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        grad, _, _ = api.bcjr_vjp(sb, 0.1, g, workspace=vws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vsec = e0.elapsed_time(e1) / 1000.0
+        out["bcjr_vjp"] = {"workload": "gradient of the soft codeword w.r.t. the targets, "
+                                       "65536 sequences x T=256, N(0,1) seed 5, upstream "
+                                       "N(0,1) seed 9, L=16, 1MAD, tau=0.1",
+                           "seconds": vsec, "seq_per_s": sb.shape[0] / vsec,
+                           "finite": bool(torch.isfinite(grad).all().item())}
+        print("[bench] bcjr vjp %.3f s" % vsec, file=sys.stderr, flush=True)
+        del vws, grad, g
 
     if not args.no_cpu:
         import oracle

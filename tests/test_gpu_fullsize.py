@@ -1,5 +1,5 @@
 """GPU checks at the full workload sizes, in the launch configuration the benchmark
-times (64 GiB workspace cap): sampled sequences (first, last and seeded random rows)
+times (64 GiB encode workspace cap, the library's default BCJR / gradient caps): sampled sequences (first, last and seeded random rows)
 against the oracle bit for bit, and properties that hold for every sequence --
 decoding the stream reproduces the encoder's MSE bit for bit, the stream's pad bits are
 zero, and the mean MSE matches the pages' free-start value (0.065 +- 0.002 at L = 16).
@@ -10,7 +10,7 @@ import pytest
 import oracle
 from trellis_coded_weight_amd import inputs
 
-from helpers import bcjr_err, dev, oracle_bcjr_par, oracle_viterbi_par, say, u32
+from helpers import bcjr_err, dev, oracle_bcjr_par, oracle_viterbi_par, oracle_vjp_par, say, u32
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +83,20 @@ def test_bcjr_full(api):
         assert err.max() <= 1e-5, "tau %g err %g" % (tau, err.max())
         lz = logz.cpu().numpy()[rows].astype(np.float64)
         assert np.all(np.abs(lz - logz_o) <= 1e-5 * np.maximum(1.0, np.abs(logz_o)))
+
+
+def test_bcjr_vjp_full(api):
+    s, _, code = inputs.workload("bcjr4096x4096_1mad")
+    B, T = s.shape
+    g = np.random.default_rng(9).standard_normal((B, T), dtype=np.float32)
+    say("full-size bcjr vjp B=%d tau=0.1" % B)
+    grad, soft, _ = api.bcjr_vjp(dev(s), 0.1, dev(g), L=16, k=2, code=code, want_soft=True)
+    sync()
+    gh = grad.cpu().numpy()
+    assert np.isfinite(gh).all()
+    rows = sample_rows(B, 3, 10)
+    C = oracle.code_table(code, 16)
+    grad_o, soft_o = oracle_vjp_par(C, s[rows], 0.1, g[rows].astype(np.float64), L=16)
+    assert bcjr_err(soft.cpu().numpy()[rows], soft_o).max() <= 1e-5
+    err = bcjr_err(gh[rows], grad_o)
+    assert err.max() <= 1e-5, "grad err %g" % err.max()

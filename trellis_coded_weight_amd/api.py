@@ -35,22 +35,36 @@ def code_table(code="1mad", L: int = 16) -> torch.Tensor:
     return out
 
 
+# Default workspace caps of the one-workgroup-per-sequence passes (BCJR soft pass and
+# its gradient): a chunk of sequences is one launch, so the cap bounds HBM use while
+# keeping each launch many workgroups deep.
+BCJR_WS_CAP = 16 << 30
+VJP_WS_CAP = 32 << 30
+
+
+def _chunk_bytes(B: int, per: int, max_bytes: int | None) -> int:
+    """Workspace bytes for min(B, what max_bytes holds) sequences of `per` bytes.  A
+    partial batch is rounded down to whole multiples of the device's CU count, so that
+    no launch ends with a nearly empty round of workgroups."""
+    if max_bytes is None or B * per <= max_bytes:
+        return max(1, B) * per
+    n = max(1, max_bytes // per)
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    if n > cus:
+        n = n // cus * cus
+    return n * per
+
+
 def encode_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
                      max_bytes: int | None = None) -> torch.Tensor:
-    need = nat.qtcq_encode_workspace_bytes(B, T, L, k)
-    if max_bytes is not None:
-        per = nat.qtcq_encode_workspace_bytes(1, T, L, k)
-        need = max(per, min(need, max_bytes // per * per))
-    return torch.empty(need, dtype=torch.uint8, device="cuda")
+    per = nat.qtcq_encode_workspace_bytes(1, T, L, k)
+    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
 
 def bcjr_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
-                   max_bytes: int | None = None) -> torch.Tensor:
-    need = nat.qtcq_bcjr_workspace_bytes(B, T, L, k)
-    if max_bytes is not None:
-        per = nat.qtcq_bcjr_workspace_bytes(1, T, L, k)
-        need = max(per, min(need, max_bytes // per * per))
-    return torch.empty(need, dtype=torch.uint8, device="cuda")
+                   max_bytes: int | None = BCJR_WS_CAP) -> torch.Tensor:
+    per = nat.qtcq_bcjr_workspace_bytes(1, T, L, k)
+    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
 
 def encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16, k: int = 2,
@@ -99,7 +113,7 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
     soft = torch.empty((B, T), dtype=torch.float32, device=seq.device)
     logz = torch.empty(B, dtype=torch.float32, device=seq.device)
     if workspace is None:
-        workspace = bcjr_workspace(B, T, L, k, max_bytes=8 << 30)
+        workspace = bcjr_workspace(B, T, L, k)
     nat.qtcq_bcjr_soft(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
                        _code(code), temperature, soft.data_ptr(), logz.data_ptr(),
                        workspace.data_ptr(), workspace.numel(), _stream())
@@ -107,12 +121,9 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
 
 
 def bcjr_vjp_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
-                       max_bytes: int | None = None) -> torch.Tensor:
-    need = nat.qtcq_bcjr_vjp_workspace_bytes(B, T, L, k)
-    if max_bytes is not None:
-        per = nat.qtcq_bcjr_vjp_workspace_bytes(1, T, L, k)
-        need = max(per, min(need, max_bytes // per * per))
-    return torch.empty(need, dtype=torch.uint8, device="cuda")
+                       max_bytes: int | None = VJP_WS_CAP) -> torch.Tensor:
+    per = nat.qtcq_bcjr_vjp_workspace_bytes(1, T, L, k)
+    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
 
 def bcjr_vjp(seq: torch.Tensor, temperature: float, grad_soft: torch.Tensor,
@@ -129,7 +140,7 @@ def bcjr_vjp(seq: torch.Tensor, temperature: float, grad_soft: torch.Tensor,
     soft = torch.empty((B, T), dtype=torch.float32, device=seq.device) if want_soft else None
     logz = torch.empty(B, dtype=torch.float32, device=seq.device) if want_soft else None
     if workspace is None:
-        workspace = bcjr_vjp_workspace(B, T, L, k, max_bytes=8 << 30)
+        workspace = bcjr_vjp_workspace(B, T, L, k)
     nat.qtcq_bcjr_vjp(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
                       _code(code), temperature, grad_soft.data_ptr(), grad.data_ptr(),
                       None if soft is None else soft.data_ptr(),
@@ -144,11 +155,8 @@ def tailbiting_words(L: int = 16, k: int = 2, T: int = 256) -> int:
 
 def tailbiting_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
                          max_bytes: int | None = None) -> torch.Tensor:
-    need = nat.qtcq_tailbiting_workspace_bytes(B, T, L, k)
-    if max_bytes is not None:
-        per = nat.qtcq_tailbiting_workspace_bytes(1, T, L, k)
-        need = max(per, min(need, max_bytes // per * per))
-    return torch.empty(need, dtype=torch.uint8, device="cuda")
+    per = nat.qtcq_tailbiting_workspace_bytes(1, T, L, k)
+    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
 
 def tailbiting_encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16,
