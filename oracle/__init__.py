@@ -426,3 +426,31 @@ def brute_tailbiting(C, s, w=None, L=6, k=2):
                                          _p(w, ctypes.c_float), T, L, k, _p(best, ctypes.c_float),
                                          _p(n, ctypes.c_int64)), "brute_tailbiting")
     return best[0], int(n[0])
+
+
+# ---------------------------------------------------------------------------------
+# Decode -> matrix-vector product (inference side)
+# ---------------------------------------------------------------------------------
+# QTIP blog, "What it buys end to end": every 16x16 tile of a weight matrix is one
+# 256-long sequence that decodes straight into the matrix operand.  Reading (the pages
+# give no order): tiles are numbered row-major, sequence b = I * (N / 16) + J holds
+# tile (I, J), and within a tile weight t = 16 r + c is W[16 I + r][16 J + c].
+
+TILE = 16
+
+
+def tiles_to_matrix(vals, M: int, N: int) -> np.ndarray:
+    """Assemble the M x N matrix from per-tile sequences vals [(M/16)(N/16)][256]."""
+    v = np.asarray(vals)
+    assert M % TILE == 0 and N % TILE == 0 and v.shape == ((M // TILE) * (N // TILE), TILE * TILE)
+    return v.reshape(M // TILE, N // TILE, TILE, TILE).transpose(0, 2, 1, 3).reshape(M, N)
+
+
+def decode_matvec(words, M: int, N: int, C, x, L=16, k=2, tailbiting=False) -> np.ndarray:
+    """y [Bx][M] = W x_i for every row x_i of x [Bx][N], in binary64, with W the window
+    decode (plain or cyclic) of the tile streams words [(M/16)(N/16)][W]."""
+    dec = tb_decode if tailbiting else decode
+    _, rec = dec(words, TILE * TILE, C, L, k)
+    Wm = tiles_to_matrix(rec, M, N).astype(np.float64)
+    x2 = np.asarray(x, dtype=np.float64).reshape(-1, N)
+    return x2 @ Wm.T
