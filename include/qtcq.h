@@ -224,6 +224,28 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
                                    float* recon, const float* seq, const float* err_w, float* mse,
                                    void* stream);
 
+/* ---- Decode -> matrix-vector product [QTIP "What it buys end to end": each 16x16 tile
+ * of a weight matrix is one 256-weight sequence that decodes straight into the matrix
+ * operand; batch-1 inference streams the 2-bit weights] ------------------------------
+ * y[i][m] = sum_n W[m][n] x[i][n] for the M x N matrix W whose 16x16 tiles are the
+ * sequences of `bits`, numbered row-major: sequence I*(N/16) + J is tile (I, J), and its
+ * weight t = 16 r + c is W[16 I + r][16 J + c] (the window decode of qtcq_decode, or of
+ * qtcq_tailbiting_decode when `tailbiting` != 0, at T = 256).
+ *   bits  [(M/16)*(N/16)][W] uint32, W = qtcq_bitstream_words(L,k,256) (17 at L=16) or,
+ *         tail-biting, qtcq_tailbiting_words(L,k,256) (16)
+ *   M, N  multiples of 16 (N = 0 gives y = 0)
+ *   x     [batch][N] float32, 16-byte aligned (may be NULL when N = 0);
+ *         y [batch][M] float32 (out)
+ *   batch 0..8 activation rows (0: nothing to do)
+ * Arithmetic: fp32 FMA of each exact fp32 code value with x, partial sums added in a
+ * fixed order (bit-deterministic; a one-hot x returns a column of W exactly); error
+ * <= (16 ceil(N/1024) + 17) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.
+ * Errors: QTCQ_ERR_INVALID_ARG (M or N negative or not multiples of 16, NULL or
+ * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8),
+ * QTCQ_ERR_DEVICE. */
+qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, int code,
+                               int tailbiting, const float* x, int batch, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,6 +143,32 @@ def test_bcjr_vjp_validation(nat):
     assert call(B=0, seq=None, g=None, grad=None, ws=None, wsb=0) == nat.QTCQ_OK
 
 
+def test_decode_matvec_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_decode_matvec", *a)
+    # bits, M, N, L, k, code, tb, x, batch, y, stream
+    ok = [FAKE, 32, 64, 16, 2, 0, 0, FAKE, 1, FAKE, None]
+    names = ["bits", "M", "N", "L", "k", "code", "tb", "x", "batch", "y", "stream"]
+
+    def call(**kw):
+        a = list(ok)
+        for kk, v in kw.items():
+            a[names.index(kk)] = v
+        return st(*a)
+
+    assert call(M=24) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(N=-16) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(batch=-1) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(batch=9) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(code=4) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(x=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(x=FAKE + 4) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(y=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(bits=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(M=0, bits=None, x=None, y=None) == nat.QTCQ_OK
+    assert call(batch=0, bits=None, x=None, y=None) == nat.QTCQ_OK
+
+
 def test_tailbiting_sizes(nat):
     assert nat.qtcq_tailbiting_words(16, 2, 256) == 16     # exactly 2T bits, word-aligned
     assert nat.qtcq_tailbiting_words(16, 2, 8) == 1

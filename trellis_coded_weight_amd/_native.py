@@ -56,6 +56,7 @@ _SIGS = {
     "qtcq_bcjr_vjp_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_bcjr_vjp": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
+    "qtcq_decode_matvec": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
     "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
@@ -165,3 +166,9 @@ def raw_status(name: str, *args) -> int:
     for a, t in zip(args, _SIGS[name][1]):
         conv.append(_ptr(a) if t is _vp else a)
     return fn(*conv)
+
+
+def qtcq_decode_matvec(bits: int, M: int, N: int, L: int, k: int, code: int, tailbiting: bool,
+                       x: int, batch: int, y: int, stream: int = 0) -> None:
+    _check(_lib.qtcq_decode_matvec(_ptr(bits), M, N, L, k, code, 1 if tailbiting else 0, _ptr(x),
+                                   batch, _ptr(y), _ptr(stream)), "qtcq_decode_matvec")

@@ -199,3 +199,22 @@ def tailbiting_decode(bits: torch.Tensor, T: int, L: int = 16, k: int = 2, code=
                                None if weights is None else weights.data_ptr(),
                                None if mse is None else mse.data_ptr(), _stream())
     return recon, mse
+
+
+def decode_matvec(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: int = 16, k: int = 2,
+                  code="1mad", tailbiting: bool = False) -> torch.Tensor:
+    """y [batch][M] = W x for the M x N matrix whose row-major 16x16 tiles are the
+    T = 256 streams `bits` ([(M/16)(N/16)][W]); x [batch][N] (or [N]) float32 on device."""
+    one = x.dim() == 1
+    x2 = x.reshape(1, -1) if one else x
+    _dev_f32(x2, "x")
+    if x2.shape[1] != N:
+        raise ValueError("x must have N columns")
+    W = tailbiting_words(L, k, 256) if tailbiting else bitstream_words(L, k, 256)
+    if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
+            and bits.numel() == (M // 16) * (N // 16) * W):
+        raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
+    y = torch.empty((x2.shape[0], M), dtype=torch.float32, device=x.device)
+    nat.qtcq_decode_matvec(bits.data_ptr(), M, N, L, k, _code(code), tailbiting, x2.data_ptr(),
+                           x2.shape[0], y.data_ptr(), _stream())
+    return y[0] if one else y

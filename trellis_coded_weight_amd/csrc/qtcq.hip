@@ -12,6 +12,7 @@
 #include "decode.hpp"
 #include "bcjr.hpp"
 #include "bcjr_vjp.hpp"
+#include "matvec.hpp"
 
 namespace {
 
@@ -300,6 +301,35 @@ qtcq_status by_L(int L, Args&&... args)
     }
 }
 
+// ---- decode -> matrix-vector product --------------------------------------------------
+
+template <int L, int CODE, bool TB>
+qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int batch, float* y,
+                        hipStream_t st)
+{
+    const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
+    hipLaunchKernelGGL((decode_matvec<L, CODE, TB>), dim3((unsigned)(M / 16)),
+                       dim3(MatvecShape::kThreads), 0, st, bits, M, N, Wd, x, batch, y);
+    return launch_status();
+}
+
+template <int L>
+qtcq_status matvec_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
+                                 const float* x, int batch, float* y, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return tb ? matvec_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, st)
+                  : matvec_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, st);
+    return tb ? matvec_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, st)
+              : matvec_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, st);
+}
+
+template <int L>
+struct MatvecF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return matvec_dispatch_code<L>(a...); }
+};
+
 template <int L>
 struct EncodeF {
     template <typename... A>
@@ -478,6 +508,17 @@ qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T
         return QTCQ_ERR_WORKSPACE;
     return by_L<VjpF>(L, code, err_w != nullptr, seq, err_w, grad_soft, B, T, temperature,
                       grad_seq, soft, log_z, workspace, workspace_bytes, as_stream(stream));
+}
+
+qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, int code,
+                               int tailbiting, const float* x, int batch, float* y, void* stream)
+{
+    if (M < 0 || N < 0 || (M % 16) != 0 || (N % 16) != 0 || batch < 0) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (batch > MatvecShape::kMaxBatch) return QTCQ_ERR_UNSUPPORTED;
+    if (M == 0 || batch == 0) return QTCQ_OK;
+    if (!y || (N > 0 && (!x || !aligned16(x) || !bits))) return QTCQ_ERR_INVALID_ARG;
+    return by_L<MatvecF>(L, code, tailbiting != 0, bits, M, N, x, batch, y, as_stream(stream));
 }
 
 }  // extern "C"
