@@ -15,6 +15,7 @@ Extra objects on the line:
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
   bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
+  decode_matvec -- y = W x straight from the streams (per launch, batch 1 and 8)
 """
 from __future__ import annotations
 
@@ -62,6 +63,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
     ap.add_argument("--no-tb", action="store_true", help="skip the tail-biting encode")
+    ap.add_argument("--no-matvec", action="store_true", help="skip the decode -> matvec")
     ap.add_argument("--cpu-seqs", type=int, default=4096)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
@@ -192,6 +194,43 @@ def main() -> int:
         "mse_mean": float(mse.mean().item()),
     }
     del ws
+
+    if not args.no_matvec and B == 65536:
+        # decode -> matrix-vector product straight from the streams just encoded (the
+        # 4096x4096 matrix as 16x16 tiles), and from 4096x14336 (3INST) and 28672x8192
+        # (1MAD) matrices of tail-biting streams (random words: every bit pattern is a
+        # stream; the rate does not depend on the content).  Per launch, back to back.
+        mv = {}
+        cases = [("4096x4096 1MAD plain (the encoded matrix)", bits, 4096, 4096, "1mad", False)]
+        g = np.random.default_rng(13)
+        tbw = api.tailbiting_words(L, K, T)
+        rand_bits = torch.from_numpy(g.integers(0, 1 << 32, size=(256 * 896, tbw), dtype=np.uint32)
+                                     .view(np.int32)).to(dev)
+        cases.append(("4096x14336 3INST tail-biting", rand_bits, 4096, 14336, "3inst", True))
+        big_bits = torch.from_numpy(g.integers(0, 1 << 32, size=(1792 * 512, tbw), dtype=np.uint32)
+                                    .view(np.int32)).to(dev)
+        cases.append(("28672x8192 1MAD tail-biting", big_bits, 28672, 8192, "1mad", True))
+        reps = 200
+        for label, bb, M_, N_, cd, tbf in cases:
+            for nb in (1, 8):
+                xv = torch.from_numpy(g.standard_normal((nb, N_), dtype=np.float32)).to(dev)
+                api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                sec = e0.elapsed_time(e1) / 1000.0 / reps
+                nbytes = bb.numel() * 4 + nb * (N_ + M_) * 4
+                mv["%s, batch %d" % (label, nb)] = {
+                    "us": sec * 1e6, "weights_per_s": M_ * N_ / sec,
+                    "hbm_gbs": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / PEAK_HBM_GBS}
+        out["decode_matvec"] = mv
+        print("[bench] decode matvec " + ", ".join("%.1f us" % v["us"] for v in mv.values()),
+              file=sys.stderr, flush=True)
+        del rand_bits, big_bits
 
     if not args.no_tb:
         # tail-biting encode of the same matrix: two forward searches per sequence

@@ -237,9 +237,10 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
  *   x     [batch][N] float32, 16-byte aligned (may be NULL when N = 0);
  *         y [batch][M] float32 (out)
  *   batch 0..8 activation rows (0: nothing to do)
- * Arithmetic: fp32 FMA of each exact fp32 code value with x, partial sums added in a
- * fixed order (bit-deterministic; a one-hot x returns a column of W exactly); error
- * <= (16 ceil(N/1024) + 17) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.
+ * Arithmetic: fp32 FMA of each code value before its rescale (exact in fp32) with x,
+ * partial sums added in a fixed order, then the code's rescale applied once per output
+ * (bit-deterministic; a one-hot x returns a column of W exactly); error
+ * <= (4 ceil(N/1024) + 22) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.
  * Errors: QTCQ_ERR_INVALID_ARG (M or N negative or not multiples of 16, NULL or
  * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8),
  * QTCQ_ERR_DEVICE. */

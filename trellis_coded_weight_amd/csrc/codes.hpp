@@ -5,11 +5,13 @@
 // state, then either the byte sum of the LCG output (1MAD) or an fp16 bit trick with
 // one fp16 add (3INST; XOR-Trellis explainer, "The sign at each junction has to be
 // cheap").  The final rescale is a binary64 division rounded once to binary32, so every
-// code value is a fixed bit pattern.  The device multiplies by the binary64 reciprocal
-// of the divisor instead of dividing: over the whole input domain of each code (byte
-// sums 0..1020; every finite fp16 value) the product rounds to the same binary32 value
-// as the quotient -- checked exhaustively on the host -- and it costs one fp64 multiply
-// instead of an IEEE division sequence.  v_sad_u8 forms the byte sum.
+// code value is a fixed bit pattern.  The device gets the same bits with binary32 work
+// only: v * (1/D) is split as v * r_hi + v * r_lo, where r_hi (13 significant bits)
+// makes v * r_hi exact and one FMA adds v * r_lo with a single rounding.  Over the whole
+// input domain of each code (byte sums 0..1020; every finite fp16 value below 4 in
+// magnitude) this rounds to the same binary32 value as the binary64 quotient -- checked
+// exhaustively on the host with exact rational arithmetic.  The LCG product uses 24-bit
+// multiplies (states have at most 24 bits), and v_sad_u8 forms the byte sum.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,28 +21,45 @@ namespace qtcq {
 
 enum : int { kCode1Mad = 0, kCode3Inst = 1 };
 
+// LCG of a state x < 2^24: (34038481 x + 76625530) mod 2^32, with the multiplier split
+// as 519 * 2^16 + 25297 so that both partial products are 24-bit multiplies.
+// (Written as instructions: the compiler would fold the two products back into one
+// 32-bit v_mul_lo_u32, a multi-pass instruction.)
 __device__ __forceinline__ uint32_t lcg_step(uint32_t x)
 {
-    return x * 34038481u + 76625530u;   // modulo 2^32
+    uint32_t lo, hi;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(lo) : "v"(x), "s"(25297u), "v"(76625530u));
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(hi) : "s"(519u), "v"(x));
+    return lo + (hi << 16);
 }
 
-// Sum of the four bytes of u: v_sad_u8 accumulates |byte_i(u) - byte_i(0)|.
-__device__ __forceinline__ uint32_t byte_sum(uint32_t u)
+// Binary32 split of 1/147.8 and 1/1.244 (the binary64 divisors): r_hi has 13 significant
+// bits, r_lo = fl32(1/D - r_hi).
+constexpr float k1MadRhi = 0x1.bb7p-8f;        // 0x3BDDB800
+constexpr float k1MadRlo = -0x1.c2569ap-22f;    // 0xB4E12B4D
+constexpr float k3InstRhi = 0x1.9b9p-1f;        // 0x3F4DC800
+constexpr float k3InstRlo = 0x1.ac09ep-16f;     // 0x37D604F0
+
+// fl32(v / D) for the code's domain: v * r_hi is exact, the FMA rounds once.
+__device__ __forceinline__ float rescale(float v, float rhi, float rlo)
 {
-    return __builtin_amdgcn_sad_u8(u, 0u, 0u);
+    return __builtin_fmaf(v, rlo, v * rhi);
 }
 
-// 1MAD for a byte sum S in [0, 1020]: (S - 510) / 147.8 in binary64, then binary32.
-__device__ __forceinline__ float mad_value_from_bytesum(uint32_t S)
+// 1MAD before the rescale: S - 510 (exact) for the byte sum S of u.  v_sad_u8 adds the
+// byte sum to an accumulator whose bits are those of the float 2^23 + 514, so the sum
+// reads as the float 2^23 + 514 + S exactly, and one exact subtraction gives S - 510.
+__device__ __forceinline__ float code_1mad_raw(uint32_t x)
 {
-    constexpr double kInv = 1.0 / 147.8;   // binary64 reciprocal of the binary64 divisor
-    double q = (double)((int)S - 510) * kInv;
-    return (float)q;
+    constexpr uint32_t kBias = 0x4B000000u + 514u;   // float 8389122.0
+    const uint32_t t = __builtin_amdgcn_sad_u8(lcg_step(x), 0u, kBias);
+    return __builtin_bit_cast(float, t) - 8389632.0f;   // 2^23 + 1024
 }
 
+// 1MAD: (S - 510) / 147.8
 __device__ __forceinline__ float code_1mad(uint32_t x)
 {
-    return mad_value_from_bytesum(byte_sum(lcg_step(x)));
+    return rescale(code_1mad_raw(x), k1MadRhi, k1MadRlo);
 }
 
 // 3INST raw value: the two fp16 halves of (u & 0x8FFF8FFF) ^ 0x3B603B60 added in fp16.
@@ -54,9 +73,27 @@ __device__ __forceinline__ _Float16 code_3inst_raw(uint32_t x)
 
 __device__ __forceinline__ float code_3inst(uint32_t x)
 {
-    constexpr double kInv = 1.0 / 1.244;
-    double q = (double)(float)code_3inst_raw(x) * kInv;
-    return (float)q;
+    return rescale((float)code_3inst_raw(x), k3InstRhi, k3InstRlo);
+}
+
+// The code before its rescale (exact in binary32), and the rescale itself:
+// code_value(x) = code_rescale(code_raw(x)) bit for bit.
+template <int CODE>
+__device__ __forceinline__ float code_raw(uint32_t x)
+{
+    if constexpr (CODE == kCode1Mad)
+        return code_1mad_raw(x);
+    else
+        return (float)code_3inst_raw(x);
+}
+
+template <int CODE>
+__device__ __forceinline__ float code_rescale(float v)
+{
+    if constexpr (CODE == kCode1Mad)
+        return rescale(v, k1MadRhi, k1MadRlo);
+    else
+        return rescale(v, k3InstRhi, k3InstRlo);
 }
 
 template <int CODE>

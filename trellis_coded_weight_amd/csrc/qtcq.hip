@@ -308,8 +308,15 @@ qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int 
                         hipStream_t st)
 {
     const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
-    hipLaunchKernelGGL((decode_matvec<L, CODE, TB>), dim3((unsigned)(M / 16)),
-                       dim3(MatvecShape::kThreads), 0, st, bits, M, N, Wd, x, batch, y);
+    const dim3 grid((unsigned)(M / 16)), block(MatvecShape::kThreads);
+    if (batch <= 1)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else if (batch <= 2)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else if (batch <= 4)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 8>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
     return launch_status();
 }
 
