@@ -1,0 +1,94 @@
+"""GPU parity at the largest sizes the C ABI accepts and at odd batch shapes: sequences
+of T = 4096 weights (the maximum) through the plain and tail-biting encoders, the
+decoders, the BCJR soft pass and its gradient; odd batches (the encoder interleaves two
+sequences per workgroup); the decode -> matvec with a 65,536-wide inner dimension.
+Each against the oracle at the bar of its own test module."""
+import numpy as np
+import pytest
+
+import oracle
+from trellis_coded_weight_amd import inputs
+
+from helpers import bcjr_err, dev, oracle_bcjr_par, oracle_vjp_par, say
+from test_gpu_encode import check_encode
+from test_gpu_tailbiting import check_tb
+
+pytestmark = pytest.mark.gpu
+
+TMAX = 4096
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    from trellis_coded_weight_amd import api as a
+    return a
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("L,B,code,weighted", [(16, 3, "1mad", False), (12, 5, "3inst", True)])
+def test_encode_decode_longest_sequences(api, L, B, code, weighted):
+    s = inputs.targets(B, TMAX, 4242 + L)
+    w = inputs.weights(B, TMAX, 4243 + L) if weighted else None
+    check_encode(api, s, w, L, code)
+
+
+@pytest.mark.parametrize("L,B", [(16, 2), (10, 3)])
+def test_tailbiting_longest_sequences(api, L, B):
+    s = inputs.targets(B, TMAX, 4343 + L)
+    check_tb(api, s, None, L, "1mad")
+
+
+def test_encode_odd_batch_L16(api):
+    s = inputs.targets(7, 256, 4444)
+    check_encode(api, s, None, 16, "1mad")
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.01])
+def test_bcjr_longest_sequences(api, tau):
+    L, B = 8, 3
+    s = inputs.targets(B, TMAX, 4545)
+    say("bcjr T=%d L=%d tau=%g" % (TMAX, L, tau))
+    soft, logz = api.bcjr_soft(dev(s), tau, L=L)
+    sync()
+    C = oracle.code_table("1mad", L)
+    soft_o, logz_o = oracle_bcjr_par(C, s, tau, L=L)
+    assert bcjr_err(soft.cpu().numpy(), soft_o).max() <= 1e-5
+    lz = logz.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(lz - logz_o) <= 1e-5 * np.maximum(1.0, np.abs(logz_o)))
+
+
+def test_bcjr_vjp_longest_sequence(api):
+    L, B, tau = 8, 2, 0.1
+    s = inputs.targets(B, TMAX, 4646)
+    g = np.random.default_rng(4647).standard_normal((B, TMAX)).astype(np.float32)
+    say("bcjr vjp T=%d L=%d" % (TMAX, L))
+    grad, _, _ = api.bcjr_vjp(dev(s), tau, dev(g), L=L)
+    sync()
+    C = oracle.code_table("1mad", L)
+    grad_o, _ = oracle_vjp_par(C, s, tau, g.astype(np.float64), L=L)
+    assert bcjr_err(grad.cpu().numpy(), grad_o).max() <= 1e-5
+
+
+def test_matvec_wide_inner_dimension(api):
+    import torch
+    M, N, L = 32, 65536, 16
+    W = oracle.stream_words(L, 2, 256)
+    words = np.random.default_rng(4748).integers(0, 1 << 32, size=((M // 16) * (N // 16), W),
+                                                  dtype=np.uint32)
+    x = inputs.targets(2, N, 4749)
+    say("matvec M=%d N=%d" % (M, N))
+    y = api.decode_matvec(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x))
+    sync()
+    C = oracle.code_table("1mad", L)
+    y_o = oracle.decode_matvec(words, M, N, C, x, L, 2)
+    _, rec = oracle.decode(words, 256, C, L, 2)
+    Wm = oracle.tiles_to_matrix(rec, M, N).astype(np.float64)
+    mag = np.abs(x.astype(np.float64)) @ np.abs(Wm).T
+    bound = (4 * -(-N // 1024) + 23) * 2.0 ** -24 * mag
+    assert np.all(np.abs(y.cpu().numpy() - y_o) <= bound)

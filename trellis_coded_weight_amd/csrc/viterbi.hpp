@@ -233,8 +233,10 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     // Targets (and weights) go through a small LDS ring of two 256-step chunks per
     // sequence and are read one phase ahead with the input loads: a per-step scalar
     // load would be waited on together with the LDS reads (one shared counter) and
-    // stall every phase.  Chunk k + 1 is loaded at the start of step 256 k into the
-    // slot chunk k - 1 used; every read of that chunk happened before step 256 k.
+    // stall every phase.  Chunk k + 1 is loaded at the start of step 256 k + 1 into the
+    // slot chunk k - 1 used: the last reads of chunk k - 1 are A's target of step
+    // 256 k - 1 (phase 2 of step 256 k - 1) and B's (phase 1 of step 256 k), both behind
+    // a barrier by then; chunk k + 1 is first read at step 256 (k + 1).
     constexpr int kChunk = 256;
     constexpr int kRing = WEIGHTED ? 4 : 2;    // sa, sb [, wa, wb]
     __shared__ float ring[kRing][2][kChunk];
@@ -262,7 +264,7 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     float spA = ring_at(0, 0), spB = 0.f;
     float wpA = WEIGHTED ? ring_at(2, 0) : 1.0f, wpB = 1.0f;
     for (int t = 1; t < T; ++t) {
-        if (t % kChunk == 0 && t + kChunk < T) fill(t / kChunk + 1);
+        if (t > kChunk && t % kChunk == 1 && (t / kChunk + 1) * kChunk < T) fill(t / kChunk + 1);
         // phase 1: fetch B's inputs and target, step A
         load_in(muB, inB);
         spB = ring_at(1, t - 1);
