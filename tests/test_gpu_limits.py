@@ -92,3 +92,19 @@ def test_matvec_wide_inner_dimension(api):
     mag = np.abs(x.astype(np.float64)) @ np.abs(Wm).T
     bound = (4 * -(-N // 1024) + 23) * 2.0 ** -24 * mag
     assert np.all(np.abs(y.cpu().numpy() - y_o) <= bound)
+
+
+@pytest.mark.parametrize("L", [14, 16])
+@pytest.mark.parametrize("T", [1, 2, 37])
+def test_bcjr_and_gradient_short_sequences_multiwave(api, L, T):
+    """Multi-wave workgroups (4 waves at L = 14, 16 at L = 16) on short sequences."""
+    B, tau = 2, 0.1
+    s = inputs.targets(B, T, 4800 + L + T)
+    g = np.random.default_rng(4900 + L + T).standard_normal((B, T)).astype(np.float32)
+    say("bcjr + vjp L=%d T=%d" % (L, T))
+    grad, soft, logz = api.bcjr_vjp(dev(s), tau, dev(g), L=L, want_soft=True)
+    sync()
+    C = oracle.code_table("1mad", L)
+    grad_o, soft_o = oracle_vjp_par(C, s, tau, g.astype(np.float64), L=L)
+    assert bcjr_err(soft.cpu().numpy(), soft_o).max() <= 1e-5
+    assert bcjr_err(grad.cpu().numpy(), grad_o).max() <= 1e-5
