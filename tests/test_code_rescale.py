@@ -6,7 +6,9 @@ fma(v, r_lo, v * r_hi) in binary32, with r_hi = 1/D rounded to 13 significant bi
 binary32 bits on the code's whole input domain: every byte sum minus 510 (1MAD) and
 every finite fp16 value below 4 in magnitude (3INST raw values are fp16 sums of two
 halves in +-[0.125, 2)).  Both domains are small, so this is checked exhaustively with
-exact rational arithmetic.  The split constants are the ones written in codes.hpp."""
+exact rational arithmetic.  The split constants are the ones written in codes.hpp.
+The search kernels' once-per-workgroup form multiplies by the binary64 reciprocal of
+the divisor instead, checked on the same domains."""
 from fractions import Fraction
 
 import numpy as np
@@ -66,3 +68,18 @@ def test_3inst_rescale_exact_on_all_fp16_values():
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
     h = h[np.isfinite(h)].astype(np.float64)
     check(h[np.abs(h) < 4], 1.244, SPLIT_3INST)
+
+
+def test_1mad_binary64_reciprocal_exact_on_all_byte_sums():
+    num = (np.arange(0, 1021, dtype=np.int64) - 510).astype(np.float64)
+    want = (num / 147.8).astype(np.float32)
+    got = (num * (1.0 / 147.8)).astype(np.float32)
+    assert np.array_equal(want.view(np.uint32), got.view(np.uint32))
+
+
+def test_3inst_binary64_reciprocal_exact_on_all_fp16_values():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    h = h[np.isfinite(h)].astype(np.float64)
+    want = (h / 1.244).astype(np.float32)
+    got = (h * (1.0 / 1.244)).astype(np.float32)
+    assert np.array_equal(want.view(np.uint32), got.view(np.uint32))

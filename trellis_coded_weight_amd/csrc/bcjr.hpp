@@ -255,7 +255,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
+                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
                 __builtin_amdgcn_sched_barrier(0);
             }
 

@@ -76,6 +76,27 @@ __device__ __forceinline__ float code_3inst(uint32_t x)
     return rescale((float)code_3inst_raw(x), k3InstRhi, k3InstRlo);
 }
 
+// The same values in the form the search kernels compute once per workgroup: the
+// 32-bit LCG product and the rescale by the binary64 reciprocal of the divisor (which
+// rounds to the same binary32 value as the binary64 quotient on the same domains, also
+// checked exhaustively on the host).  Their cost does not matter there, and with this
+// form the step loops keep their register allocation (no spills).
+template <int CODE>
+__device__ __forceinline__ float code_value_prologue(uint32_t x)
+{
+    const uint32_t u = x * 34038481u + 76625530u;
+    if constexpr (CODE == kCode1Mad) {
+        const int n = (int)__builtin_amdgcn_sad_u8(u, 0u, 0u) - 510;
+        return (float)((double)n * (1.0 / 147.8));
+    } else {
+        const uint32_t v = (u & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+        const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+        const _Float16 h = hi + lo;   // one fp16 add, round to nearest even
+        return (float)((double)(float)h * (1.0 / 1.244));
+    }
+}
+
 // The code before its rescale (exact in binary32), and the rescale itself:
 // code_value(x) = code_rescale(code_raw(x)) bit for bit.
 template <int CODE>

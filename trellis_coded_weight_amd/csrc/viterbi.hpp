@@ -140,7 +140,7 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x));
+                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x));
                 __builtin_amdgcn_sched_barrier(0);
             }
 
