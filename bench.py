@@ -67,6 +67,8 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=4096)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
+    ap.add_argument("--bcjr-seqs", type=int, default=0,
+                    help="profiling only: run the BCJR passes on the first N sequences")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
@@ -267,7 +269,7 @@ def main() -> int:
 
     if not args.no_bcjr:
         bname = "bcjr4096x4096_1mad"
-        sb_host, _, _ = inputs.workload(bname)
+        sb_host, _, _ = inputs.workload(bname, B=args.bcjr_seqs or None)
         sb = torch.from_numpy(sb_host).to(dev)
         bws = api.bcjr_workspace(sb.shape[0], T, L, K)
         api.bcjr_soft(sb[:256], 0.1, workspace=bws)      # warm-up
@@ -278,7 +280,8 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         bsec = e0.elapsed_time(e1) / 1000.0
-        out["bcjr"] = {"workload": "65536 sequences x T=256, N(0,1) seed 5, L=16, 1MAD, tau=0.1",
+        out["bcjr"] = {"workload": "%d sequences x T=256, N(0,1) seed 5, L=16, 1MAD, tau=0.1"
+                                   % sb.shape[0],
                        "seconds": bsec, "seq_per_s": sb.shape[0] / bsec,
                        "weights_per_s": sb.shape[0] * T / bsec}
         print("[bench] bcjr %.3f s" % bsec, file=sys.stderr, flush=True)
@@ -296,8 +299,8 @@ def main() -> int:
         torch.cuda.synchronize()
         vsec = e0.elapsed_time(e1) / 1000.0
         out["bcjr_vjp"] = {"workload": "gradient of the soft codeword w.r.t. the targets, "
-                                       "65536 sequences x T=256, N(0,1) seed 5, upstream "
-                                       "N(0,1) seed 9, L=16, 1MAD, tau=0.1",
+                                       "%d sequences x T=256, N(0,1) seed 5, upstream "
+                                       "N(0,1) seed 9, L=16, 1MAD, tau=0.1" % sb.shape[0],
                            "seconds": vsec, "seq_per_s": sb.shape[0] / vsec,
                            "finite": bool(torch.isfinite(grad).all().item())}
         print("[bench] bcjr vjp %.3f s" % vsec, file=sys.stderr, flush=True)
