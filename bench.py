@@ -201,7 +201,9 @@ def main() -> int:
         # decode -> matrix-vector product straight from the streams just encoded (the
         # 4096x4096 matrix as 16x16 tiles), and from 4096x14336 (3INST) and 28672x8192
         # (1MAD) matrices of tail-biting streams (random words: every bit pattern is a
-        # stream; the rate does not depend on the content).  Per launch, back to back.
+        # stream; the rate does not depend on the content).  Per launch, back to back, through
+        # the C entry point with preallocated outputs (the smallest shape is near the host's
+        # launch rate).
         mv = {}
         cases = [("4096x4096 1MAD plain (the encoded matrix)", bits, 4096, 4096, "1mad", False)]
         g = np.random.default_rng(13)
@@ -216,12 +218,14 @@ def main() -> int:
         for label, bb, M_, N_, cd, tbf in cases:
             for nb in (1, 8):
                 xv = torch.from_numpy(g.standard_normal((nb, N_), dtype=np.float32)).to(dev)
-                api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)
+                yv = api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)   # checks shapes
+                codei = nat.QTCQ_CODE_1MAD if cd == "1mad" else nat.QTCQ_CODE_3INST
+                args_ = (bb.data_ptr(), M_, N_, L, K, codei, tbf, xv.data_ptr(), nb, yv.data_ptr(), sptr)
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for _ in range(reps):
-                    api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)
+                    nat.qtcq_decode_matvec(*args_)
                 e1.record(stream)
                 torch.cuda.synchronize()
                 sec = e0.elapsed_time(e1) / 1000.0 / reps
