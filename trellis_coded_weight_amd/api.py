@@ -25,6 +25,36 @@ def _dev_f32(x: torch.Tensor, name: str) -> torch.Tensor:
     return x
 
 
+def _like_seq(x: torch.Tensor | None, seq: torch.Tensor, name: str) -> None:
+    """An optional per-weight tensor (error weights, upstream gradient) shaped as seq."""
+    if x is not None:
+        _dev_f32(x, name)
+        if x.shape != seq.shape:
+            raise ValueError("%s must have the shape of seq" % name)
+
+
+def _dev_words(bits: torch.Tensor, B: int, W: int) -> None:
+    """Streams as the kernels read them: B rows of W contiguous 32-bit words."""
+    if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
+            and bits.dtype in (torch.int32, torch.uint32) and tuple(bits.shape) == (B, W)):
+        raise ValueError("bits must be a contiguous [%d][%d] 32-bit device tensor" % (B, W))
+
+
+def _decode_inputs(bits, T, W, seq, weights, want_mse):
+    B = bits.shape[0]
+    if W < 0:
+        raise ValueError("unsupported (L, k, T)")
+    _dev_words(bits, B, W)
+    if seq is not None:
+        _dev_f32(seq, "seq")
+        if tuple(seq.shape) != (B, T):
+            raise ValueError("seq must be [B][T]")
+        _like_seq(weights, seq, "weights")
+    elif want_mse or weights is not None:
+        raise ValueError("the MSE needs seq (and weights only come with seq)")
+    return B
+
+
 def bitstream_words(L: int = 16, k: int = 2, T: int = 256) -> int:
     return nat.qtcq_bitstream_words(L, k, T)
 
@@ -35,9 +65,9 @@ def code_table(code="1mad", L: int = 16) -> torch.Tensor:
     return out
 
 
-# Default workspace caps of the one-workgroup-per-sequence passes (BCJR soft pass and
-# its gradient): a chunk of sequences is one launch, so the cap bounds HBM use while
-# keeping each launch many workgroups deep.
+# Default workspace caps: a chunk of sequences is one launch, so the cap bounds HBM use
+# while keeping each launch many workgroups deep (the 4096x4096 encode fits one chunk).
+ENCODE_WS_CAP = 64 << 30
 BCJR_WS_CAP = 16 << 30
 VJP_WS_CAP = 32 << 30
 
@@ -56,7 +86,7 @@ def _chunk_bytes(B: int, per: int, max_bytes: int | None) -> int:
 
 
 def encode_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
-                     max_bytes: int | None = None) -> torch.Tensor:
+                     max_bytes: int | None = ENCODE_WS_CAP) -> torch.Tensor:
     per = nat.qtcq_encode_workspace_bytes(1, T, L, k)
     return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
@@ -73,10 +103,7 @@ def encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16, 
     mse [B] float32, states [B][T] int32 view of uint32 or None)."""
     _dev_f32(seq, "seq")
     B, T = seq.shape
-    if weights is not None:
-        _dev_f32(weights, "weights")
-        if weights.shape != seq.shape:
-            raise ValueError("weights must have the shape of seq")
+    _like_seq(weights, seq, "weights")
     W = nat.qtcq_bitstream_words(L, k, T)
     bits = torch.empty((B, W), dtype=torch.int32, device=seq.device)
     mse = torch.empty(B, dtype=torch.float32, device=seq.device)
@@ -94,7 +121,7 @@ def decode(bits: torch.Tensor, T: int, L: int = 16, k: int = 2, code="1mad",
            seq: torch.Tensor | None = None, weights: torch.Tensor | None = None,
            want_recon: bool = True, want_mse: bool = False):
     """Window-decode [B][W] streams.  Returns (recon [B][T] or None, mse [B] or None)."""
-    B = bits.shape[0]
+    B = _decode_inputs(bits, T, nat.qtcq_bitstream_words(L, k, T), seq, weights, want_mse)
     recon = torch.empty((B, T), dtype=torch.float32, device=bits.device) if want_recon else None
     mse = torch.empty(B, dtype=torch.float32, device=bits.device) if want_mse else None
     nat.qtcq_decode(bits.data_ptr(), B, T, L, k, _code(code),
@@ -109,6 +136,7 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
               L: int = 16, k: int = 2, code="1mad", workspace: torch.Tensor | None = None):
     """BCJR soft codewords.  Returns (soft [B][T] float32, log_z [B] float32)."""
     _dev_f32(seq, "seq")
+    _like_seq(weights, seq, "weights")
     B, T = seq.shape
     soft = torch.empty((B, T), dtype=torch.float32, device=seq.device)
     logz = torch.empty(B, dtype=torch.float32, device=seq.device)
@@ -132,10 +160,9 @@ def bcjr_vjp(seq: torch.Tensor, temperature: float, grad_soft: torch.Tensor,
     """Gradient of sum_t grad_soft[b][t] * soft[b][t] with respect to seq.  Returns
     (grad_seq [B][T] float32, soft [B][T] or None, log_z [B] or None)."""
     _dev_f32(seq, "seq")
-    _dev_f32(grad_soft, "grad_soft")
+    _like_seq(grad_soft, seq, "grad_soft")
+    _like_seq(weights, seq, "weights")
     B, T = seq.shape
-    if grad_soft.shape != seq.shape:
-        raise ValueError("grad_soft must have the shape of seq")
     grad = torch.empty((B, T), dtype=torch.float32, device=seq.device)
     soft = torch.empty((B, T), dtype=torch.float32, device=seq.device) if want_soft else None
     logz = torch.empty(B, dtype=torch.float32, device=seq.device) if want_soft else None
@@ -154,7 +181,7 @@ def tailbiting_words(L: int = 16, k: int = 2, T: int = 256) -> int:
 
 
 def tailbiting_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
-                         max_bytes: int | None = None) -> torch.Tensor:
+                         max_bytes: int | None = ENCODE_WS_CAP) -> torch.Tensor:
     per = nat.qtcq_tailbiting_workspace_bytes(1, T, L, k)
     return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
 
@@ -166,10 +193,7 @@ def tailbiting_encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L:
     (bits [B][ceil(kT/32)] int32 view of uint32 words, mse [B], states [B][T] or None)."""
     _dev_f32(seq, "seq")
     B, T = seq.shape
-    if weights is not None:
-        _dev_f32(weights, "weights")
-        if weights.shape != seq.shape:
-            raise ValueError("weights must have the shape of seq")
+    _like_seq(weights, seq, "weights")
     W = nat.qtcq_tailbiting_words(L, k, T)
     if W < 0:
         raise ValueError("tail-biting needs k*T >= L")
@@ -190,7 +214,7 @@ def tailbiting_decode(bits: torch.Tensor, T: int, L: int = 16, k: int = 2, code=
                       want_recon: bool = True, want_mse: bool = False):
     """Cyclic window decode of [B][W] tail-biting streams.  Returns (recon or None,
     mse or None)."""
-    B = bits.shape[0]
+    B = _decode_inputs(bits, T, nat.qtcq_tailbiting_words(L, k, T), seq, weights, want_mse)
     recon = torch.empty((B, T), dtype=torch.float32, device=bits.device) if want_recon else None
     mse = torch.empty(B, dtype=torch.float32, device=bits.device) if want_mse else None
     nat.qtcq_tailbiting_decode(bits.data_ptr(), B, T, L, k, _code(code),
