@@ -16,6 +16,8 @@ Extra objects on the line:
   bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
   decode_matvec -- y = W x straight from the streams (per launch, batch 1 and 8)
+  configs       -- the other encode configurations (16 sequences; 4096x14336 3INST;
+                   weighted 4096x4096) and the BCJR pass at tau = 1, 0.1, 0.01
 """
 from __future__ import annotations
 
@@ -64,6 +66,8 @@ def main() -> int:
     ap.add_argument("--no-bcjr", action="store_true", help="skip the BCJR pass")
     ap.add_argument("--no-tb", action="store_true", help="skip the tail-biting encode")
     ap.add_argument("--no-matvec", action="store_true", help="skip the decode -> matvec")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other encode / BCJR configurations")
     ap.add_argument("--cpu-seqs", type=int, default=4096)
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
@@ -309,6 +313,53 @@ def main() -> int:
                            "finite": bool(torch.isfinite(grad).all().item())}
         print("[bench] bcjr vjp %.3f s" % vsec, file=sys.stderr, flush=True)
         del vws, grad, g
+
+    if not args.no_configs and not args.seqs:
+        # the other configurations of the path, one timed call each after a warm-up:
+        # encode (+ decode with the round-trip MSE) of 16 sequences, of the 4096x14336
+        # matrix in 3INST and of the weighted 4096x4096 matrix; the BCJR soft pass of the
+        # 4096x4096 matrix at each temperature
+        cfg = {}
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1000.0, r
+
+        for wname in ("enc16_1mad", "enc4096x14336_3inst", "enc4096x4096_1mad_weighted"):
+            sh, wh, cd = inputs.workload(wname)
+            sd = torch.from_numpy(sh).to(dev)
+            wd = None if wh is None else torch.from_numpy(wh).to(dev)
+            Bc = sd.shape[0]
+            cws = api.encode_workspace(Bc, T, L, K)
+            esec, (cb, cm, _) = timed(lambda: api.encode(sd, wd, L=L, k=K, code=cd, workspace=cws))
+            dsec, (_, cm2) = timed(lambda: api.decode(cb, T, L=L, k=K, code=cd, seq=sd, weights=wd,
+                                                      want_mse=True))
+            ops = (acs_ops_per_sequence(T, wd is not None)) * Bc
+            cfg[wname] = {"sequences": Bc, "code": cd, "weighted": wd is not None,
+                          "encode_ms": esec * 1e3, "decode_ms": dsec * 1e3,
+                          "weights_per_s": Bc * T / (esec + dsec),
+                          "encode_valu_frac": ops / esec / 1e12 / PEAK_VALU_TOPS,
+                          "mse_mean": float(cm.mean().item()),
+                          "decoded_mse_equal": bool(torch.equal(cm, cm2))}
+            del sd, wd, cws, cb, cm, cm2
+        sh, _, _ = inputs.workload("bcjr4096x4096_1mad")
+        sd = torch.from_numpy(sh).to(dev)
+        bws = api.bcjr_workspace(sd.shape[0], T, L, K)
+        for tau in (1.0, 0.1, 0.01):
+            bsec, (bsoft, _) = timed(lambda: api.bcjr_soft(sd, tau, workspace=bws))
+            cfg["bcjr4096x4096_1mad tau=%g" % tau] = {
+                "sequences": sd.shape[0], "seconds": bsec, "seq_per_s": sd.shape[0] / bsec,
+                "finite": bool(torch.isfinite(bsoft).all().item())}
+        del sd, bws
+        out["configs"] = cfg
+        print("[bench] configs " + ", ".join("%s %.3g ms" % (k, v.get("encode_ms", v.get("seconds", 0) * 1e3))
+                                             for k, v in cfg.items()), file=sys.stderr, flush=True)
 
     if not args.no_cpu:
         import oracle
