@@ -77,7 +77,7 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are "
+        print("bench.py measures one GPU: the library has no multi-GPU path (sequences are "
               "independent; see the design notes on sharding)", file=sys.stderr)
         return 2
 

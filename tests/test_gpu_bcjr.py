@@ -117,3 +117,25 @@ def test_bcjr_zero_temperature_limit(api, L, T):
         # at tau = 1e-5 every position with a clear gap carries the hard value
         clear = ok & (nwalks_log - gap / 1e-5 < np.log(1e-7))
         assert errs[2][b][clear].max() <= 1e-6
+
+
+@pytest.mark.parametrize("L", [8, 16])
+def test_bcjr_high_temperature(api, L):
+    """tau -> infinity: every walk weighs the same, so the soft codeword is the mean code
+    value (about -0.002 / -0.0004 at L = 8 / 16) at every step.  The soft values then
+    cancel to near 0 while the sums behind them average code values of unit scale, so the
+    bound is taken against that scale (the error of a sum with cancellation is relative
+    to the magnitude of its terms): |soft_gpu - soft_oracle| <= 1e-5 * RMS(C)."""
+    import torch
+    B, T, tau = 2, 64, 1e6
+    s = inputs.targets(B, T, 620 + L)
+    say("bcjr high temperature L=%d" % L)
+    soft, logz = api.bcjr_soft(dev(s), tau, L=L)
+    sync()
+    C = oracle.code_table("1mad", L).astype(np.float64)
+    soft_o, logz_o = oracle_bcjr_par(C.astype(np.float32), s, tau, L=L)
+    rms_c = np.sqrt((C ** 2).mean())
+    assert np.abs(soft.cpu().numpy() - soft_o).max() <= 1e-5 * rms_c
+    assert np.abs(soft_o - C.mean()).max() <= 1e-4
+    lz = logz.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(lz - logz_o) <= TOL * np.maximum(1.0, np.abs(logz_o)))
