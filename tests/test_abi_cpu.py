@@ -216,3 +216,25 @@ def test_product_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "qtcq_oracle" not in text, f
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/qtcq.h compiles as C11 with warnings as errors, and a C program taking the
+    address of every declared entry point links against the built library."""
+    import subprocess
+    from trellis_coded_weight_amd import _native
+    syms = declared_symbols()
+    src = tmp_path / "use_abi.c"
+    src.write_text('#include "qtcq.h"\n#include <stdio.h>\n'
+                   "typedef void (*fn)(void);\n"
+                   "int main(void) {\n    fn p[] = {\n" +
+                   "".join("        (fn)&%s,\n" % n for n in syms) +
+                   "    };\n    printf(\"%d\\n\", (int)(sizeof p / sizeof p[0]));\n"
+                   "    return qtcq_bitstream_words(16, 2, 256) == 17 ? 0 : 1;\n}\n")
+    exe = tmp_path / "use_abi"
+    lib = os.path.dirname(_native.LIB_PATH)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I" + os.path.join(ROOT, "include"),
+           str(src), "-o", str(exe), "-L" + lib, "-l:libqtcq.so", "-Wl,-rpath," + lib,
+           "-Wl,--unresolved-symbols=ignore-in-shared-libs"]
+    subprocess.run(cmd, check=True, capture_output=True)
+    assert exe.exists()
