@@ -151,7 +151,7 @@ def test_tailbiting_full_size(api, name, mse_ref):
     m = mse.cpu().numpy()
     assert abs(float(m.mean()) - mse_ref) <= 0.002
     rng = np.random.default_rng(11)
-    rows = np.array(sorted(set([0, B - 1]) | set(rng.choice(B, size=10, replace=False).tolist())))
+    rows = np.array(sorted(set([0, B - 1]) | set(rng.choice(B, size=1022, replace=False).tolist())))
     C = oracle.code_table(code, 16)
     st_o, _, mse_o = oracle_tb_par(C, s[rows], L=16)
     assert np.array_equal(u32(bits)[rows], oracle.tb_pack(st_o, 16, 2))
