@@ -32,7 +32,9 @@
 // backward message is added.
 // Posterior at t: gamma_t(j) = 2^( la_t(j) + lb_t(j) - log2 Z ), computed in the backward
 // sweep from the stashed Xn_t[(a, c)], the normalised backward input Yn_t[(c, x)] =
-// Y_t - h_t and the step energy, with the exact offset O_t = log2 Z - G_t - H_t.
+// Y_t - h_t and the step energy, with the exact offset O_t = log2 Z - G_t - H_t.  The
+// four states (a, c, x), x = 0..3, are the inputs of one backward LSE, so their
+// posteriors reuse its exponentials: one more exp2 per group instead of four.
 // soft_t = sum gamma C / sum gamma: per-wave partial sums per step go to the
 // workspace, a small kernel divides.
 // VJP mode (for the gradient kernel, bcjr_vjp.hpp) also stashes Yn_t in the same
@@ -413,6 +415,33 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     }
 
     // ---------------- backward + posterior ----------------
+    // The backward keeps more values live per step (the stash and the posterior sums), so
+    // it holds the code values as their raw values (1MAD: S - 510, an integer below 2^10;
+    // 3INST: the fp16 sum -- both exact in fp16), two per register, and rescales one at
+    // each use: 32 registers instead of 64, which keeps the step loop free of spills.
+    uint32_t Ch[4][4][2];   // [a][r][x >> 1], x even in the low half
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int hx = 0; hx < 2; ++hx) {
+                const uint32_t j = (uint32_t)(a * M + 16 * tid + 4 * r + 2 * hx);
+                const float lo = code_raw<CODE>(j), hi = code_raw<CODE>(j + 1);
+                Ch[a][r][hx] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    // (the widening is written as an instruction so that it stays at its use: hoisted out
+    // of the step loop, the 64 decoded values would again need 64 registers)
+    auto code_at = [&](int a, int r, int x) -> float {
+        float f;
+        if (x & 1)
+            asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
+                         : "=v"(f) : "v"(Ch[a][r][x >> 1]));
+        else
+            asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(Ch[a][r][x >> 1]));
+        return code_rescale<CODE>(f);
+    };
     // Y_{T-1} = 0
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
@@ -471,18 +500,30 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
                     const int r = 2 * h + rr;
-                    // posterior exponent = X_t - O_t + (Y_t - h_t) - kappa e_t
-                    const double xo = (from_fix(xsr[r]) - Ot) + ref[r];
+                    float cx[4];
                     double v[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        v[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[r][x]));
-                        const float p = fast_exp2((float)(xo + v[x]));
-                        pg += p;
-                        pc = __builtin_fmaf(p, Cv[a][r][x], pc);
+                        cx[x] = code_at(a, r, x);
+                        v[x] = __builtin_fma(-kappa, energy(cx[x], sp, wp), widen(rel[r][x]));
                     }
+                    // LSE over x (as lse2_4), whose exponentials q_x = 2^(v_x - m) also give
+                    // the posterior of the four states (a, c, x): with the exponent
+                    // X_t - O_t + (Y_t - h_t) - kappa e_t = xo + v_x, each is 2^(xo + m) q_x
+                    const double m = max64(max64(v[0], v[1]), max64(v[2], v[3]));
+                    float q[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) q[x] = fast_exp2((float)(v[x] - m));
+                    const float sq = (q[0] + q[1]) + (q[2] + q[3]);
+                    float qc = q[0] * cx[0];
+#pragma unroll
+                    for (int x = 1; x < 4; ++x) qc = __builtin_fmaf(q[x], cx[x], qc);
+                    const double xo = (from_fix(xsr[r]) - Ot) + ref[r];
+                    const float pb = fast_exp2((float)(xo + m));
+                    pg = __builtin_fmaf(pb, sq, pg);
+                    pc = __builtin_fmaf(pb, qc, pc);
                     if (produce) {
-                        y[rr] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                        y[rr] = ref[r] + (m + (double)fast_log2(sq));
                         ymax = __builtin_fmaxf(ymax, (float)y[rr]);
                     }
                 }

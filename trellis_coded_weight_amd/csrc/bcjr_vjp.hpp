@@ -201,31 +201,32 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = 2 * h + i;
-                    const double xo = from_fix(xqi[i]) - Ou;
                     double lq[4];
-                    float cj[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        lq[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(yq[i][x]));
+                    // Q_x = 2^(lq_x - m) / den; the posterior of state (a, c, x) is
+                    // 2^(Xn_u - O_u + lq_x) = 2^(Xn_u - O_u + m) * 2^(lq_x - m)
+                    const double m = max64(max64(lq[0], lq[1]), max64(lq[2], lq[3]));
+                    float den = 0.f, num = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        lq[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(yq[i][x]));
-                        cj[x] = Cv[a][r][x] - sft;
-                        const float gm = fast_exp2((float)(xo + lq[x]));
-                        const float f = phi[i] + gp * cj[x] + ps[i][x];
-                        S0 += gm;
-                        S1 += gm * cj[x];
-                        S2 += gm * f;
-                        S3 += gm * (cj[x] * f);
+                        const float q = fast_exp2((float)(lq[x] - m));
+                        const float cj = Cv[a][r][x] - sft;
+                        const float bk = gp * cj + ps[i][x];   // the future's part of f
+                        const float f = phi[i] + bk;
+                        den += q;
+                        num += q * bk;
+                        s1 += q * cj;
+                        s2 += q * f;
+                        s3 += q * (cj * f);
                     }
-                    if constexpr (PRODUCE) {
-                        const double m = max64(max64(lq[0], lq[1]), max64(lq[2], lq[3]));
-                        float num = 0.f, den = 0.f;
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            const float q = fast_exp2((float)(lq[x] - m));
-                            den += q;
-                            num += q * (gp * cj[x] + ps[i][x]);
-                        }
-                        outp[i] = num * __builtin_amdgcn_rcpf(den);
-                    }
+                    const float pb = fast_exp2((float)((from_fix(xqi[i]) - Ou) + m));
+                    S0 = __builtin_fmaf(pb, den, S0);
+                    S1 = __builtin_fmaf(pb, s1, S1);
+                    S2 = __builtin_fmaf(pb, s2, S2);
+                    S3 = __builtin_fmaf(pb, s3, S3);
+                    if constexpr (PRODUCE) outp[i] = num * __builtin_amdgcn_rcpf(den);
                 }
                 if constexpr (PRODUCE) half(cur ^ 1, rd(a), h) = make_float2(outp[0], outp[1]);
                 __builtin_amdgcn_sched_barrier(0);
