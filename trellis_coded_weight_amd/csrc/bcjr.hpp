@@ -205,6 +205,43 @@ __device__ __forceinline__ void lds_write4(char* base, int addr, int P, double v
     *reinterpret_cast<double2*>(base + addr + P) = make_double2(v2, v3);
 }
 
+// The code values of a thread's 64 states (a, c = 4 tid + r, x) held as their raw values
+// (1MAD: S - 510, an integer of magnitude below 2^10; 3INST: the fp16 sum -- both exact
+// in fp16), two per register, and rescaled at each use (code_rescale: the same bits as
+// code_value).  The widening is written as an instruction so that it stays at its use:
+// hoisted out of a step loop, the 64 decoded values would need 64 registers again.
+template <int L, int CODE>
+struct PackedCodes {
+    uint32_t w[4][4][2];   // [a][r][x >> 1], x even in the low half
+
+    __device__ __forceinline__ void init(int tid)
+    {
+        constexpr int M = Trellis<L>::kGroups;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int hx = 0; hx < 2; ++hx) {
+                    const uint32_t j = (uint32_t)(a * M + 16 * tid + 4 * r + 2 * hx);
+                    const float lo = code_raw<CODE>(j), hi = code_raw<CODE>(j + 1);
+                    w[a][r][hx] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    }
+
+    __device__ __forceinline__ float at(int a, int r, int x) const
+    {
+        float f;
+        if (x & 1)
+            asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
+                         : "=v"(f) : "v"(w[a][r][x >> 1]));
+        else
+            asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(w[a][r][x >> 1]));
+        return code_rescale<CODE>(f);
+    }
+};
+
 inline size_t bcjr_bytes_per_seq(int T, int L, bool vjp = false)
 {
     switch (L) {
@@ -416,32 +453,10 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 
     // ---------------- backward + posterior ----------------
     // The backward keeps more values live per step (the stash and the posterior sums), so
-    // it holds the code values as their raw values (1MAD: S - 510, an integer below 2^10;
-    // 3INST: the fp16 sum -- both exact in fp16), two per register, and rescales one at
-    // each use: 32 registers instead of 64, which keeps the step loop free of spills.
-    uint32_t Ch[4][4][2];   // [a][r][x >> 1], x even in the low half
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int hx = 0; hx < 2; ++hx) {
-                const uint32_t j = (uint32_t)(a * M + 16 * tid + 4 * r + 2 * hx);
-                const float lo = code_raw<CODE>(j), hi = code_raw<CODE>(j + 1);
-                Ch[a][r][hx] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-    // (the widening is written as an instruction so that it stays at its use: hoisted out
-    // of the step loop, the 64 decoded values would again need 64 registers)
-    auto code_at = [&](int a, int r, int x) -> float {
-        float f;
-        if (x & 1)
-            asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
-                         : "=v"(f) : "v"(Ch[a][r][x >> 1]));
-        else
-            asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(Ch[a][r][x >> 1]));
-        return code_rescale<CODE>(f);
-    };
+    // it holds the code values packed (PackedCodes): 32 registers instead of 64, which
+    // keeps the step loop free of spills.
+    PackedCodes<L, CODE> Ch;
+    Ch.init(tid);
     // Y_{T-1} = 0
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
@@ -504,7 +519,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     double v[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        cx[x] = code_at(a, r, x);
+                        cx[x] = Ch.at(a, r, x);
                         v[x] = __builtin_fma(-kappa, energy(cx[x], sp, wp), widen(rel[r][x]));
                     }
                     // LSE over x (as lse2_4), whose exponentials q_x = 2^(v_x - m) also give

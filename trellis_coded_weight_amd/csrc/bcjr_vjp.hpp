@@ -33,6 +33,10 @@
 
 namespace qtcq {
 
+// Longest sequence the gradient kernel takes (the entry points reject longer ones): the
+// soft codeword of every step is staged in LDS.
+constexpr int kVjpMaxT = 4096;
+
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws: the chunk's VJP
 // workspace as left by bcjr_sweep<..., VJP = true> (bytes_per_seq_vjp(T) per sequence).
 // gup: [*][T] upstream gradient; row b0 + blockIdx.x.
@@ -50,6 +54,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     constexpr int kWaves = Ly::kWaves;
     constexpr int WID = NT < 64 ? NT : 64;
     __shared__ float4 buf[2][NB];
+    __shared__ float softs[kVjpMaxT];   // soft_t, formed as the soft pass's finalize forms it
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -65,16 +70,17 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     float2* phs = reinterpret_cast<float2*>(base + Ly::off_phi(T));              // [t][a][h][tau]
     float* vpart = reinterpret_cast<float*>(base + Ly::off_vpart(T));
 
-    float Cv[4][4][4];   // code value of state (a, c = 4 tid + r, x)
+    for (int t = tid; t < T; t += NT) {
+        float pg = 0.f, pc = 0.f;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                Cv[a][r][x] = code_value<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int q = 0; q < kWaves; ++q) {
+            pg += part[((size_t)t * kWaves + q) * 2 + 0];
+            pc += part[((size_t)t * kWaves + q) * 2 + 1];
+        }
+        softs[t] = pc / pg;
+    }
+    PackedCodes<L, CODE> Cp;   // code values of the states (a, c = 4 tid + r, x)
+    Cp.init(tid);
 
     auto opaque_tid = [&]() {
         int v = tid;
@@ -85,16 +91,6 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     auto wr = [&](int r) { return lds_chunk(4 * opaque_tid() + r); };   // groups (4tid + r, x)
     auto half = [&](int cur, int chunk, int h) -> float2& {
         return reinterpret_cast<float2*>(&buf[cur][chunk])[h];
-    };
-    // soft_t as the soft pass's finalize forms it
-    auto soft_at = [&](int t) -> float {
-        float pg = 0.f, pc = 0.f;
-#pragma unroll
-        for (int q = 0; q < kWaves; ++q) {
-            pg += part[((size_t)t * kWaves + q) * 2 + 0];
-            pc += part[((size_t)t * kWaves + q) * 2 + 1];
-        }
-        return pc / pg;
     };
     // the soft pass's exact binary64 energy
     auto energy = [&](float c, double sp, double wp) -> double {
@@ -116,7 +112,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         const double sp = (double)s[t - 1];
         const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
         const float gp = gu[t - 1];
-        const float sft = soft_at(t - 1);
+        const float sft = softs[t - 1];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float ph[4][2];   // Phi_{t-1}[(a, 4 tid + 2h + i)]
@@ -137,16 +133,19 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     double lw[4];
+                    float cx[4];
 #pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        lw[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(xq[a][i]));
+                    for (int a = 0; a < 4; ++a) {
+                        cx[a] = Cp.at(a, r, x);
+                        lw[a] = __builtin_fma(-kappa, energy(cx[a], sp, wp), from_fix(xq[a][i]));
+                    }
                     const double m = max64(max64(lw[0], lw[1]), max64(lw[2], lw[3]));
                     float num = 0.f, den = 0.f;
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         const float p = fast_exp2((float)(lw[a] - m));
                         den += p;
-                        num += p * (ph[a][i] + gp * (Cv[a][r][x] - sft));
+                        num = __builtin_fmaf(p, __builtin_fmaf(gp, cx[a] - sft, ph[a][i]), num);
                     }
                     out[x] = num * __builtin_amdgcn_rcpf(den);   // den >= 1: its largest term is 2^0
                 }
@@ -176,7 +175,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         const double sp = (double)s[u];
         const double wp = WEIGHTED ? (double)w[u] : 1.0;
         const float gp = gu[u];
-        const float sft = soft_at(u);
+        const float sft = softs[u];
         const double Ou = ofs[u];
         float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
 #pragma unroll
@@ -202,30 +201,34 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                 for (int i = 0; i < 2; ++i) {
                     const int r = 2 * h + i;
                     double lq[4];
+                    float cx[4];
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        lq[x] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), from_fix(yq[i][x]));
+                    for (int x = 0; x < 4; ++x) {
+                        cx[x] = Cp.at(a, r, x);
+                        lq[x] = __builtin_fma(-kappa, energy(cx[x], sp, wp), from_fix(yq[i][x]));
+                    }
                     // Q_x = 2^(lq_x - m) / den; the posterior of state (a, c, x) is
                     // 2^(Xn_u - O_u + lq_x) = 2^(Xn_u - O_u + m) * 2^(lq_x - m)
                     const double m = max64(max64(lq[0], lq[1]), max64(lq[2], lq[3]));
-                    float den = 0.f, num = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+                    // with f = phi + bk (bk = g_u c + Psi_u, the future's part):
+                    //   sum q f = phi den + sum q bk,  sum q c f = phi sum q c + sum q c bk
+                    float den = 0.f, num = 0.f, s1 = 0.f, t3 = 0.f;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const float q = fast_exp2((float)(lq[x] - m));
-                        const float cj = Cv[a][r][x] - sft;
-                        const float bk = gp * cj + ps[i][x];   // the future's part of f
-                        const float f = phi[i] + bk;
+                        const float cj = cx[x] - sft;
+                        const float bk = __builtin_fmaf(gp, cj, ps[i][x]);
+                        const float qc = q * cj;
                         den += q;
-                        num += q * bk;
-                        s1 += q * cj;
-                        s2 += q * f;
-                        s3 += q * (cj * f);
+                        num = __builtin_fmaf(q, bk, num);
+                        s1 += qc;
+                        t3 = __builtin_fmaf(qc, bk, t3);
                     }
                     const float pb = fast_exp2((float)((from_fix(xqi[i]) - Ou) + m));
                     S0 = __builtin_fmaf(pb, den, S0);
                     S1 = __builtin_fmaf(pb, s1, S1);
-                    S2 = __builtin_fmaf(pb, s2, S2);
-                    S3 = __builtin_fmaf(pb, s3, S3);
+                    S2 = __builtin_fmaf(pb, __builtin_fmaf(phi[i], den, num), S2);
+                    S3 = __builtin_fmaf(pb, __builtin_fmaf(phi[i], s1, t3), S3);
                     if constexpr (PRODUCE) outp[i] = num * __builtin_amdgcn_rcpf(den);
                 }
                 if constexpr (PRODUCE) half(cur ^ 1, rd(a), h) = make_float2(outp[0], outp[1]);
