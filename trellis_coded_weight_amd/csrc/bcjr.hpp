@@ -132,12 +132,16 @@ __device__ __forceinline__ int4 xn_load(const int* st, size_t i, int a, int tid)
     }
 }
 
+// Longest sequence the BCJR kernels take (the entry points reject longer ones): per-step
+// scalars (the forward normalisers, the soft codeword) are staged in LDS.
+constexpr int kBcjrMaxT = 4096;
+
 template <int L>
 struct BcjrLayout {
     using Tr = Trellis<L>;
     static constexpr int kWaves = (Tr::kThreads + 63) / 64;
     // Per-sequence workspace, each part 256-byte aligned:
-    //   log2 Z (double) | g_0..g_{T-1} (float) | posterior partial sums [T][kWaves][2]
+    //   log2 Z (double) | posterior partial sums [T][kWaves][2]
     //   | stash Xn_1..Xn_{T-1} (groups (a, 4 tau + r): see xn_store)
     // and in VJP mode, after those:
     //   | Yn_0..Yn_{T-1} ([T][4][kThreads] int4: groups (4 tau + r, x), x = 0..3, at
@@ -145,8 +149,7 @@ struct BcjrLayout {
     //     float2: groups (a, 4 tau + 2h + i), i = 0, 1, at [a][h][tau]) | gradient
     //     partial sums [T][kWaves][4] (float)
     __host__ __device__ static size_t up(size_t b) { return (b + 255) / 256 * 256; }
-    __host__ __device__ static size_t off_g() { return 256; }
-    __host__ __device__ static size_t off_part(int T) { return off_g() + up((size_t)T * 4); }
+    __host__ __device__ static size_t off_part(int) { return 256; }
     __host__ __device__ static size_t off_stash(int T) { return off_part(T) + up((size_t)T * kWaves * 8); }
     __host__ __device__ static size_t bytes_per_seq(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 4); }
     __host__ __device__ static size_t off_ystash(int T) { return bytes_per_seq(T); }
@@ -273,15 +276,17 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     __shared__ __align__(16) char buf[Ld::kBytes];
     __shared__ float wmax[2][kWaves];
     __shared__ float redm[kWaves], reds[kWaves];
+    __shared__ float gsh[kBcjrMaxT];   // the forward normalisers g_0 .. g_{T-1}
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // the wave index in an SGPR: kept in a VGPR across the step loops it would be spilled
+    // and reloaded (an exposed scratch read) at every per-wave store
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int64_t row = b0 + blockIdx.x;
     const float* s = seq + row * T;
     const float* w = WEIGHTED ? wts + row * T : nullptr;
     char* base = ws + (size_t)blockIdx.x * (VJP ? Ly::bytes_per_seq_vjp(T) : Ly::bytes_per_seq(T));
     double* l2z = reinterpret_cast<double*>(base);
-    float* gnorm = reinterpret_cast<float*>(base + Ly::off_g());
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
     int* stash = reinterpret_cast<int*>(base + Ly::off_stash(T));
     int4* ystash = reinterpret_cast<int4*>(base + Ly::off_ystash(T));     // VJP only
@@ -367,12 +372,15 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         }
         __syncthreads();   // every input read before any output overwrites it
         G = uniform64(G + g64);
-        if (tid == 0) gnorm[t - 1] = g;
+        if (tid == 0) gsh[t - 1] = g;
         const double sp = (double)s[t - 1];
         const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            double relw[4];   // the butterfly's four inputs, shared by its four outputs
+#pragma unroll
+            for (int a = 0; a < 4; ++a) relw[a] = widen(rel[a][r]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs x = 2h, 2h + 1
                 double o[2];
@@ -382,7 +390,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     double v[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
-                        v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), widen(rel[a][r]));
+                        v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), relw[a]);
                     o[xx] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
                     lmax = __builtin_fmaxf(lmax, (float)o[xx]);
                 }
@@ -402,7 +410,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
     for (int q = 1; q < kWaves; ++q) gl = __builtin_fmaxf(gl, wmax[par][q]);
     G = uniform64(G + (double)gl);
-    if (tid == 0) gnorm[T - 1] = gl;
+    if (tid == 0) gsh[T - 1] = gl;
     double log2z;
     {
         const double sp = (double)s[T - 1];
@@ -468,6 +476,13 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // One backward step at t (t >= 1 produces Y_{t-1}); the posterior of step t is
     // accumulated on the way.  At t = 0 only the posterior is formed (X_0 = 0).
     auto bstep = [&](int t, bool produce) {
+        // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
+        // ahead; the first before the step's LDS reads and barrier
+        auto stash_at = [&](int a) -> int4 {
+            if (!produce) return make_int4(0, 0, 0, 0);
+            return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
+        };
+        int4 xs_next = stash_at(0);
         float h = wmax[par][0];
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[par][q]);
@@ -492,17 +507,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         H = uniform64(H + h64);                       // H_t
         const double Ot = uniform64(log2z - Gm - H);  // log2 Z - G_t - H_t
         if (VJP && tid == 0) ofs[t] = Ot;
-        Gm = uniform64(Gm - (double)gnorm[t]);        // G_{t-1}
+        Gm = uniform64(Gm - (double)gsh[t]);          // G_{t-1}
         const double sp = (double)s[t];
         const double wp = WEIGHTED ? (double)w[t] : 1.0;
         float pg = 0.f, pc = 0.f;
         float ymax = -__builtin_inff();
-        // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a ahead
-        auto stash_at = [&](int a) -> int4 {
-            if (!produce) return make_int4(0, 0, 0, 0);
-            return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
-        };
-        int4 xs_next = stash_at(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int4 xs = xs_next;

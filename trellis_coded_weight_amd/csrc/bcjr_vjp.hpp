@@ -33,10 +33,6 @@
 
 namespace qtcq {
 
-// Longest sequence the gradient kernel takes (the entry points reject longer ones): the
-// soft codeword of every step is staged in LDS.
-constexpr int kVjpMaxT = 4096;
-
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws: the chunk's VJP
 // workspace as left by bcjr_sweep<..., VJP = true> (bytes_per_seq_vjp(T) per sequence).
 // gup: [*][T] upstream gradient; row b0 + blockIdx.x.
@@ -54,7 +50,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     constexpr int kWaves = Ly::kWaves;
     constexpr int WID = NT < 64 ? NT : 64;
     __shared__ float4 buf[2][NB];
-    __shared__ float softs[kVjpMaxT];   // soft_t, formed as the soft pass's finalize forms it
+    __shared__ float softs[kBcjrMaxT];   // soft_t, formed as the soft pass's finalize forms it
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;

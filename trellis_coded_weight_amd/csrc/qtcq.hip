@@ -19,7 +19,7 @@ namespace {
 using namespace qtcq;
 
 constexpr int kMaxT = 4096;
-static_assert(kMaxT <= kVjpMaxT, "the gradient kernel stages T soft values in LDS");
+static_assert(kMaxT <= kBcjrMaxT, "the BCJR kernels stage T per-step values in LDS");
 
 bool supported_trellis(int L, int k)
 {
