@@ -174,6 +174,15 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         const float sft = softs[u];
         const double Ou = ofs[u];
         float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
+        // Xn_u and Phi_u of the groups (a, 4 tid + 2h + i), loaded one (h, a) ahead of use
+        auto load_xp = [&](int h, int a, int2& xq, float2& ph) {
+            xq = make_int2(0, 0);   // Xn_0 = 0
+            if constexpr (PRODUCE) xq = xst[(((size_t)(u - 1) * 4 + a) * 2 + h) * NT + tid];
+            ph = phs[phi_slot(u, a, h)];
+        };
+        int2 xq_next;
+        float2 ph_next;
+        load_xp(0, 0, xq_next, ph_next);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float ps[2][4];   // Psi_u[(4 tid + 2h + i, x)]
@@ -187,9 +196,12 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                int2 xq = make_int2(0, 0);   // Xn_0 = 0
-                if constexpr (PRODUCE) xq = xst[(((size_t)(u - 1) * 4 + a) * 2 + h) * NT + tid];
-                const float2 ph = phs[phi_slot(u, a, h)];
+                const int2 xq = xq_next;
+                const float2 ph = ph_next;
+                if (a < 3)
+                    load_xp(h, a + 1, xq_next, ph_next);
+                else if (h == 0)
+                    load_xp(1, 0, xq_next, ph_next);
                 const int xqi[2] = {xq.x, xq.y};
                 const float phi[2] = {ph.x, ph.y};
                 float outp[2];
