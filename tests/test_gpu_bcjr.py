@@ -69,6 +69,12 @@ def test_bcjr_L16(api, tau):
     run_and_compare(api, s, None, tau, 16, code)
 
 
+def test_bcjr_L16_3inst_weighted(api):
+    s = inputs.targets(2, 256, 44)
+    w = inputs.weights(2, 256, 45)
+    run_and_compare(api, s, w, 0.1, 16, "3inst")
+
+
 def test_bcjr_chunked_workspace(api):
     import torch
     s = inputs.targets(5, 64, 43)

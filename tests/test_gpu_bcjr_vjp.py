@@ -80,6 +80,12 @@ def test_vjp_L16(api, tau):
     run_and_compare(api, s, None, upstream(2, 256, 54), tau, 16, code)
 
 
+def test_vjp_L16_3inst_weighted(api):
+    s = inputs.targets(2, 256, 58)
+    w = inputs.weights(2, 256, 59)
+    run_and_compare(api, s, w, upstream(2, 256, 60), 0.1, 16, "3inst")
+
+
 def test_vjp_zero_and_linear(api):
     import torch
     L, T, B = 12, 256, 4

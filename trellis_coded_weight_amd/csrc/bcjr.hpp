@@ -342,23 +342,16 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float rel[4][4];    // [a][r]
         double ref[4];      // [r] = max_a X - g
         {
-            // two passes over the four input chunks (maximum, then differences) so that
-            // only one chunk of fp64 inputs is live at a time
-            double mx[4] = {-__builtin_inf(), -__builtin_inf(), -__builtin_inf(), -__builtin_inf()};
+            double xin[4][4];   // [a][r]
+#pragma unroll
+            for (int a = 0; a < 4; ++a) lds_read4(buf, rd(a), P, xin[a]);
+            double mx[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mx[r] = max64(max64(xin[0][r], xin[1][r]), max64(xin[2][r], xin[3][r]));
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                double xa[4];
-                lds_read4(buf, rd(a), P, xa);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx[r] = max64(mx[r], xa[r]);
-            }
-            // keep the second pass's reads (the compiler would reuse the first pass's
-            // sixteen fp64 values, which is what the two passes avoid)
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                double xa[4];
-                lds_read4(buf, rd(a), P, xa);
+                const double (&xa)[4] = xin[a];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) rel[a][r] = (float)(xa[r] - mx[r]);
                 // Xn_{t-1}[(a, 4 tid + r)] (Xn_0 = 0 is not stored)
