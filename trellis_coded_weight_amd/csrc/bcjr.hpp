@@ -17,10 +17,11 @@
 // Precision.  A message accumulates one rounding per step; in fp32 at tau = 0.01 the
 // per-step increments (kappa e ~ 10 log2 units) make those roundings ~1e-6 each, which
 // over ~250 steps shifts competing walks' weights by ~1e-5.  So messages are stored and
-// combined in fp64: the energy is the exact binary64 value of (C - s)^2 [* w] from the
-// binary32 inputs, each LSE's four inputs are held as an fp64 reference (their maximum)
-// plus fp32 differences (the dominant input is then exact), the LSE's max and
-// differences are fp64, and only exp2 / log2 of small arguments run in fp32.
+// combined in fp64: each state's energy term is formed in fp64 from the binary32 inputs
+// (shifted by a per-step constant that cancels, StepEnergy), each LSE's four inputs are
+// held as an fp64 reference (their maximum) plus fp32 differences (the dominant input is
+// then exact), the LSE's max and differences are fp64, and only exp2 / log2 of small
+// arguments run in fp32.
 // Messages live in one fp64 LDS buffer (128 KiB at L = 16): each step reads all its
 // inputs, barrier, writes all outputs, barrier.
 // Normalisation: stored X_t = A_t - G_{t-1}; the next step subtracts g_t = max X_t
@@ -194,6 +195,31 @@ __device__ __forceinline__ double widen(float f)
     return d;
 }
 
+// The log2-domain energy term of a state at one step, shifted by the state-independent
+// kappa w s^2:
+//     -kappa w (C - s)^2 + kappa w s^2 = C (2 kappa w s - kappa w C),
+// two fp64 FMAs on the exactly widened code value (instead of the exact binary64 square
+// and one FMA with kappa: one operation fewer per state).  All states of a step get the
+// same shift, so it cancels in every LSE and in every posterior and gradient weight
+// (normalised within a step, or formed with log2 Z computed from the same shifted
+// energies); only log Z itself is corrected, by the sum of the shifts.
+struct StepEnergy {
+    double kw;   // kappa * w_t
+    double a2;   // 2 kappa w_t s_t
+    // (2 s is formed first: a loop-invariant 2 kappa would be kept in, and spilled from,
+    // a VGPR pair)
+    __device__ __forceinline__ StepEnergy(double kappa, float s, float w)
+        : kw(kappa * (double)w), a2(kappa * (double)w * (2.0 * (double)s)) {}
+    // x + shifted energy term of code value c
+    __device__ __forceinline__ double add_to(float c, double x) const
+    {
+        const double cd = widen(c);
+        return __builtin_fma(cd, __builtin_fma(-kw, cd, a2), x);
+    }
+    // the shift kappa w s^2 itself
+    __device__ __forceinline__ double shift(float s) const { return kw * (double)s * (double)s; }
+};
+
 __device__ __forceinline__ void lds_read4(const char* base, int addr, int P, double (&v)[4])
 {
     const double2 lo = *reinterpret_cast<const double2*>(base + addr);
@@ -314,13 +340,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + opaque_tid())); };
     auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * opaque_tid() + r)); };
 
-    // exact binary64 energy (C - s)^2 [* w] of binary32 inputs; sp, wp already widened
-    auto energy = [&](float c, double sp, double wp) -> double {
-        const double d = widen(c) - sp;
-        double e = d * d;
-        if constexpr (WEIGHTED) e = wp * e;
-        return e;
-    };
+    auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
 
     // ---------------- forward ----------------
 #pragma unroll
@@ -328,7 +348,8 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     if (tid < kWaves) wmax[0][tid] = 0.f;
     __syncthreads();
 
-    double G = 0.0;   // sum of g_0 .. g_{t-1}
+    double G = 0.0;    // sum of g_0 .. g_{t-1}
+    double Sh = 0.0;   // sum of the energy shifts kappa w s^2 of the steps so far
     int par = 0;
     for (int t = 1; t < T; ++t) {
         float g = wmax[par][0];
@@ -366,8 +387,8 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         __syncthreads();   // every input read before any output overwrites it
         G = uniform64(G + g64);
         if (tid == 0) gsh[t - 1] = g;
-        const double sp = (double)s[t - 1];
-        const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
+        const StepEnergy se = step_energy(t - 1);
+        Sh = uniform64(Sh + se.shift(s[t - 1]));
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -383,7 +404,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     double v[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
-                        v[a] = __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), relw[a]);
+                        v[a] = se.add_to(Cv[a][r][x], relw[a]);
                     o[xx] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
                     lmax = __builtin_fmaxf(lmax, (float)o[xx]);
                 }
@@ -406,8 +427,8 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     if (tid == 0) gsh[T - 1] = gl;
     double log2z;
     {
-        const double sp = (double)s[T - 1];
-        const double wp = WEIGHTED ? (double)w[T - 1] : 1.0;
+        const StepEnergy se = step_energy(T - 1);
+        Sh = uniform64(Sh + se.shift(s[T - 1]));
         const double gl64 = (double)gl;
         double m = -__builtin_inf();
 #pragma unroll
@@ -422,7 +443,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
-                    m = max64(m, __builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64));
+                    m = max64(m, se.add_to(Cv[a][r][x], xa[r] - gl64));
         }
         float wm = wave_max<WID>((float)m);
         if (lane == 0) redm[wave] = wm;
@@ -440,7 +461,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
-                    sum += fast_exp2((float)(__builtin_fma(-kappa, energy(Cv[a][r][x], sp, wp), xa[r] - gl64) - bm64));
+                    sum += fast_exp2((float)(se.add_to(Cv[a][r][x], xa[r] - gl64) - bm64));
         }
         sum = wave_sum<WID>(sum);
         if (lane == 0) reds[wave] = sum;
@@ -448,8 +469,9 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float tot = 0.f;
 #pragma unroll
         for (int qq = 0; qq < kWaves; ++qq) tot += reds[qq];
+        // log2 Z of the shifted energies (what the posterior offsets use), and the true one
         log2z = uniform64(G + bm64 + (double)fast_log2(tot));
-        if (tid == 0) l2z[0] = log2z;
+        if (tid == 0) l2z[0] = log2z - Sh;
     }
 
     // ---------------- backward + posterior ----------------
@@ -501,8 +523,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         const double Ot = uniform64(log2z - Gm - H);  // log2 Z - G_t - H_t
         if (VJP && tid == 0) ofs[t] = Ot;
         Gm = uniform64(Gm - (double)gsh[t]);          // G_{t-1}
-        const double sp = (double)s[t];
-        const double wp = WEIGHTED ? (double)w[t] : 1.0;
+        const StepEnergy se = step_energy(t);
         float pg = 0.f, pc = 0.f;
         float ymax = -__builtin_inff();
 #pragma unroll
@@ -522,7 +543,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         cx[x] = Ch.at(a, r, x);
-                        v[x] = __builtin_fma(-kappa, energy(cx[x], sp, wp), widen(rel[r][x]));
+                        v[x] = se.add_to(cx[x], widen(rel[r][x]));
                     }
                     // LSE over x (as lse2_4), whose exponentials q_x = 2^(v_x - m) also give
                     // the posterior of the four states (a, c, x): with the exponent

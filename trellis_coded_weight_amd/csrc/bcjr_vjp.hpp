@@ -88,13 +88,8 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     auto half = [&](int cur, int chunk, int h) -> float2& {
         return reinterpret_cast<float2*>(&buf[cur][chunk])[h];
     };
-    // the soft pass's exact binary64 energy
-    auto energy = [&](float c, double sp, double wp) -> double {
-        const double d = widen(c) - sp;
-        double e = d * d;
-        if constexpr (WEIGHTED) e = wp * e;
-        return e;
-    };
+    // the soft pass's (shifted) energy terms: its posterior offsets O_u were formed with them
+    auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
     auto phi_slot = [&](int t, int a, int h) -> size_t {
         return (((size_t)t * 4 + a) * 2 + h) * NT + tid;
     };
@@ -105,8 +100,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     __syncthreads();
     int cur = 0;
     for (int t = 1; t < T; ++t) {
-        const double sp = (double)s[t - 1];
-        const double wp = WEIGHTED ? (double)w[t - 1] : 1.0;
+        const StepEnergy se = step_energy(t - 1);
         const float gp = gu[t - 1];
         const float sft = softs[t - 1];
 #pragma unroll
@@ -133,7 +127,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         cx[a] = Cp.at(a, r, x);
-                        lw[a] = __builtin_fma(-kappa, energy(cx[a], sp, wp), from_fix(xq[a][i]));
+                        lw[a] = se.add_to(cx[a], from_fix(xq[a][i]));
                     }
                     const double m = max64(max64(lw[0], lw[1]), max64(lw[2], lw[3]));
                     float num = 0.f, den = 0.f;
@@ -168,8 +162,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     // Psi_{u-1}.  The step with u = 0 is peeled so that the loop body has no branches.
     auto bstep = [&](int u, auto produce_tag) {
         constexpr bool PRODUCE = decltype(produce_tag)::value;
-        const double sp = (double)s[u];
-        const double wp = WEIGHTED ? (double)w[u] : 1.0;
+        const StepEnergy se = step_energy(u);
         const float gp = gu[u];
         const float sft = softs[u];
         const double Ou = ofs[u];
@@ -213,7 +206,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         cx[x] = Cp.at(a, r, x);
-                        lq[x] = __builtin_fma(-kappa, energy(cx[x], sp, wp), from_fix(yq[i][x]));
+                        lq[x] = se.add_to(cx[x], from_fix(yq[i][x]));
                     }
                     // Q_x = 2^(lq_x - m) / den; the posterior of state (a, c, x) is
                     // 2^(Xn_u - O_u + lq_x) = 2^(Xn_u - O_u + m) * 2^(lq_x - m)
