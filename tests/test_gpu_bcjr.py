@@ -75,6 +75,15 @@ def test_bcjr_L16_3inst_weighted(api):
     run_and_compare(api, s, w, 0.1, 16, "3inst")
 
 
+@pytest.mark.parametrize("tau", [1.0, 0.1, 0.01])
+def test_bcjr_large_targets(api, tau):
+    # targets far outside the codebook's range (|s| up to ~15) and log-normal weights: the
+    # per-step energies and their shifts are thousands of log2 units
+    s = (4.0 + 3.0 * inputs.targets(3, 256, 46)).astype(np.float32)
+    w = inputs.weights(3, 256, 47)
+    run_and_compare(api, s, w, tau, 12, "1mad")
+
+
 def test_bcjr_chunked_workspace(api):
     import torch
     s = inputs.targets(5, 64, 43)

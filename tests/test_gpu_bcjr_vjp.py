@@ -40,7 +40,7 @@ def upstream(B, T, seed):
     return np.random.default_rng(seed).standard_normal((B, T)).astype(np.float32)
 
 
-def run_and_compare(api, s, w, g, tau, L, code):
+def run_and_compare(api, s, w, g, tau, L, code, tol=TOL):
     import torch
     B, T = s.shape
     say("bcjr_vjp L=%d T=%d B=%d tau=%g code=%s weighted=%s" % (L, T, B, tau, code, w is not None))
@@ -54,7 +54,7 @@ def run_and_compare(api, s, w, g, tau, L, code):
     grad_o, soft_o = oracle_vjp_par(C, s, tau, g.astype(np.float64), w, L=L)
     assert bcjr_err(soft.cpu().numpy(), soft_o).max() <= TOL
     err = bcjr_err(grad.cpu().numpy(), grad_o)
-    assert err.max() <= TOL, "max grad err/rms %g" % err.max()
+    assert err.max() <= tol, "max grad err/rms %g" % err.max()
     return err
 
 
@@ -84,6 +84,20 @@ def test_vjp_L16_3inst_weighted(api):
     s = inputs.targets(2, 256, 58)
     w = inputs.weights(2, 256, 59)
     run_and_compare(api, s, w, upstream(2, 256, 60), 0.1, 16, "3inst")
+
+
+# Targets far outside the codebook's range (4 + 3 N(0,1), |s| up to ~15) with log-normal
+# weights: energy gaps of thousands of log2 units concentrate the walk distribution, and
+# the covariance becomes a small difference of much larger moments, so the fixed
+# resolution of the message stash (2.4e-7 log2) weighs more.  The unit-scale bound holds
+# at tau = 1; at tau = 0.1 the bound is 5e-5 (measured worst 2.1e-5 over 12 such sequences).
+# At tau = 0.01 one of these sequences has gradient RMS ~1e-8, below what a relative bound
+# can measure.
+@pytest.mark.parametrize("tau,tol", [(1.0, TOL), (0.1, 5e-5)])
+def test_vjp_large_targets(api, tau, tol):
+    s = (4.0 + 3.0 * inputs.targets(3, 256, 61)).astype(np.float32)
+    w = inputs.weights(3, 256, 62)
+    run_and_compare(api, s, w, upstream(3, 256, 63), tau, 12, "1mad", tol=tol)
 
 
 def test_vjp_zero_and_linear(api):
