@@ -1,6 +1,6 @@
 """GPU checks at the full workload sizes, in the launch configuration the benchmark
 times (64 GiB encode workspace cap, the library's default BCJR / gradient caps): sampled
-sequences (first, last and seeded random rows: 4,096 per encode configuration, 64 per
+sequences (first, last and seeded random rows: 4,096 per encode configuration, 256 per
 BCJR temperature, 16 for the gradient) against the oracle, bit for bit for the encodes,
 and properties that hold for every sequence --
 decoding the stream reproduces the encoder's MSE bit for bit, the stream's pad bits are
@@ -72,7 +72,7 @@ def test_bcjr_full(api):
     s, _, code = inputs.workload("bcjr4096x4096_1mad")
     B, T = s.shape
     sd = dev(s)
-    rows = sample_rows(B, 64, 8)
+    rows = sample_rows(B, 256, 8)
     C = oracle.code_table(code, 16)
     for tau in (1.0, 0.1, 0.01):
         say("full-size bcjr B=%d tau=%g" % (B, tau))
