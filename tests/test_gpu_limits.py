@@ -44,6 +44,22 @@ def test_tailbiting_longest_sequences(api, L, B):
     check_tb(api, s, None, L, "1mad")
 
 
+# The search stages targets through an LDS ring of two 256-step chunks and refills a
+# slot while the other is read; lengths around the chunk boundaries exercise the refill
+# schedule (and the tail-biting rotation, which wraps inside a chunk).
+@pytest.mark.parametrize("T", [255, 257, 511, 512, 513, 767, 768, 769, 1025])
+def test_encode_ring_boundaries(api, T):
+    s = inputs.targets(3, T, 4500 + T)
+    w = inputs.weights(3, T, 4600 + T) if T % 2 else None
+    check_encode(api, s, w, 10, "1mad")
+
+
+@pytest.mark.parametrize("T", [257, 513, 768])
+def test_tailbiting_ring_boundaries(api, T):
+    s = inputs.targets(3, T, 4700 + T)
+    check_tb(api, s, None, 10, "3inst")
+
+
 def test_encode_odd_batch_L16(api):
     s = inputs.targets(7, 256, 4444)
     check_encode(api, s, None, 16, "1mad")
