@@ -76,6 +76,23 @@ def test_matvec_random_streams(api, tb, L, code, M, N, batch):
     check(api, words, M, N, L, code, tb, x, "random")
 
 
+# every batch width (the kernel is compiled for 1, 2, 4 and 8 rows; the rows beyond the
+# batch re-read its last row and are never stored)
+@pytest.mark.parametrize("batch", [4, 5, 6, 7])
+def test_matvec_every_batch_width(api, batch):
+    M, N, L = 32, 1040, 16
+    words = random_words(M, N, L, False, 900 + batch)
+    x = inputs.targets(batch, N, 910 + batch)
+    y = check(api, words, M, N, L, "1mad", False, x, "batch")
+    # each row equals the same row computed alone
+    import torch
+    for i in (0, batch - 1):
+        yi = api.decode_matvec(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x[i:i + 1]),
+                               L=L, k=2, code="1mad", tailbiting=False)
+        sync()
+        assert torch.equal(yi[0], y[i])
+
+
 @pytest.mark.parametrize("tb", [False, True])
 def test_matvec_one_hot_columns_exact(api, tb):
     import torch
