@@ -19,9 +19,18 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_current_device(x: torch.Tensor, name: str) -> None:
+    # the kernels run on the current device's current stream, and workspaces and outputs
+    # are allocated there
+    if x.device.index is not None and x.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s, not on the current device cuda:%d"
+                         % (name, x.device, torch.cuda.current_device()))
+
+
 def _dev_f32(x: torch.Tensor, name: str) -> torch.Tensor:
     if not (x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2):
         raise ValueError("%s must be a contiguous 2-D float32 device tensor" % name)
+    _on_current_device(x, name)
     return x
 
 
@@ -38,6 +47,7 @@ def _dev_words(bits: torch.Tensor, B: int, W: int) -> None:
     if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
             and bits.dtype in (torch.int32, torch.uint32) and tuple(bits.shape) == (B, W)):
         raise ValueError("bits must be a contiguous [%d][%d] 32-bit device tensor" % (B, W))
+    _on_current_device(bits, "bits")
 
 
 def _decode_inputs(bits, T, W, seq, weights, want_mse):
@@ -238,6 +248,7 @@ def decode_matvec(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: int = 
     if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
             and bits.numel() == (M // 16) * (N // 16) * W):
         raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
+    _on_current_device(bits, "bits")
     y = torch.empty((x2.shape[0], M), dtype=torch.float32, device=x.device)
     nat.qtcq_decode_matvec(bits.data_ptr(), M, N, L, k, _code(code), tailbiting, x2.data_ptr(),
                            x2.shape[0], y.data_ptr(), _stream())
