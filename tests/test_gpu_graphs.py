@@ -1,0 +1,86 @@
+"""The entry points can be captured in a HIP graph: they launch kernels on the caller's
+stream and allocate nothing, and no call records a memset.  Each captured sequence is
+replayed several times, with the inputs changed by eager work and the device synchronised
+between replays, and every replay is compared with the same calls run eagerly."""
+import numpy as np
+import pytest
+
+from trellis_coded_weight_amd import inputs
+
+from helpers import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    from trellis_coded_weight_amd import api as a
+    return a
+
+
+def capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph; returns (graph, outputs)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    torch.cuda.synchronize()
+    return g, out
+
+
+def test_graph_encode_decode_bcjr(api):
+    import torch
+    L, T, B = 12, 256, 64
+    seq = dev(inputs.targets(B, T, 81))
+    ws = api.encode_workspace(B, T, L, 2)
+    bws = api.bcjr_workspace(B, T, L, 2)
+
+    def step():
+        bits, mse, _ = api.encode(seq, L=L, workspace=ws)
+        recon, mse2 = api.decode(bits, T, L=L, seq=seq, want_mse=True)
+        soft, lz = api.bcjr_soft(seq, 0.1, L=L, workspace=bws)
+        return bits, mse, recon, mse2, soft, lz
+
+    say("graph: encode + decode + bcjr L=%d B=%d" % (L, B))
+    g, out = capture(step)
+    for rep in range(3):
+        seq.copy_(dev(inputs.targets(B, T, 90 + rep)))     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = step()
+        torch.cuda.synchronize()
+        for a, b in zip(out, ref):
+            assert torch.equal(a, b), "replay %d differs from the eager calls" % rep
+
+
+def test_graph_decode_matvec(api):
+    import torch
+    M, N, L = 256, 1024, 16
+    rng = np.random.default_rng(82)
+    words = rng.integers(0, 1 << 32, size=((M // 16) * (N // 16), 17), dtype=np.uint32)
+    bits = torch.from_numpy(words.view(np.int32)).cuda()
+    x = dev(inputs.targets(4, N, 83))
+
+    def step():
+        return [api.decode_matvec(bits, M, N, x, L=L) for _ in range(8)]
+
+    say("graph: 8 x decode_matvec M=%d N=%d batch 4" % (M, N))
+    g, out = capture(step)
+    for rep in range(3):
+        x.copy_(dev(inputs.targets(4, N, 84 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = api.decode_matvec(bits, M, N, x, L=L)
+        torch.cuda.synchronize()
+        for y in out:
+            assert torch.equal(y, ref), "replay %d differs from the eager call" % rep
