@@ -46,7 +46,6 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     using Ly = BcjrLayout<L>;
     constexpr int NT = Tr::kThreads;
     constexpr int NB = Tr::kButterflies;
-    constexpr int M = Tr::kGroups;
     constexpr int kWaves = Ly::kWaves;
     constexpr int WID = NT < 64 ? NT : 64;
     __shared__ float4 buf[2][NB];
