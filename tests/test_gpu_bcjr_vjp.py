@@ -87,12 +87,11 @@ def test_vjp_L16_3inst_weighted(api):
 
 
 # Targets far outside the codebook's range (4 + 3 N(0,1), |s| up to ~15) with log-normal
-# weights: energy gaps of thousands of log2 units.  The unit-scale bound holds at tau = 1.
-# At tau = 0.1 a few runs of large entries lose precision (up to 6.6e-6 of the entry,
-# 2.1e-5 of the RMS over 12 such sequences), so the bound here is 5e-5.
-# At tau = 0.01 one of these sequences has gradient RMS ~1e-8, below what a relative bound
-# can measure.
-@pytest.mark.parametrize("tau,tol", [(1.0, TOL), (0.1, 5e-5)])
+# weights: energy gaps of thousands of log2 units, where the candidate that wins an LSE is
+# often far below the largest input (the case that needs every input in fp64).  At
+# tau = 0.01 one of these sequences has gradient RMS ~1e-8, below what a relative bound
+# can measure, so the test stops at 0.1.
+@pytest.mark.parametrize("tau,tol", [(1.0, TOL), (0.1, TOL)])
 def test_vjp_large_targets(api, tau, tol):
     s = (4.0 + 3.0 * inputs.targets(3, 256, 61)).astype(np.float32)
     w = inputs.weights(3, 256, 62)

@@ -18,10 +18,11 @@
 // per-step increments (kappa e ~ 10 log2 units) make those roundings ~1e-6 each, which
 // over ~250 steps shifts competing walks' weights by ~1e-5.  So messages are stored and
 // combined in fp64: each state's energy term is formed in fp64 from the binary32 inputs
-// (shifted by a per-step constant that cancels, StepEnergy), each LSE's four inputs are
-// held as an fp64 reference (their maximum) plus fp32 differences (the dominant input is
-// then exact), the LSE's max and differences are fp64, and only exp2 / log2 of small
-// arguments run in fp32.
+// (shifted by a per-step constant that cancels, StepEnergy), each LSE's four inputs stay
+// in fp64 (the candidate that wins once its energy term is added can sit far below the
+// largest input, so a reduced-precision difference from that input would carry its
+// rounding into the winner), the LSE's max and differences are fp64, and only exp2 /
+// log2 of small arguments run in fp32.
 // Messages live in one fp64 LDS buffer (128 KiB at L = 16): each step reads all its
 // inputs, barrier, writes all outputs, barrier.
 // Normalisation: stored X_t = A_t - G_{t-1}; the next step subtracts g_t = max X_t
@@ -356,33 +357,23 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) g = __builtin_fmaxf(g, wmax[par][q]);
         const double g64 = (double)g;
-        // Inputs of butterfly 4 tid + r: X_{t-1}[(a, 4 tid + r)], a = 0..3.  Each LSE's
-        // inputs are held relative to their own maximum (ref, exact in fp64): the
-        // dominant predecessor is represented exactly, only the (small) differences of
-        // the others are rounded to fp32.
-        float rel[4][4];    // [a][r]
-        double ref[4];      // [r] = max_a X - g
+        // Inputs of butterfly 4 tid + r, normalised: X_{t-1}[(a, 4 tid + r)] - g, a = 0..3,
+        // held in fp64.  The candidate that wins an LSE once its energy term is added can be
+        // any of the four (at low temperature or large energies, often one far below the
+        // others), so every input keeps full precision.
+        double xn[4][4];    // [a][r]
         {
-            double xin[4][4];   // [a][r]
-#pragma unroll
-            for (int a = 0; a < 4; ++a) lds_read4(buf, rd(a), P, xin[a]);
-            double mx[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                mx[r] = max64(max64(xin[0][r], xin[1][r]), max64(xin[2][r], xin[3][r]));
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const double (&xa)[4] = xin[a];
+                lds_read4(buf, rd(a), P, xn[a]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) rel[a][r] = (float)(xa[r] - mx[r]);
+                for (int r = 0; r < 4; ++r) xn[a][r] -= g64;
                 // Xn_{t-1}[(a, 4 tid + r)] (Xn_0 = 0 is not stored)
                 if (t >= 2)
                     xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
-                                      make_int4(to_fix(xa[0] - g64), to_fix(xa[1] - g64),
-                                                to_fix(xa[2] - g64), to_fix(xa[3] - g64)));
+                                      make_int4(to_fix(xn[a][0]), to_fix(xn[a][1]),
+                                                to_fix(xn[a][2]), to_fix(xn[a][3])));
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ref[r] = mx[r] - g64;
         }
         __syncthreads();   // every input read before any output overwrites it
         G = uniform64(G + g64);
@@ -392,9 +383,6 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float lmax = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            double relw[4];   // the butterfly's four inputs, shared by its four outputs
-#pragma unroll
-            for (int a = 0; a < 4; ++a) relw[a] = widen(rel[a][r]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs x = 2h, 2h + 1
                 double o[2];
@@ -404,8 +392,8 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     double v[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
-                        v[a] = se.add_to(Cv[a][r][x], relw[a]);
-                    o[xx] = ref[r] + lse2_4(v[0], v[1], v[2], v[3]);
+                        v[a] = se.add_to(Cv[a][r][x], xn[a][r]);
+                    o[xx] = lse2_4(v[0], v[1], v[2], v[3]);
                     lmax = __builtin_fmaxf(lmax, (float)o[xx]);
                 }
                 *reinterpret_cast<double2*>(buf + wr(r) + h * P) = make_double2(o[0], o[1]);
@@ -502,21 +490,16 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[par][q]);
         const double h64 = (double)h;
-        // inputs Y_t[(4 tid + r, x)], x = 0..3, relative to their maximum (as forward)
-        float rel[4][4];    // [r][x]
-        double ref[4];      // [r] = max_x Y - h
+        // inputs Y_t[(4 tid + r, x)] - h, x = 0..3, in fp64 (as forward)
+        double yn[4][4];    // [r][x]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            double yv[4];
-            lds_read4(buf, wr(r), P, yv);
-            const double mx = max64(max64(yv[0], yv[1]), max64(yv[2], yv[3]));
+            lds_read4(buf, wr(r), P, yn[r]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) rel[r][x] = (float)(yv[x] - mx);
-            ref[r] = mx - h64;
+            for (int x = 0; x < 4; ++x) yn[r][x] -= h64;
             if constexpr (VJP)   // Yn_t[(4 tid + r, x)]
                 ystash[((size_t)t * 4 + r) * NT + tid] =
-                    make_int4(to_fix(yv[0] - h64), to_fix(yv[1] - h64), to_fix(yv[2] - h64),
-                              to_fix(yv[3] - h64));
+                    make_int4(to_fix(yn[r][0]), to_fix(yn[r][1]), to_fix(yn[r][2]), to_fix(yn[r][3]));
         }
         if (produce) __syncthreads();   // every input read before any output overwrites it
         H = uniform64(H + h64);                       // H_t
@@ -543,7 +526,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         cx[x] = Ch.at(a, r, x);
-                        v[x] = se.add_to(cx[x], widen(rel[r][x]));
+                        v[x] = se.add_to(cx[x], yn[r][x]);
                     }
                     // LSE over x (as lse2_4), whose exponentials q_x = 2^(v_x - m) also give
                     // the posterior of the four states (a, c, x): with the exponent
@@ -556,12 +539,12 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     float qc = q[0] * cx[0];
 #pragma unroll
                     for (int x = 1; x < 4; ++x) qc = __builtin_fmaf(q[x], cx[x], qc);
-                    const double xo = (from_fix(xsr[r]) - Ot) + ref[r];
+                    const double xo = from_fix(xsr[r]) - Ot;
                     const float pb = fast_exp2((float)(xo + m));
                     pg = __builtin_fmaf(pb, sq, pg);
                     pc = __builtin_fmaf(pb, qc, pc);
                     if (produce) {
-                        y[rr] = ref[r] + (m + (double)fast_log2(sq));
+                        y[rr] = m + (double)fast_log2(sq);
                         ymax = __builtin_fmaxf(ymax, (float)y[rr]);
                     }
                 }
