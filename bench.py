@@ -15,7 +15,8 @@ Extra objects on the line:
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
   bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
-  decode_matvec -- y = W x straight from the streams (per launch, batch 1 and 8)
+  decode_matvec -- y = W x straight from the streams (per launch, batch 1 and 8; fp32
+                   VALU products and matrix-core products)
   configs       -- the other encode configurations (16 sequences; 4096x14336 3INST;
                    weighted 4096x4096) and the BCJR pass at tau = 1, 0.1, 0.01
 """
@@ -218,25 +219,34 @@ def main() -> int:
         big_bits = torch.from_numpy(g.integers(0, 1 << 32, size=(1792 * 512, tbw), dtype=np.uint32)
                                     .view(np.int32)).to(dev)
         cases.append(("28672x8192 1MAD tail-biting", big_bits, 28672, 8192, "1mad", True))
+        # Each shape is timed through both entry points: the fp32 VALU product
+        # (qtcq_decode_matvec) and the matrix-core product (qtcq_decode_matvec_mfma, its
+        # split of x included, workspace preallocated).
         reps = 200
         for label, bb, M_, N_, cd, tbf in cases:
+            mws = api.matvec_mfma_workspace(N_)
             for nb in (1, 8):
                 xv = torch.from_numpy(g.standard_normal((nb, N_), dtype=np.float32)).to(dev)
                 yv = api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)   # checks shapes
+                api.decode_matvec_mfma(bb, M_, N_, xv, code=cd, tailbiting=tbf, workspace=mws)
                 codei = nat.QTCQ_CODE_1MAD if cd == "1mad" else nat.QTCQ_CODE_3INST
-                args_ = (bb.data_ptr(), M_, N_, L, K, codei, tbf, xv.data_ptr(), nb, yv.data_ptr(), sptr)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    nat.qtcq_decode_matvec(*args_)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                sec = e0.elapsed_time(e1) / 1000.0 / reps
-                nbytes = bb.numel() * 4 + nb * (N_ + M_) * 4
-                mv["%s, batch %d" % (label, nb)] = {
-                    "us": sec * 1e6, "weights_per_s": M_ * N_ / sec,
-                    "hbm_gbs": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / PEAK_HBM_GBS}
+                args_ = (bb.data_ptr(), M_, N_, L, K, codei, tbf, xv.data_ptr(), nb, yv.data_ptr())
+                for kind, call in (("", lambda: nat.qtcq_decode_matvec(*args_, sptr)),
+                                   (", mfma", lambda: nat.qtcq_decode_matvec_mfma(
+                                       *args_, mws.data_ptr(), mws.numel(), sptr))):
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        call()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    sec = e0.elapsed_time(e1) / 1000.0 / reps
+                    nbytes = bb.numel() * 4 + nb * (N_ + M_) * 4
+                    mv["%s, batch %d%s" % (label, nb, kind)] = {
+                        "us": sec * 1e6, "weights_per_s": M_ * N_ / sec,
+                        "hbm_gbs": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / PEAK_HBM_GBS}
+            del mws
         out["decode_matvec"] = mv
         print("[bench] decode matvec " + ", ".join("%.1f us" % v["us"] for v in mv.values()),
               file=sys.stderr, flush=True)

@@ -258,6 +258,27 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
 qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, int code,
                                int tailbiting, const float* x, int batch, float* y, void* stream);
 
+/* The same product with the multiplications on the matrix cores [same passage].  The
+ * code values before their rescale are exact in fp16; each batch row of x is scaled by
+ * a power of two 2^s_i (its largest magnitude into [2^14, 2^15)) and split into two fp16
+ * parts, hi = rn16(x 2^s_i) and lo = rn16(x 2^s_i - hi); fp16 MFMAs take W times both
+ * parts, their results are added in a fixed order, scaled back by 2^-s_i and rescaled
+ * once (bit-deterministic; a one-hot x returns a column of W exactly).  With
+ * K = ceil(ceil(N/32)/16) and allowing each addition inside the matrix instruction one
+ * unit in the last place, the error is
+ *   <= (84.5 + K) * 2^-24 * sum_n |W[m][n] x[i][n]| + 2^-39 * max_n |x[i][n]| * sum_n |W[m][n]|
+ * to first order.  A row of x holding inf or NaN gives non-finite outputs in that row.
+ * Arguments as qtcq_decode_matvec, plus
+ *   workspace  device scratch, 16-byte aligned, >= qtcq_decode_matvec_mfma_workspace_bytes(N)
+ *              (the split x of this call; contents on entry are ignored)
+ * Two kernels are enqueued on `stream` (the split, then the product).
+ * Errors: as qtcq_decode_matvec, QTCQ_ERR_UNSUPPORTED also for N > 2^24, and
+ * QTCQ_ERR_WORKSPACE (workspace NULL, misaligned or too small). */
+size_t qtcq_decode_matvec_mfma_workspace_bytes(int N);   /* 0 if N < 0, N % 16 != 0 or N > 2^24 */
+qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, int k, int code,
+                                    int tailbiting, const float* x, int batch, float* y,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

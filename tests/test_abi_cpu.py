@@ -169,6 +169,44 @@ def test_decode_matvec_validation(nat):
     assert call(batch=0, bits=None, x=None, y=None) == nat.QTCQ_OK
 
 
+def test_decode_matvec_mfma_validation(nat):
+    st = lambda *a: nat.raw_status("qtcq_decode_matvec_mfma", *a)
+    # bits, M, N, L, k, code, tb, x, batch, y, workspace, workspace_bytes, stream
+    need = nat.qtcq_decode_matvec_mfma_workspace_bytes(64)
+    ok = [FAKE, 32, 64, 16, 2, 0, 0, FAKE, 1, FAKE, FAKE, need, None]
+    names = ["bits", "M", "N", "L", "k", "code", "tb", "x", "batch", "y", "ws", "wsb", "stream"]
+
+    def call(**kw):
+        a = list(ok)
+        for kk, v in kw.items():
+            a[names.index(kk)] = v
+        return st(*a)
+
+    # the split x: 1 KiB per 32 columns (a half block rounds up), then the row exponents
+    assert need == 2 * 1024 + 256
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(48) == 2 * 1024 + 256
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(0) == 256
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(24) == 0
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(-16) == 0
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes((1 << 24) + 16) == 0
+    assert call(M=24) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(N=-16) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(batch=-1) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(batch=9) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(N=(1 << 24) + 16) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(code=4) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(x=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(x=FAKE + 4) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(y=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(bits=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(ws=None) == nat.QTCQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == nat.QTCQ_ERR_WORKSPACE
+    assert call(wsb=need - 1) == nat.QTCQ_ERR_WORKSPACE
+    assert call(M=0, bits=None, x=None, y=None, ws=None) == nat.QTCQ_OK
+    assert call(batch=0, bits=None, x=None, y=None, ws=None) == nat.QTCQ_OK
+
+
 def test_tailbiting_sizes(nat):
     assert nat.qtcq_tailbiting_words(16, 2, 256) == 16     # exactly 2T bits, word-aligned
     assert nat.qtcq_tailbiting_words(16, 2, 8) == 1

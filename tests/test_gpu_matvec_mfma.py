@@ -1,0 +1,225 @@
+"""GPU parity of the decode -> matrix-vector product on the matrix cores
+(qtcq_decode_matvec_mfma) against the oracle (binary64 matmul over the oracle's window
+decode, row-major 16x16 tiles).
+
+Bar, per output (u = 2^-24, K = ceil(ceil(N/32)/16) k-blocks per wave):
+    |y_gpu - y_oracle| <= (86 + K) u sum_n |W x| + 2^-38 max_n |x| sum_n |W|,
+the kernel's stated bound -- x split into two scaled fp16 parts (4u), each addition in a
+32-product matrix instruction allowed 2u (62u), K accumulator additions, hi + lo, 15 wave
+additions, the code's rescale (2.5u) -- plus one unit for the comparison, and twice the
+split's absolute term.  A one-hot x must return the decoded column bit for bit.  Streams
+are random words (every bit pattern is a valid stream) and the encoder's own streams of
+the 4096x4096 matrix.  Inner dimensions with N/16 odd cover the half k-block.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from trellis_coded_weight_amd import inputs
+
+from helpers import dev, say, u32
+from test_gpu_matvec import matrix, random_words
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    from trellis_coded_weight_amd import api as a
+    return a
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def bound(x, Wm, N):
+    K = -(-(-(-N // 32)) // 16)
+    x64 = x.astype(np.float64)
+    mag = np.abs(x64) @ np.abs(Wm).T
+    amax = np.abs(x64).max(axis=1, initial=0.0)[:, None]
+    return (86 + K) * U32 * mag + 2.0 ** -38 * amax * np.abs(Wm).sum(axis=1)[None, :]
+
+
+def check(api, words, M, N, L, code, tb, x, tag):
+    import torch
+    say("matvec_mfma %s M=%d N=%d L=%d code=%s tb=%s batch=%d" % (tag, M, N, L, code, tb, x.shape[0]))
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    y = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, k=2, code=code, tailbiting=tb)
+    sync()
+    C = oracle.code_table(code, L)
+    y_o = oracle.decode_matvec(words, M, N, C, x, L, 2, tailbiting=tb)
+    Wm = matrix(words, M, N, C, L, tb)
+    b = bound(x, Wm, N)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - y_o)
+    assert np.all(err <= b), "worst err/bound %g" % (err / np.maximum(b, 1e-300)).max()
+    return y
+
+
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("L,code", [(16, "1mad"), (16, "3inst"), (12, "1mad"), (6, "3inst")])
+@pytest.mark.parametrize("M,N,batch", [(16, 16, 1), (32, 48, 3), (48, 1040, 8), (64, 2064, 2),
+                                       (16, 1024, 8)])
+def test_matvec_mfma_random_streams(api, tb, L, code, M, N, batch):
+    words = random_words(M, N, L, tb, M + N + L)
+    x = inputs.targets(batch, N, 7 + N)
+    check(api, words, M, N, L, code, tb, x, "random")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_matvec_mfma_every_batch_width(api, batch):
+    """Every batch width; each row equals the same row computed alone, bit for bit (the
+    row's scale and matrix-core column do not depend on the other rows)."""
+    import torch
+    M, N, L = 32, 1040, 16
+    words = random_words(M, N, L, False, 900 + batch)
+    x = inputs.targets(batch, N, 910 + batch)
+    y = check(api, words, M, N, L, "1mad", False, x, "batch")
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    for i in sorted({0, batch - 1}):
+        yi = api.decode_matvec_mfma(bd, M, N, dev(x[i:i + 1]), L=L)
+        sync()
+        assert torch.equal(yi[0], y[i])
+
+
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("code", ["1mad", "3inst"])
+def test_matvec_mfma_one_hot_columns_exact(api, tb, code):
+    import torch
+    L, M, N = 16, 48, 1056
+    words = random_words(M, N, L, tb, 99)
+    C = oracle.code_table(code, L)
+    Wm = matrix(words, M, N, C, L, tb).astype(np.float32)
+    cols = np.array([0, 15, 16, 31, 32, 511, 1024, N - 1])
+    x = np.zeros((len(cols), N), dtype=np.float32)
+    x[np.arange(len(cols)), cols] = 1.0
+    x[3] *= -0.375                     # scaled by 2^16 to an exact fp16 -24576
+    say("matvec_mfma one-hot tb=%s code=%s" % (tb, code))
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    y = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, code=code, tailbiting=tb).cpu().numpy()
+    want = Wm[:, cols].T.astype(np.float64) * x[np.arange(len(cols)), cols][:, None]
+    # rows with x = 1 are W's columns bit for bit; the -3/8 row's sum is exact, and its
+    # rescale rounds raw * (-3/8) / D once where W * (-3/8) rounded raw / D
+    ones = [i for i in range(len(cols)) if i != 3]
+    assert np.array_equal(y[ones].view(np.uint32), want[ones].astype(np.float32).view(np.uint32))
+    assert np.all(np.abs(y[3] - want[3]) <= 3 * U32 * np.abs(want[3]))
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 100, 2.0 ** -100, 1e-30, 3e30])
+def test_matvec_mfma_scaled_rows(api, scale):
+    """The per-row power-of-two scale keeps fp16 in range whatever the magnitude of x."""
+    M, N = 32, 2064
+    words = random_words(M, N, 16, False, 31)
+    x = (inputs.targets(3, N, 32).astype(np.float64) * scale).astype(np.float32)
+    check(api, words, M, N, 16, "1mad", False, x, "scale %g" % scale)
+
+
+def test_matvec_mfma_mixed_magnitudes(api):
+    """Elements spanning many binades within a row (the small ones lose nothing but the
+    split's absolute term against the row maximum), a zero row and a one-element row."""
+    M, N = 48, 1040
+    words = random_words(M, N, 16, True, 41)
+    rng = np.random.default_rng(42)
+    x = inputs.targets(4, N, 43)
+    x[0] *= (10.0 ** rng.uniform(-12, 6, size=N)).astype(np.float32)
+    x[1] = 0.0
+    x[2] = 0.0
+    x[2, 517] = 3.0e-7
+    x[3] *= (2.0 ** rng.integers(-60, 60, size=N)).astype(np.float32)
+    y = check(api, words, M, N, 16, "1mad", True, x, "mixed")
+    assert not np.any(y.cpu().numpy()[1])
+
+
+def test_matvec_mfma_nonfinite_row(api):
+    """inf / NaN in a row of x give non-finite outputs in that row only."""
+    import torch
+    M, N = 32, 1024
+    words = random_words(M, N, 16, False, 51)
+    x = inputs.targets(3, N, 52)
+    x[0, 5] = np.inf
+    x[2, 700] = np.nan
+    say("matvec_mfma non-finite rows")
+    y = api.decode_matvec_mfma(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x))
+    sync()
+    yh = y.cpu().numpy()
+    assert not np.isfinite(yh[0]).any() and not np.isfinite(yh[2]).any()
+    C = oracle.code_table("1mad", 16)
+    y_o = oracle.decode_matvec(words, M, N, C, x[1:2], 16, 2)
+    Wm = matrix(words, M, N, C, 16, False)
+    assert np.all(np.abs(yh[1:2] - y_o) <= bound(x[1:2], Wm, N))
+
+
+def test_matvec_mfma_empty_and_degenerate(api):
+    import torch
+    say("matvec_mfma N=0, M=0, batch=0")
+    x = torch.empty((2, 0), dtype=torch.float32, device="cuda")
+    bd = torch.empty((0, 17), dtype=torch.int32, device="cuda")
+    y = api.decode_matvec_mfma(bd, 32, 0, x)
+    sync()
+    assert torch.count_nonzero(y).item() == 0 and tuple(y.shape) == (2, 32)
+    y0 = api.decode_matvec_mfma(torch.empty((0, 17), dtype=torch.int32, device="cuda"), 0, 64,
+                                torch.ones((3, 64), device="cuda"))
+    xb = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    yb = api.decode_matvec_mfma(torch.zeros((4 * 4, 17), dtype=torch.int32, device="cuda"), 64, 64, xb)
+    sync()
+    assert tuple(y0.shape) == (3, 0) and tuple(yb.shape) == (0, 64)
+
+
+def test_matvec_mfma_deterministic_and_workspace_reuse(api):
+    """Two calls give the same bits; a workspace reused after a wider call (stale split
+    values of other rows and columns in it) changes nothing."""
+    import torch
+    M, N = 64, 4096
+    words = random_words(M, N, 16, False, 5)
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    ws = api.matvec_mfma_workspace(N)
+    x8 = dev(inputs.targets(8, N, 6))
+    x2 = dev(inputs.targets(2, N, 7))
+    say("matvec_mfma determinism")
+    a = api.decode_matvec_mfma(bd, M, N, x2, workspace=ws)
+    api.decode_matvec_mfma(bd, M, N, x8, workspace=ws)
+    b = api.decode_matvec_mfma(bd, M, N, x2, workspace=ws)
+    c = api.decode_matvec_mfma(bd, M, N, x2)
+    sync()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_matvec_mfma_wide_inner_dimension(api):
+    M, N, L = 32, 65536, 16
+    words = random_words(M, N, L, False, 4748)
+    x = inputs.targets(8, N, 4749)
+    check(api, words, M, N, L, "1mad", False, x, "wide")
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_matvec_mfma_encoded_4096x4096(api, tb):
+    """The encoder's streams of the 4096x4096 matrix, batch 8, every output against the
+    oracle, and against the fp32 VALU product within the sum of both bounds."""
+    import torch
+    s, _, code = inputs.workload("enc4096x4096_1mad")
+    M = N = 4096
+    say("matvec_mfma encoded 4096x4096 tb=%s" % tb)
+    sd = dev(s)
+    if tb:
+        bits, _, _ = api.tailbiting_encode(sd, L=16, k=2, code=code,
+                                           workspace=api.tailbiting_workspace(65536, max_bytes=64 << 30))
+    else:
+        bits, _, _ = api.encode(sd, L=16, k=2, code=code,
+                                workspace=api.encode_workspace(65536, max_bytes=64 << 30))
+    sync()
+    x = inputs.targets(8, N, 12)
+    y = check(api, u32(bits), M, N, 16, code, tb, x, "encoded")
+    yv = api.decode_matvec(bits, M, N, dev(x), L=16, k=2, code=code, tailbiting=tb)
+    sync()
+    C = oracle.code_table(code, 16)
+    Wm = matrix(u32(bits), M, N, C, 16, tb)
+    mag = np.abs(x.astype(np.float64)) @ np.abs(Wm).T
+    both = bound(x, Wm, N) + (4 * -(-N // 1024) + 23) * U32 * mag
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yv.cpu().numpy()) <= both)
+    del bits
+    torch.cuda.empty_cache()

@@ -57,6 +57,9 @@ _SIGS = {
     "qtcq_bcjr_vjp": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
     "qtcq_decode_matvec": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
+    "qtcq_decode_matvec_mfma_workspace_bytes": (_sz, [_int]),
+    "qtcq_decode_matvec_mfma": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp,
+                                       _vp, _sz, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
     "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
@@ -172,3 +175,16 @@ def qtcq_decode_matvec(bits: int, M: int, N: int, L: int, k: int, code: int, tai
                        x: int, batch: int, y: int, stream: int = 0) -> None:
     _check(_lib.qtcq_decode_matvec(_ptr(bits), M, N, L, k, code, 1 if tailbiting else 0, _ptr(x),
                                    batch, _ptr(y), _ptr(stream)), "qtcq_decode_matvec")
+
+
+def qtcq_decode_matvec_mfma_workspace_bytes(N: int) -> int:
+    return _lib.qtcq_decode_matvec_mfma_workspace_bytes(N)
+
+
+def qtcq_decode_matvec_mfma(bits: int, M: int, N: int, L: int, k: int, code: int,
+                            tailbiting: bool, x: int, batch: int, y: int, workspace: int,
+                            workspace_bytes: int, stream: int = 0) -> None:
+    _check(_lib.qtcq_decode_matvec_mfma(_ptr(bits), M, N, L, k, code, 1 if tailbiting else 0,
+                                        _ptr(x), batch, _ptr(y), _ptr(workspace),
+                                        workspace_bytes, _ptr(stream)),
+           "qtcq_decode_matvec_mfma")

@@ -253,3 +253,41 @@ def decode_matvec(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: int = 
     nat.qtcq_decode_matvec(bits.data_ptr(), M, N, L, k, _code(code), tailbiting, x2.data_ptr(),
                            x2.shape[0], y.data_ptr(), _stream())
     return y[0] if one else y
+
+
+def matvec_mfma_workspace(N: int) -> torch.Tensor:
+    """Device scratch for decode_matvec_mfma over N columns (reusable across calls on one
+    stream)."""
+    n = nat.qtcq_decode_matvec_mfma_workspace_bytes(N)
+    if n == 0:
+        raise ValueError("N must be a multiple of 16 in [0, 2^24]")
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def decode_matvec_mfma(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: int = 16,
+                       k: int = 2, code="1mad", tailbiting: bool = False,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_matvec with the products on the matrix cores: the code values (exact in fp16)
+    times x split per row into two scaled fp16 parts.  Same arguments and result layout;
+    `workspace` (matvec_mfma_workspace(N)) is allocated when not given."""
+    one = x.dim() == 1
+    x2 = x.reshape(1, -1) if one else x
+    _dev_f32(x2, "x")
+    if x2.shape[1] != N:
+        raise ValueError("x must have N columns")
+    W = tailbiting_words(L, k, 256) if tailbiting else bitstream_words(L, k, 256)
+    if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
+            and bits.numel() == (M // 16) * (N // 16) * W):
+        raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
+    _on_current_device(bits, "bits")
+    if workspace is None:
+        workspace = matvec_mfma_workspace(N)
+    elif not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    else:
+        _on_current_device(workspace, "workspace")
+    y = torch.empty((x2.shape[0], M), dtype=torch.float32, device=x.device)
+    nat.qtcq_decode_matvec_mfma(bits.data_ptr(), M, N, L, k, _code(code), tailbiting,
+                                x2.data_ptr(), x2.shape[0], y.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream())
+    return y[0] if one else y

@@ -13,6 +13,7 @@
 #include "bcjr.hpp"
 #include "bcjr_vjp.hpp"
 #include "matvec.hpp"
+#include "matvec_mfma.hpp"
 
 namespace {
 
@@ -332,6 +333,43 @@ qtcq_status matvec_dispatch_code(int code, bool tb, const uint32_t* bits, int M,
               : matvec_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, st);
 }
 
+// the same product with the decoded weights and the split x on the matrix cores
+template <int L, int CODE, bool TB>
+qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x, int batch,
+                             float* y, void* workspace, hipStream_t st)
+{
+    const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
+    const int nkb = (N / 16 + 1) / 2;
+    uint4* xs = static_cast<uint4*>(workspace);
+    int* sexp = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)nkb * MatvecMfmaShape::kBlockBytes);
+    hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)batch), dim3(MatvecMfmaShape::kSplitThreads), 0, st,
+                       x, N, nkb, xs, sexp);
+    qtcq_status rc = launch_status();
+    if (rc != QTCQ_OK) return rc;
+    hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB>), dim3((unsigned)(M / 16)),
+                       dim3(MatvecMfmaShape::kThreads), 0, st, bits, M, N, Wd,
+                       static_cast<const uint4*>(xs), static_cast<const int*>(sexp), batch, y);
+    return launch_status();
+}
+
+template <int L>
+qtcq_status matvec_mfma_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
+                                      const float* x, int batch, float* y, void* workspace,
+                                      hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return tb ? matvec_mfma_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, workspace, st)
+                  : matvec_mfma_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, workspace, st);
+    return tb ? matvec_mfma_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, workspace, st)
+              : matvec_mfma_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, workspace, st);
+}
+
+template <int L>
+struct MatvecMfmaF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return matvec_mfma_dispatch_code<L>(a...); }
+};
+
 template <int L>
 struct MatvecF {
     template <typename... A>
@@ -527,6 +565,27 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
     if (M == 0 || batch == 0) return QTCQ_OK;
     if (!y || (N > 0 && (!x || !aligned16(x) || !bits))) return QTCQ_ERR_INVALID_ARG;
     return by_L<MatvecF>(L, code, tailbiting != 0, bits, M, N, x, batch, y, as_stream(stream));
+}
+
+size_t qtcq_decode_matvec_mfma_workspace_bytes(int N)
+{
+    if (N < 0 || (N % 16) != 0 || N > MatvecMfmaShape::kMaxN) return 0;
+    return MatvecMfmaShape::workspace_bytes(N);
+}
+
+qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, int k, int code,
+                                    int tailbiting, const float* x, int batch, float* y,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M < 0 || N < 0 || (M % 16) != 0 || (N % 16) != 0 || batch < 0) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (batch > MatvecMfmaShape::kMaxBatch || N > MatvecMfmaShape::kMaxN) return QTCQ_ERR_UNSUPPORTED;
+    if (M == 0 || batch == 0) return QTCQ_OK;
+    if (!y || (N > 0 && (!x || !aligned16(x) || !bits))) return QTCQ_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < MatvecMfmaShape::workspace_bytes(N))
+        return QTCQ_ERR_WORKSPACE;
+    return by_L<MatvecMfmaF>(L, code, tailbiting != 0, bits, M, N, x, batch, y, workspace,
+                             as_stream(stream));
 }
 
 }  // extern "C"
