@@ -259,18 +259,20 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
                                int tailbiting, const float* x, int batch, float* y, void* stream);
 
 /* The same product with the multiplications on the matrix cores [same passage].  The
- * code values before their rescale are exact in fp16; each batch row of x is scaled by
- * a power of two 2^s_i (its largest magnitude into [2^14, 2^15)) and split into two fp16
- * parts, hi = rn16(x 2^s_i) and lo = rn16(x 2^s_i - hi); fp16 MFMAs take W times both
- * parts, their results are added in a fixed order, scaled back by 2^-s_i and rescaled
- * once (bit-deterministic; a one-hot x returns a column of W exactly).  With
- * K = ceil(ceil(N/32)/16) and allowing each addition inside the matrix instruction one
- * unit in the last place, the error is
+ * code values before their rescale are exact in fp16; each batch row of x is cut into
+ * blocks of 32 columns, each scaled by a power of two 2^s (its largest magnitude into
+ * [2^14, 2^15)) and split into two fp16 parts, hi = rn16(x 2^s) and
+ * lo = rn16(x 2^s - hi); fp16 MFMAs take W times both parts, and their results, scaled
+ * back by 2^-s, are added in a fixed order and rescaled once (bit-deterministic; a
+ * one-hot x returns a column of W exactly).  With K = ceil(ceil(N/32)/16) and allowing
+ * each addition inside the matrix instruction one unit in the last place, the error is
  *   <= (84.5 + K) * 2^-24 * sum_n |W[m][n] x[i][n]| + 2^-39 * max_n |x[i][n]| * sum_n |W[m][n]|
- * to first order.  A row of x holding inf or NaN gives non-finite outputs in that row.
+ * to first order, without underflow (blocks of x whose largest magnitude is below
+ * 2^-111 keep less precision).  A row of x holding inf or NaN gives non-finite outputs
+ * in that row.
  * Arguments as qtcq_decode_matvec, plus
  *   workspace  device scratch, 16-byte aligned, >= qtcq_decode_matvec_mfma_workspace_bytes(N)
- *              (the split x of this call; contents on entry are ignored)
+ *              (the split x and its block scales; contents on entry are ignored)
  * Two kernels are enqueued on `stream` (the split, then the product).
  * Errors: as qtcq_decode_matvec, QTCQ_ERR_UNSUPPORTED also for N > 2^24, and
  * QTCQ_ERR_WORKSPACE (workspace NULL, misaligned or too small). */

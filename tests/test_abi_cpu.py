@@ -182,9 +182,13 @@ def test_decode_matvec_mfma_validation(nat):
             a[names.index(kk)] = v
         return st(*a)
 
-    # the split x: 1 KiB per 32 columns (a half block rounds up), then the row exponents
-    assert need == 2 * 1024 + 256
-    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(48) == 2 * 1024 + 256
+    # per 32 columns (a half block rounds up): 1 KiB of split x and 8 block scales,
+    # rounded up to 256 bytes, plus 256
+    def size(nkb):
+        return -(-nkb * (1024 + 32) // 256) * 256 + 256
+    assert need == size(2)
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(48) == size(2)
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(8192) == size(256)
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(0) == 256
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(24) == 0
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(-16) == 0

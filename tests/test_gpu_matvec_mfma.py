@@ -4,10 +4,10 @@ decode, row-major 16x16 tiles).
 
 Bar, per output (u = 2^-24, K = ceil(ceil(N/32)/16) k-blocks per wave):
     |y_gpu - y_oracle| <= (86 + K) u sum_n |W x| + 2^-38 max_n |x| sum_n |W|,
-the kernel's stated bound -- x split into two scaled fp16 parts (4u), each addition in a
-32-product matrix instruction allowed 2u (62u), K accumulator additions, hi + lo, 15 wave
-additions, the code's rescale (2.5u) -- plus one unit for the comparison, and twice the
-split's absolute term.  A one-hot x must return the decoded column bit for bit.  Streams
+the kernel's stated bound -- x split per 32-column block into two scaled fp16 parts (4u),
+each addition in a 32-product matrix instruction allowed 2u (62u), K accumulator
+additions, hi + lo, 15 wave additions, the code's rescale (2.5u) -- plus one unit for the
+comparison, and twice the split's absolute term.  A one-hot x must return the decoded column bit for bit.  Streams
 are random words (every bit pattern is a valid stream) and the encoder's own streams of
 the 4096x4096 matrix.  Inner dimensions with N/16 odd cover the half k-block.
 """
@@ -74,7 +74,7 @@ def test_matvec_mfma_random_streams(api, tb, L, code, M, N, batch):
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_matvec_mfma_every_batch_width(api, batch):
     """Every batch width; each row equals the same row computed alone, bit for bit (the
-    row's scale and matrix-core column do not depend on the other rows)."""
+    row's block scales and matrix-core columns do not depend on the other rows)."""
     import torch
     M, N, L = 32, 1040, 16
     words = random_words(M, N, L, False, 900 + batch)
@@ -98,7 +98,7 @@ def test_matvec_mfma_one_hot_columns_exact(api, tb, code):
     cols = np.array([0, 15, 16, 31, 32, 511, 1024, N - 1])
     x = np.zeros((len(cols), N), dtype=np.float32)
     x[np.arange(len(cols)), cols] = 1.0
-    x[3] *= -0.375                     # scaled by 2^16 to an exact fp16 -24576
+    x[3] *= -0.375                     # its block scaled by 2^16 to an exact fp16 -24576
     say("matvec_mfma one-hot tb=%s code=%s" % (tb, code))
     bd = torch.from_numpy(words.view(np.int32)).cuda()
     y = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, code=code, tailbiting=tb).cpu().numpy()
@@ -112,7 +112,7 @@ def test_matvec_mfma_one_hot_columns_exact(api, tb, code):
 
 @pytest.mark.parametrize("scale", [2.0 ** 100, 2.0 ** -100, 1e-30, 3e30])
 def test_matvec_mfma_scaled_rows(api, scale):
-    """The per-row power-of-two scale keeps fp16 in range whatever the magnitude of x."""
+    """The per-block power-of-two scale keeps fp16 in range whatever the magnitude of x."""
     M, N = 32, 2064
     words = random_words(M, N, 16, False, 31)
     x = (inputs.targets(3, N, 32).astype(np.float64) * scale).astype(np.float32)
@@ -121,7 +121,8 @@ def test_matvec_mfma_scaled_rows(api, scale):
 
 def test_matvec_mfma_mixed_magnitudes(api):
     """Elements spanning many binades within a row (the small ones lose nothing but the
-    split's absolute term against the row maximum), a zero row and a one-element row."""
+    split's absolute term against their block's maximum), a zero row and a one-element
+    row."""
     M, N = 48, 1040
     words = random_words(M, N, 16, True, 41)
     rng = np.random.default_rng(42)

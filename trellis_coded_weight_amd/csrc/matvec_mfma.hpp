@@ -9,13 +9,14 @@
 //
 // Operands.  The code before its rescale is exact in fp16 (1MAD: the integer S - 510,
 // |S - 510| <= 510; 3INST: the fp16 sum itself), so W needs one fp16 operand.  x does
-// not fit fp16, so each batch row i is scaled by a power of two 2^s_i (chosen from
-// max_n |x[i][n]| so the largest element lands in [2^14, 2^15)) and split into two fp16
-// parts, x' = x 2^s_i = xh + xl + d with xh = rn16(x'), xl = rn16(x' - xh) (the
-// difference is exact in fp32) and |d| <= 2^-22 |x'| + 2^-25.  The 16 columns of the
-// MFMA's B operand hold xh of batch rows 0..7 (columns 0..7) and xl (columns 8..15), so
-// one MFMA multiplies 16 rows x 32 columns of W by both parts of all eight rows.  A
-// small first kernel writes the split, in the B operand's lane order, to the workspace.
+// not fit fp16, so each batch row i is cut into k-blocks of 32 columns, each scaled by
+// a power of two 2^s (chosen from the block's largest magnitude, which lands in
+// [2^14, 2^15)) and split into two fp16 parts, x' = x 2^s = xh + xl + d with
+// xh = rn16(x'), xl = rn16(x' - xh) (the difference is exact in fp32) and
+// |d| <= 2^-22 |x'| + 2^-25.  The 16 columns of the MFMA's B operand hold xh of batch
+// rows 0..7 (columns 0..7) and xl (columns 8..15), so one MFMA multiplies 16 rows x 32
+// columns of W by both parts of all eight rows.  A small first kernel writes the split,
+// in the B operand's lane order, and the factors 2^-s to the workspace.
 //
 // Layout of v_mfma_f32_16x16x32_f16 (checked on the device): lane l holds
 //   A[l % 16][8 (l / 16) + e], B[8 (l / 16) + e][l % 16] for e = 0..7, and
@@ -27,16 +28,18 @@
 // one bit-field extract per weight.
 //
 // Mapping.  One workgroup of 16 waves per band of 16 output rows (tile row I); wave w
-// takes k-blocks w, w + 16, ...  Each MFMA starts from zero and its 4 outputs per lane
-// are added to the lane's accumulators in k-block order; then hi + lo (lanes l and
-// l ^ 8), the 16 waves in sequence, the power of two 2^-s_i (exact) and the code's
-// rescale.  Results are bit-deterministic and a one-hot x (scale 2^14, xl = 0) returns
-// a column of W bit for bit.
+// takes k-blocks w, w + 16, ...  Each MFMA starts from zero; its 4 outputs per lane,
+// times the block's 2^-s (exact), are added to the lane's accumulators in k-block order
+// by FMA; then hi + lo (lanes l and l ^ 8), the 16 waves in sequence and the code's
+// rescale.  Results are bit-deterministic and a one-hot x (its block scaled to 2^14,
+// xl = 0) returns a column of W bit for bit.
 //
 // Rounding: with K = ceil(ceil(N / 32) / 16) k-blocks per wave, u = 2^-24, and allowing
 // each addition inside an MFMA one unit in the last place (2u),
 //   |y - W x| <= (4 + 62 + K + 1 + 15 + 2.5) u sum_n |W[m][n] x[n]|
-//               + 2^-39 max_n |x[n]| sum_n |W[m][n]|          (to first order).
+//               + 2^-39 max_n |x[n]| sum_n |W[m][n]|
+// to first order (no underflow: blocks whose largest |x| is below 2^-111 are scaled by
+// at most 2^126 and keep less precision).
 #pragma once
 
 #include "codes.hpp"
@@ -51,114 +54,137 @@ struct MatvecMfmaShape {
     static constexpr int kThreads = 1024;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int kMaxBatch = 8;
-    static constexpr int kSplitThreads = 1024;
     // one k-block (32 columns of x): the B operand of one MFMA, 64 lanes x 8 halves
     static constexpr size_t kBlockBytes = 64 * 16;
-    static constexpr int kExpAlign = 256;
-    // byte offsets into the split x stay below 2^31 (twice its size)
+    // per k-block: 8 row scales 2^-s (float)
+    static constexpr size_t kScaleBytes = 8 * 4;
+    static constexpr int kSplitBlock = 256;
+    // byte offsets into the workspace stay below 2^31
     static constexpr int kMaxN = 1 << 24;
-    // workspace: [ceil(N/32)][64 lanes][8 halves] split x, then int s_i[8]
+    // uint32 words of one T = 256 stream: L + 2 * 255 bits, or 512 tail-biting
+    template <int L, bool TB>
+    static constexpr int stream_words() { return TB ? 16 : (L + 2 * 255 + 31) / 32; }
+    static int kblocks(int N) { return (N / 16 + 1) / 2; }
+    // workspace: [nkb][64 lanes][8 halves] split x, then float scale[nkb][8]
     static size_t workspace_bytes(int N)
     {
-        const size_t nkb = (size_t)((N / 16 + 1) / 2);
-        return nkb * kBlockBytes + kExpAlign;
+        const size_t nkb = (size_t)kblocks(N);
+        return ((nkb * (kBlockBytes + kScaleBytes) + 255) / 256) * 256 + 256;
     }
 };
 
-// Split of x into the B operand.  grid.x = batch, block = kSplitThreads.
-//   x [batch][N] (16-byte aligned, N a multiple of 16); xs [nkb][64] 16-byte fragments;
-//   sexp [batch] the exponent s_i.  Writes columns i (xh) and 8 + i (xl) of every
-//   k-block; k >= N (the half k-block after an odd N / 16) is written as zero.
-__global__ void __launch_bounds__(MatvecMfmaShape::kSplitThreads)
-matvec_split_x(const float* __restrict__ x, int N, int nkb, uint4* __restrict__ xs,
-               int* __restrict__ sexp)
+// Split of x into the B operand, one scale per batch row and k-block (32 columns).
+//   grid.x = ceil(nkb * 64 / kSplitBlock), block = kSplitBlock; thread t writes lane
+//   slot l = t % 64 of k-block kb = t / 64, i.e. the 8 halves B[8 g + e][j] (g = l / 16,
+//   j = l % 16): xh (j < 8) or xl (j >= 8) of batch row j & 7 at columns 32 kb + 8 g + e,
+//   so a wave writes one k-block's kilobyte contiguously.  The four slots of a (row,
+//   block) pair (g = 0..3) are lanes 16 apart in one wave and share the block's maximum
+//   by two shuffles.  x [batch][N] (16-byte aligned, N a multiple of 16); xs [nkb][64]
+//   16-byte fragments; sc [nkb][8] the factor 2^-s of each row's block.  Columns k >= N
+//   (the half k-block after an odd N / 16) are written as zero; slots of rows >= batch
+//   are not written (the product kernel never reads them).
+__global__ void __launch_bounds__(MatvecMfmaShape::kSplitBlock)
+matvec_split_x(const float* __restrict__ x, int N, int nkb, int batch, uint4* __restrict__ xs,
+               float* __restrict__ sc)
 {
-    constexpr int NT = MatvecMfmaShape::kSplitThreads;
-    __shared__ float wmax[NT / 64];
-    const int i = blockIdx.x, tid = threadIdx.x;
-    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)i * N);
-    const int ng = N >> 3;            // groups of 8 consecutive columns
+    const int t = blockIdx.x * MatvecMfmaShape::kSplitBlock + threadIdx.x;
+    const int kb = t >> 6, l = t & 63, g = l >> 4, j = l & 15, i = j & 7;
+    // whole waves share kb, and the shuffle partners (l ^ 16, l ^ 32) share i: a lane
+    // that leaves here takes its partners with it
+    if (kb >= nkb || i >= batch) return;
+    const int n0 = 32 * kb + 8 * g;
+    float v[8];
+    if (n0 < N) {
+        const float4* xr = reinterpret_cast<const float4*>(x + (size_t)i * N + n0);
+        const float4 a = xr[0], b = xr[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
     float m = 0.0f;
-    for (int q = tid; q < ng; q += NT) {
-        const float4 a = xr[2 * q], b = xr[2 * q + 1];
-        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)),
-                                               __builtin_fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))));
-        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)),
-                                               __builtin_fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
-    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
-    if ((tid & 63) == 0) wmax[tid >> 6] = m;
-    __syncthreads();
-    m = wmax[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) m = __builtin_fmaxf(m, wmax[w]);
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
     // max = f 2^e with f in [1/2, 1): x 2^(15 - e) has its largest magnitude in
-    // [2^14, 2^15).  A zero or non-finite maximum keeps s = 0 (non-finite inputs give
-    // non-finite outputs either way).
+    // [2^14, 2^15).  s <= 126 keeps the factor 2^-s a normal float (blocks below 2^-111
+    // lose precision, as fp32 products there underflow anyway).  A zero or non-finite
+    // maximum keeps s = 0 (non-finite inputs give non-finite outputs either way).
     int s = 0;
-    if (m > 0.0f && m <= 3.402823466e38f) s = 15 - __builtin_amdgcn_frexp_expf(m);
-    if (tid == 0) sexp[i] = s;
-
-    for (int q = tid; q < 4 * nkb; q += NT) {
-        float v[8];
-        if (q < ng) {
-            const float4 a = xr[2 * q], b = xr[2 * q + 1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-        }
-        mv_half8 h, l;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xp = __builtin_ldexpf(v[e], s);
-            const _Float16 hh = (_Float16)xp;          // round to nearest even
-            h[e] = hh;
-            l[e] = (_Float16)(xp - (float)hh);         // the difference is exact
-        }
-        const int kb = q >> 2, g = q & 3;
-        xs[(size_t)kb * 64 + 16 * g + i] = __builtin_bit_cast(uint4, h);
-        xs[(size_t)kb * 64 + 16 * g + 8 + i] = __builtin_bit_cast(uint4, l);
+    if (m > 0.0f && m <= 3.402823466e38f) {
+        s = 15 - __builtin_amdgcn_frexp_expf(m);
+        s = s < 126 ? s : 126;
     }
+    mv_half8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float xp = __builtin_ldexpf(v[e], s);
+        const _Float16 hh = (_Float16)xp;                  // round to nearest even
+        h[e] = j < 8 ? hh : (_Float16)(xp - (float)hh);    // the difference is exact
+    }
+    xs[(size_t)kb * 64 + l] = __builtin_bit_cast(uint4, h);
+    if (l < 8) sc[(size_t)kb * 8 + i] = __builtin_ldexpf(1.0f, -s);
+}
+
+// A constant copied into a VGPR (opaque to the compiler, so it stays a VGPR operand).
+__device__ __forceinline__ uint32_t vgpr_u32(uint32_t c)
+{
+    uint32_t v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(c));
+    return v;
+}
+
+// lcg_step with the 519 multiplier in a VGPR
+__device__ __forceinline__ uint32_t lcg_step_v(uint32_t x, uint32_t k519)
+{
+    uint32_t lo, hi;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(lo) : "v"(x), "s"(25297u), "v"(76625530u));
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(hi) : "v"(k519), "v"(x));
+    return lo + (hi << 16);
 }
 
 // Two windows' codes before their rescale, as one packed pair of fp16.
+//   k519: 519 in a VGPR; kbias: fp16 -1534 in both halves, in a VGPR
 template <int CODE>
-__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1)
+__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, uint32_t k519,
+                                                      uint32_t kbias)
 {
     if constexpr (CODE == kCode1Mad) {
-        // v_sad_u8 into an accumulator 0x6400 (fp16 1024): the halves read 1024 + S
-        // exactly (S <= 1020), and one packed fp16 subtraction of 1534 gives S - 510
-        const uint32_t t0 = __builtin_amdgcn_sad_u8(lcg_step(w0), 0u, 0x6400u);
-        const uint32_t t1 = __builtin_amdgcn_sad_u8(lcg_step(w1), 0u, 0x6400u);
-        const mv_half2 p = __builtin_bit_cast(mv_half2, t0 | (t1 << 16));
-        const mv_half2 bias = {(_Float16)-1534.0f, (_Float16)-1534.0f};
-        return __builtin_bit_cast(uint32_t, p + bias);
+        // byte sums into both halves of an accumulator 0x64006400 (fp16 1024 twice):
+        // v_sad_u8 adds S0 to the low half, v_sad_hi_u8 adds S1 << 16, so the halves read
+        // 1024 + S0 and 1024 + S1 exactly (S <= 1020, no carry between them); one packed
+        // fp16 subtraction of 1534 gives S - 510
+        const uint32_t t0 = __builtin_amdgcn_sad_u8(lcg_step_v(w0, k519), 0u, 0x64006400u);
+        const uint32_t t = __builtin_amdgcn_sad_hi_u8(lcg_step_v(w1, k519), 0u, t0);
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mv_half2, t) + __builtin_bit_cast(mv_half2, kbias));
     } else {
         // the two halves of each (u & 0x8FFF8FFF) ^ 0x3B603B60, gathered as (lo0, lo1)
         // and (hi0, hi1), added by one packed fp16 add (round to nearest even)
-        const uint32_t v0 = (lcg_step(w0) & 0x8FFF8FFFu) ^ 0x3B603B60u;
-        const uint32_t v1 = (lcg_step(w1) & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const uint32_t v0 = (lcg_step_v(w0, k519) & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const uint32_t v1 = (lcg_step_v(w1, k519) & 0x8FFF8FFFu) ^ 0x3B603B60u;
         const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
         const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
         return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mv_half2, hi) + __builtin_bit_cast(mv_half2, lo));
     }
 }
 
-// grid.x = M / 16, block = MatvecMfmaShape::kThreads.  bits [(M/16)(N/16)][Wd];
-// xs, sexp as written by matvec_split_x for this x; y [batch][M].
+// grid.x = M / 16, block = MatvecMfmaShape::kThreads.  bits [(M/16)(N/16)][Wd] with
+// Wd = MatvecMfmaShape::stream_words<L, TB>();
+// xs, sc as written by matvec_split_x for this x; y [batch][M].
 template <int L, int CODE, bool TB>
 __global__ void __launch_bounds__(MatvecMfmaShape::kThreads)
-decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N, int Wd,
-                   const uint4* __restrict__ xs, const int* __restrict__ sexp, int batch,
+decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
+                   const uint4* __restrict__ xs, const float* __restrict__ sc, int batch,
                    float* __restrict__ y)
 {
     constexpr int NW = MatvecMfmaShape::kWaves;
+    constexpr int Wd = MatvecMfmaShape::stream_words<L, TB>();
     __shared__ float red[NW][8][16];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int I = blockIdx.x;
     const int NTJ = N >> 4, nkb = (NTJ + 1) >> 1;
@@ -168,56 +194,89 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N, int Wd,
     const uint32_t sh = (g & 1) ? 16u : 0u;
     const int o_hi = r;
     const int o_lo = (g & 1) ? ((TB && r == 15) ? 0 : r + 1) : r;
-    // The split x is read through a buffer descriptor sized to its k-blocks; the lanes
-    // of batch rows beyond the batch read at an offset past that size, which the buffer
-    // unit returns as zero without touching memory.
+    // Both operands are read through buffer descriptors sized to the band's streams and
+    // to the split x: an offset past the end reads as zero without touching memory.  So
+    // the tile after the last one (the second half of the last k-block when N / 16 is
+    // odd) decodes as the all-zero window, whose finite codes meet the zero columns
+    // k >= N of the split x; the prefetch after a wave's last k-block reads zeros; and
+    // the lanes of batch rows beyond the batch start past the end of the split x.
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint4*>(xs), (short)0, nkb * (int)MatvecMfmaShape::kBlockBytes, 0x00020000);
-    const int boff = ((r & 7) < batch) ? lane * 16 : nkb * (int)MatvecMfmaShape::kBlockBytes;
-
-    // Loads of k-block kb: the stream words of this lane's row and the B fragment.  A
-    // tile past the last one (the second half of the last k-block after an odd N / 16)
-    // is replaced by the last tile: its products meet the zero columns k >= N of x.
-    // A k-block past the last one (prefetch after the last iteration) re-reads the last.
-    auto load = [&](int kb, uint32_t& wh, uint32_t& wl, uint4& bx) {
-        kb = kb < nkb ? kb : nkb - 1;
-        int J = 2 * kb + (g >> 1);
-        J = J < NTJ ? J : NTJ - 1;
-        const uint32_t* sw = band + (size_t)J * Wd;
-        wh = sw[o_hi];
-        wl = sw[o_lo];
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, boff + kb * (int)MatvecMfmaShape::kBlockBytes, 0, 0);
-        bx = __builtin_bit_cast(uint4, v);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(sc), (short)0, nkb * (int)MatvecMfmaShape::kScaleBytes, 0x00020000);
+    // Byte offsets of k-block kb = wave + 2 NW j (tiles 2 kb and 2 kb + 1); the second
+    // register set (kb + NW, 2 NW tiles further) adds a constant to the stream offsets
+    // and has its own B offset.
+    constexpr int dstr = 4 * NW * Wd * 4;        // stream bytes of 2 NW k-blocks
+    constexpr int dstr1 = 2 * NW * Wd * 4;       // of NW k-blocks
+    const int dx = 2 * (int)MatvecMfmaShape::kBlockBytes * NW;
+    int oh = ((2 * wave + (g >> 1)) * Wd + o_hi) * 4;
+    int ol = ((2 * wave + (g >> 1)) * Wd + o_lo) * 4;
+    const bool live = (r & 7) < batch;
+    int ob0 = live ? wave * (int)MatvecMfmaShape::kBlockBytes + lane * 16
+                   : nkb * (int)MatvecMfmaShape::kBlockBytes;
+    int ob1 = ob0 + (int)MatvecMfmaShape::kBlockBytes * NW;
+    // the scale of this lane's batch row in k-block kb (zero past the end, like B)
+    constexpr int dsc = 2 * (int)MatvecMfmaShape::kScaleBytes * NW;
+    int os0 = live ? wave * (int)MatvecMfmaShape::kScaleBytes + (r & 7) * 4
+                   : nkb * (int)MatvecMfmaShape::kScaleBytes;
+    int os1 = os0 + (int)MatvecMfmaShape::kScaleBytes * NW;
+    auto load = [&](int d, int ob, int os, uint32_t& wh, uint32_t& wl, uint4& bx, float& scl) {
+        wh = __builtin_amdgcn_raw_buffer_load_b32(wr, oh + d, 0, 0);
+        wl = __builtin_amdgcn_raw_buffer_load_b32(wr, ol + d, 0, 0);
+        bx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ob, 0, 0));
+        scl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, os, 0, 0));
     };
+    // loop-invariant operands held in VGPRs (an SGPR operand halves a VALU op's issue rate)
+    const uint32_t k519 = vgpr_u32(519u);
+    const uint32_t kbias = vgpr_u32(0xE5FEE5FEu);   // fp16 -1534 in both halves
+    // Each MFMA's result, times its block's 2^-s (exact), is added to the accumulators
+    // one k-block later, so its latency hides behind the next block's decode; the
+    // additions stay in k-block order.
     mv_float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto step = [&](uint32_t wh, uint32_t wl, const uint4& bx) {
+    mv_float4 pend = {0.0f, 0.0f, 0.0f, 0.0f};
+    float pscl = 0.0f;
+    auto step = [&](uint32_t wh, uint32_t wl, const uint4& bx, float scl) {
         const uint32_t f = __builtin_amdgcn_alignbit(wh, wl, sh);
         uint32_t a[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t w0 = (f >> (32 - L - 4 * p)) & ((1u << L) - 1u);
             const uint32_t w1 = (f >> (30 - L - 4 * p)) & ((1u << L) - 1u);
-            a[p] = code_raw_pair_f16<CODE>(w0, w1);
+            a[p] = code_raw_pair_f16<CODE>(w0, w1, k519, kbias);
         }
         const mv_half8 av = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         const mv_float4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc += __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(mv_half8, bx), zero, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(pend[v], pscl, acc[v]);
+        pend = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(mv_half8, bx), zero, 0, 0, 0);
+        pscl = scl;
     };
 
-    // two register sets, k-blocks alternating between them; every load is in range
-    // (past the last k-block it re-reads the last), so none of them is conditional
+    // two register sets, k-blocks alternating between them; no load is conditional
     if (wave < nkb) {
         uint32_t h0, l0, h1, l1;
         uint4 b0, b1;
+        float s0, s1;
         int kb = wave;
-        load(kb, h0, l0, b0);
+        load(0, ob0, os0, h0, l0, b0, s0);
         for (; kb + NW < nkb; kb += 2 * NW) {
-            load(kb + NW, h1, l1, b1);
-            step(h0, l0, b0);
-            load(kb + 2 * NW, h0, l0, b0);
-            step(h1, l1, b1);
+            load(dstr1, ob1, os1, h1, l1, b1, s1);
+            step(h0, l0, b0, s0);
+            oh += dstr;
+            ol += dstr;
+            ob0 += dx;
+            ob1 += dx;
+            os0 += dsc;
+            os1 += dsc;
+            load(0, ob0, os0, h0, l0, b0, s0);
+            step(h1, l1, b1, s1);
         }
-        if (kb < nkb) step(h0, l0, b0);
+        if (kb < nkb) step(h0, l0, b0, s0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(pend[v], pscl, acc[v]);
     }
 
     // lane l holds rows 4 g + v of column r: xh products of batch row r (r < 8) or xl
@@ -233,7 +292,7 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N, int Wd,
         float s = red[0][i][rr];
 #pragma unroll
         for (int q = 1; q < NW; ++q) s += red[q][i][rr];
-        y[(size_t)i * M + 16 * I + rr] = code_rescale<CODE>(__builtin_ldexpf(s, -sexp[i]));
+        y[(size_t)i * M + 16 * I + rr] = code_rescale<CODE>(s);
     }
 }
 

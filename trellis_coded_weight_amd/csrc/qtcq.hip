@@ -338,17 +338,21 @@ template <int L, int CODE, bool TB>
 qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x, int batch,
                              float* y, void* workspace, hipStream_t st)
 {
-    const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
-    const int nkb = (N / 16 + 1) / 2;
+    static_assert(MatvecMfmaShape::stream_words<L, TB>() == (TB ? 16 : 17), "stream words");
+    const int nkb = MatvecMfmaShape::kblocks(N);
     uint4* xs = static_cast<uint4*>(workspace);
-    int* sexp = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)nkb * MatvecMfmaShape::kBlockBytes);
-    hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)batch), dim3(MatvecMfmaShape::kSplitThreads), 0, st,
-                       x, N, nkb, xs, sexp);
-    qtcq_status rc = launch_status();
-    if (rc != QTCQ_OK) return rc;
+    float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)nkb * MatvecMfmaShape::kBlockBytes);
+    if (nkb > 0) {
+        const int threads = nkb * 64;
+        const int bs = MatvecMfmaShape::kSplitBlock;
+        hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, st,
+                           x, N, nkb, batch, xs, sc);
+        qtcq_status rc = launch_status();
+        if (rc != QTCQ_OK) return rc;
+    }
     hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB>), dim3((unsigned)(M / 16)),
-                       dim3(MatvecMfmaShape::kThreads), 0, st, bits, M, N, Wd,
-                       static_cast<const uint4*>(xs), static_cast<const int*>(sexp), batch, y);
+                       dim3(MatvecMfmaShape::kThreads), 0, st, bits, M, N,
+                       static_cast<const uint4*>(xs), static_cast<const float*>(sc), batch, y);
     return launch_status();
 }
 
