@@ -84,3 +84,31 @@ def test_graph_decode_matvec(api):
         torch.cuda.synchronize()
         for y in out:
             assert torch.equal(y, ref), "replay %d differs from the eager call" % rep
+
+
+def test_graph_decode_matvec_mfma(api):
+    """The matrix-core product (split kernel + product kernel, one shared workspace)
+    captured 8 times over, replays equal to the eager call."""
+    import torch
+    M, N, L = 256, 1040, 16
+    rng = np.random.default_rng(85)
+    words = rng.integers(0, 1 << 32, size=((M // 16) * (N // 16), 16), dtype=np.uint32)
+    bits = torch.from_numpy(words.view(np.int32)).cuda()
+    x = dev(inputs.targets(8, N, 86))
+    ws = api.matvec_mfma_workspace(N)
+
+    def step():
+        return [api.decode_matvec_mfma(bits, M, N, x, L=L, code="3inst", tailbiting=True,
+                                       workspace=ws) for _ in range(8)]
+
+    say("graph: 8 x decode_matvec_mfma M=%d N=%d batch 8" % (M, N))
+    g, out = capture(step)
+    for rep in range(3):
+        x.copy_(dev(inputs.targets(8, N, 87 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = api.decode_matvec_mfma(bits, M, N, x, L=L, code="3inst", tailbiting=True)
+        torch.cuda.synchronize()
+        for y in out:
+            assert torch.equal(y, ref), "replay %d differs from the eager call" % rep

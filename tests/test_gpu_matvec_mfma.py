@@ -224,3 +224,29 @@ def test_matvec_mfma_encoded_4096x4096(api, tb):
     assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yv.cpu().numpy()) <= both)
     del bits
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("code,M,N", [("1mad", 28672, 8192), ("3inst", 4096, 14336)])
+def test_matvec_mfma_full_size_sampled_bands(api, code, M, N):
+    """The benchmark's tail-biting shapes at batch 8 (random streams): 16 sampled bands of
+    16 output rows (first, last and seeded) against the oracle on those bands' streams."""
+    import torch
+    L, W = 16, 16
+    rng = np.random.default_rng(60 + M)
+    words = rng.integers(0, 1 << 32, size=((M // 16) * (N // 16), W), dtype=np.uint32)
+    x = inputs.targets(8, N, 61)
+    say("matvec_mfma full size %dx%d %s" % (M, N, code))
+    y = api.decode_matvec_mfma(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x),
+                               L=L, code=code, tailbiting=True)
+    sync()
+    yh = y.cpu().numpy()
+    bands = sorted({0, M // 16 - 1} | set(rng.choice(M // 16, size=14, replace=False).tolist()))
+    NTJ = N // 16
+    sub = np.concatenate([words[I * NTJ:(I + 1) * NTJ] for I in bands])
+    Ms = 16 * len(bands)
+    C = oracle.code_table(code, L)
+    y_o = oracle.decode_matvec(sub, Ms, N, C, x, L, 2, tailbiting=True)
+    Wm = matrix(sub, Ms, N, C, L, True)
+    cols = np.concatenate([np.arange(16 * I, 16 * I + 16) for I in bands])
+    err = np.abs(yh[:, cols].astype(np.float64) - y_o)
+    assert np.all(err <= bound(x, Wm, N))
