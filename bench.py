@@ -74,6 +74,8 @@ def main() -> int:
                     help="profiling only: encode the first N sequences instead of all 65536")
     ap.add_argument("--bcjr-seqs", type=int, default=0,
                     help="profiling only: run the BCJR passes on the first N sequences")
+    ap.add_argument("--matvec-reps", type=int, default=200,
+                    help="launches timed per decode -> matvec shape (fewer under a profiler)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
@@ -222,7 +224,7 @@ def main() -> int:
         # Each shape is timed through both entry points: the fp32 VALU product
         # (qtcq_decode_matvec) and the matrix-core product (qtcq_decode_matvec_mfma, its
         # split of x included, workspace preallocated).
-        reps = 200
+        reps = max(1, args.matvec_reps)
         for label, bb, M_, N_, cd, tbf in cases:
             mws = api.matvec_mfma_workspace(N_)
             for nb in (1, 8):

@@ -42,4 +42,25 @@ def test_wrappers_reject_mismatched_tensors(api):
     with pytest.raises(ValueError):
         api.decode_matvec(torch.zeros((4, 17), dtype=torch.int32, device=dev), 32, 32,
                           torch.zeros(48, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        api.decode_matvec_mfma(torch.zeros((3, 17), dtype=torch.int32, device=dev), 32, 32,
+                               torch.zeros(32, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        api.decode_matvec_mfma(torch.zeros((4, 17), dtype=torch.int32, device=dev), 32, 32,
+                               torch.zeros((2, 48), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        api.matvec_mfma_workspace(40)
+    torch.cuda.synchronize()
+
+
+def test_matvec_mfma_rejects_small_workspace(api):
+    """A workspace below qtcq_decode_matvec_mfma_workspace_bytes(N) is refused by the C
+    entry point before any launch."""
+    import torch
+    from trellis_coded_weight_amd import _native as nat
+    dev = "cuda"
+    small = torch.empty(nat.qtcq_decode_matvec_mfma_workspace_bytes(64) - 16, dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError, match="QTCQ_ERR_WORKSPACE|workspace"):
+        api.decode_matvec_mfma(torch.zeros((16, 17), dtype=torch.int32, device=dev), 64, 64,
+                               torch.zeros(64, dtype=torch.float32, device=dev), workspace=small)
     torch.cuda.synchronize()

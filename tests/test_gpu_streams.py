@@ -63,7 +63,9 @@ def test_tailbiting_and_matvec_deterministic(api):
     x = dev(inputs.targets(3, 128, 76))
     y1 = api.decode_matvec(r1[0], 128, 128, x, tailbiting=True)
     y2 = api.decode_matvec(r2[0], 128, 128, x, tailbiting=True)
+    z1 = api.decode_matvec_mfma(r1[0], 128, 128, x, tailbiting=True)
+    z2 = api.decode_matvec_mfma(r2[0], 128, 128, x, tailbiting=True)
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
-    assert torch.equal(y1, y2)
+    assert torch.equal(y1, y2) and torch.equal(z1, z2)
