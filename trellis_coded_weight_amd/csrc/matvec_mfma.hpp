@@ -46,6 +46,11 @@
 
 namespace qtcq {
 
+// Fourth word of a raw (unstructured, stride 0) buffer descriptor on gfx9-family chips:
+// DATA_FORMAT = 32 bits, no swizzle, no index, so the range check compares each byte
+// offset against the descriptor's size and an access past it returns zero.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 typedef _Float16 mv_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mv_half2 __attribute__((ext_vector_type(2)));
 typedef float mv_float4 __attribute__((ext_vector_type(4)));
@@ -201,11 +206,11 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     // k >= N of the split x; the prefetch after a wave's last k-block reads zeros; and
     // the lanes of batch rows beyond the batch start past the end of the split x.
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, 0x00020000);
+        const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint4*>(xs), (short)0, nkb * (int)MatvecMfmaShape::kBlockBytes, 0x00020000);
+        const_cast<uint4*>(xs), (short)0, nkb * (int)MatvecMfmaShape::kBlockBytes, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(sc), (short)0, nkb * (int)MatvecMfmaShape::kScaleBytes, 0x00020000);
+        const_cast<float*>(sc), (short)0, nkb * (int)MatvecMfmaShape::kScaleBytes, kRawBufferWord3);
     // Byte offsets of k-block kb = wave + 2 NW j (tiles 2 kb and 2 kb + 1); the second
     // register set (kb + NW, 2 NW tiles further) adds a constant to the stream offsets
     // and has its own B offset.
