@@ -15,8 +15,8 @@ Extra objects on the line:
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
   bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
-  decode_matvec -- y = W x straight from the streams (per launch, batch 1 and 8; fp32
-                   VALU products and matrix-core products)
+  decode_matvec -- y = W x straight from the streams (per call, batch 1 and 8 with fp32
+                   VALU products; batch 1, 8 and 32 with matrix-core products)
   configs       -- the other encode configurations (16 sequences; 4096x14336 3INST;
                    weighted 4096x4096) and the BCJR pass at tau = 1, 0.1, 0.01
 """
@@ -227,15 +227,18 @@ def main() -> int:
         reps = max(1, args.matvec_reps)
         for label, bb, M_, N_, cd, tbf in cases:
             mws = api.matvec_mfma_workspace(N_)
-            for nb in (1, 8):
+            for nb in (1, 8, 32):
                 xv = torch.from_numpy(g.standard_normal((nb, N_), dtype=np.float32)).to(dev)
-                yv = api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)   # checks shapes
-                api.decode_matvec_mfma(bb, M_, N_, xv, code=cd, tailbiting=tbf, workspace=mws)
+                yv = api.decode_matvec_mfma(bb, M_, N_, xv, code=cd, tailbiting=tbf, workspace=mws)
+                if nb <= 8:
+                    api.decode_matvec(bb, M_, N_, xv, code=cd, tailbiting=tbf)   # checks shapes
                 codei = nat.QTCQ_CODE_1MAD if cd == "1mad" else nat.QTCQ_CODE_3INST
                 args_ = (bb.data_ptr(), M_, N_, L, K, codei, tbf, xv.data_ptr(), nb, yv.data_ptr())
-                for kind, call in (("", lambda: nat.qtcq_decode_matvec(*args_, sptr)),
-                                   (", mfma", lambda: nat.qtcq_decode_matvec_mfma(
-                                       *args_, mws.data_ptr(), mws.numel(), sptr))):
+                calls = [(", mfma", lambda: nat.qtcq_decode_matvec_mfma(
+                    *args_, mws.data_ptr(), mws.numel(), sptr))]
+                if nb <= 8:      # the fp32 VALU product takes at most 8 rows
+                    calls.insert(0, ("", lambda: nat.qtcq_decode_matvec(*args_, sptr)))
+                for kind, call in calls:
                     torch.cuda.synchronize()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record(stream)

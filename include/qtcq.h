@@ -270,13 +270,15 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
  * to first order, without underflow (blocks of x whose largest magnitude is below
  * 2^-111 keep less precision).  A row of x holding inf or NaN gives non-finite outputs
  * in that row.
- * Arguments as qtcq_decode_matvec, plus
+ * Arguments as qtcq_decode_matvec, except that batch may be 0..32 (rows are taken 8 at a
+ * time by one matrix instruction per 8 rows, so a wider batch adds little time), plus
  *   workspace  device scratch, 16-byte aligned, >= qtcq_decode_matvec_mfma_workspace_bytes(N)
  *              (the split x and its block scales; contents on entry are ignored)
  * Two kernels are enqueued on `stream` (the split, then the product).
- * Errors: as qtcq_decode_matvec, QTCQ_ERR_UNSUPPORTED also for N > 2^24, and
- * QTCQ_ERR_WORKSPACE (workspace NULL, misaligned or too small). */
-size_t qtcq_decode_matvec_mfma_workspace_bytes(int N);   /* 0 if N < 0, N % 16 != 0 or N > 2^24 */
+ * Errors: as qtcq_decode_matvec (QTCQ_ERR_UNSUPPORTED for batch > 32), also
+ * QTCQ_ERR_UNSUPPORTED for N > 2^22, and QTCQ_ERR_WORKSPACE (workspace NULL, misaligned
+ * or too small). */
+size_t qtcq_decode_matvec_mfma_workspace_bytes(int N);   /* 0 if N < 0, N % 16 != 0 or N > 2^22 */
 qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, int k, int code,
                                     int tailbiting, const float* x, int batch, float* y,
                                     void* workspace, size_t workspace_bytes, void* stream);

@@ -182,22 +182,23 @@ def test_decode_matvec_mfma_validation(nat):
             a[names.index(kk)] = v
         return st(*a)
 
-    # per 32 columns (a half block rounds up): 1 KiB of split x and 8 block scales,
-    # rounded up to 256 bytes, plus 256
+    # per 32 columns (a half block rounds up) and 8 rows of the largest batch (32): 1 KiB
+    # of split x and 8 block scales, rounded up to 256 bytes, plus 256
     def size(nkb):
-        return -(-nkb * (1024 + 32) // 256) * 256 + 256
+        return -(-nkb * 4 * (1024 + 32) // 256) * 256 + 256
     assert need == size(2)
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(48) == size(2)
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(8192) == size(256)
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(0) == 256
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(24) == 0
     assert nat.qtcq_decode_matvec_mfma_workspace_bytes(-16) == 0
-    assert nat.qtcq_decode_matvec_mfma_workspace_bytes((1 << 24) + 16) == 0
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes(1 << 22) == size(1 << 17)
+    assert nat.qtcq_decode_matvec_mfma_workspace_bytes((1 << 22) + 16) == 0
     assert call(M=24) == nat.QTCQ_ERR_INVALID_ARG
     assert call(N=-16) == nat.QTCQ_ERR_INVALID_ARG
     assert call(batch=-1) == nat.QTCQ_ERR_INVALID_ARG
-    assert call(batch=9) == nat.QTCQ_ERR_UNSUPPORTED
-    assert call(N=(1 << 24) + 16) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(batch=33) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(N=(1 << 22) + 16) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(code=4) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(x=None) == nat.QTCQ_ERR_INVALID_ARG

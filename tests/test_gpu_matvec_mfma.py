@@ -71,20 +71,30 @@ def test_matvec_mfma_random_streams(api, tb, L, code, M, N, batch):
     check(api, words, M, N, L, code, tb, x, "random")
 
 
-@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 17, 24, 25, 31, 32])
 def test_matvec_mfma_every_batch_width(api, batch):
-    """Every batch width; each row equals the same row computed alone, bit for bit (the
-    row's block scales and matrix-core columns do not depend on the other rows)."""
+    """Batch widths over one to four B fragments of 8 rows, full and partial; each row
+    equals the same row computed alone, bit for bit (the row's block scales and
+    matrix-core column do not depend on the other rows or on how many fragments run)."""
     import torch
     M, N, L = 32, 1040, 16
     words = random_words(M, N, L, False, 900 + batch)
     x = inputs.targets(batch, N, 910 + batch)
     y = check(api, words, M, N, L, "1mad", False, x, "batch")
     bd = torch.from_numpy(words.view(np.int32)).cuda()
-    for i in sorted({0, batch - 1}):
+    for i in sorted({0, 7 % batch, 8 % batch, batch - 1}):
         yi = api.decode_matvec_mfma(bd, M, N, dev(x[i:i + 1]), L=L)
         sync()
         assert torch.equal(yi[0], y[i])
+
+
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("code", ["1mad", "3inst"])
+def test_matvec_mfma_batch_32(api, tb, code):
+    """Four fragments, ragged N / 16, both codes and stream kinds."""
+    words = random_words(48, 2064, 16, tb, 70)
+    x = inputs.targets(32, 2064, 71)
+    check(api, words, 48, 2064, 16, code, tb, x, "batch 32")
 
 
 @pytest.mark.parametrize("tb", [False, True])
@@ -179,11 +189,11 @@ def test_matvec_mfma_deterministic_and_workspace_reuse(api):
     words = random_words(M, N, 16, False, 5)
     bd = torch.from_numpy(words.view(np.int32)).cuda()
     ws = api.matvec_mfma_workspace(N)
-    x8 = dev(inputs.targets(8, N, 6))
+    x32 = dev(inputs.targets(32, N, 6))
     x2 = dev(inputs.targets(2, N, 7))
     say("matvec_mfma determinism")
     a = api.decode_matvec_mfma(bd, M, N, x2, workspace=ws)
-    api.decode_matvec_mfma(bd, M, N, x8, workspace=ws)
+    api.decode_matvec_mfma(bd, M, N, x32, workspace=ws)
     b = api.decode_matvec_mfma(bd, M, N, x2, workspace=ws)
     c = api.decode_matvec_mfma(bd, M, N, x2)
     sync()

@@ -268,8 +268,9 @@ def decode_matvec_mfma(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: i
                        k: int = 2, code="1mad", tailbiting: bool = False,
                        workspace: torch.Tensor | None = None) -> torch.Tensor:
     """decode_matvec with the products on the matrix cores: the code values (exact in fp16)
-    times x split per row into two scaled fp16 parts.  Same arguments and result layout;
-    `workspace` (matvec_mfma_workspace(N)) is allocated when not given."""
+    times x split per 32-column block into two scaled fp16 parts.  Same arguments and
+    result layout, with up to 32 rows of x; `workspace` (matvec_mfma_workspace(N)) is
+    allocated when not given."""
     one = x.dim() == 1
     x2 = x.reshape(1, -1) if one else x
     _dev_f32(x2, "x")

@@ -58,43 +58,51 @@ typedef float mv_float4 __attribute__((ext_vector_type(4)));
 struct MatvecMfmaShape {
     static constexpr int kThreads = 1024;
     static constexpr int kWaves = kThreads / 64;
-    static constexpr int kMaxBatch = 8;
-    // one k-block (32 columns of x): the B operand of one MFMA, 64 lanes x 8 halves
+    // batch rows per B fragment (hi and lo of 8 rows fill its 16 columns) and fragments
+    static constexpr int kRowsPerFrag = 8;
+    static constexpr int kMaxFrags = 4;
+    static constexpr int kMaxBatch = kRowsPerFrag * kMaxFrags;
+    // one B fragment (32 columns of x for 8 rows): 64 lanes x 8 halves
     static constexpr size_t kBlockBytes = 64 * 16;
-    // per k-block: 8 row scales 2^-s (float)
+    // per fragment and k-block: 8 row scales 2^-s (float)
     static constexpr size_t kScaleBytes = 8 * 4;
     static constexpr int kSplitBlock = 256;
-    // byte offsets into the workspace stay below 2^31
-    static constexpr int kMaxN = 1 << 24;
+    // byte offsets into the workspace (at most twice its size) stay below 2^31
+    static constexpr int kMaxN = 1 << 22;
     // uint32 words of one T = 256 stream: L + 2 * 255 bits, or 512 tail-biting
     template <int L, bool TB>
     static constexpr int stream_words() { return TB ? 16 : (L + 2 * 255 + 31) / 32; }
-    static int kblocks(int N) { return (N / 16 + 1) / 2; }
-    // workspace: [nkb][64 lanes][8 halves] split x, then float scale[nkb][8]
+    __host__ __device__ static int kblocks(int N) { return (N / 16 + 1) / 2; }
+    __host__ __device__ static int frags(int batch) { return (batch + kRowsPerFrag - 1) / kRowsPerFrag; }
+    // workspace (sized for the largest batch): split x [nkb][frags][64 lanes][8 halves],
+    // then float scale [nkb][frags][8]
     static size_t workspace_bytes(int N)
     {
         const size_t nkb = (size_t)kblocks(N);
-        return ((nkb * (kBlockBytes + kScaleBytes) + 255) / 256) * 256 + 256;
+        return ((nkb * kMaxFrags * (kBlockBytes + kScaleBytes) + 255) / 256) * 256 + 256;
     }
 };
 
 // Split of x into the B operand, one scale per batch row and k-block (32 columns).
-//   grid.x = ceil(nkb * 64 / kSplitBlock), block = kSplitBlock; thread t writes lane
-//   slot l = t % 64 of k-block kb = t / 64, i.e. the 8 halves B[8 g + e][j] (g = l / 16,
-//   j = l % 16): xh (j < 8) or xl (j >= 8) of batch row j & 7 at columns 32 kb + 8 g + e,
-//   so a wave writes one k-block's kilobyte contiguously.  The four slots of a (row,
-//   block) pair (g = 0..3) are lanes 16 apart in one wave and share the block's maximum
-//   by two shuffles.  x [batch][N] (16-byte aligned, N a multiple of 16); xs [nkb][64]
-//   16-byte fragments; sc [nkb][8] the factor 2^-s of each row's block.  Columns k >= N
-//   (the half k-block after an odd N / 16) are written as zero; slots of rows >= batch
-//   are not written (the product kernel never reads them).
+//   grid.x = ceil(nkb * nf * 64 / kSplitBlock), block = kSplitBlock, nf = frags(batch);
+//   thread t writes lane slot l = t % 64 of fragment f of k-block kb (t / 64 = kb nf + f),
+//   i.e. the 8 halves B[8 g + e][j] (g = l / 16, j = l % 16): xh (j < 8) or xl (j >= 8)
+//   of batch row 8 f + (j & 7) at columns 32 kb + 8 g + e, so a wave writes one
+//   fragment's kilobyte contiguously.  The four slots of a (row, block) pair (g = 0..3)
+//   are lanes 16 apart in one wave and share the block's maximum by two shuffles.
+//   x [batch][N] (16-byte aligned, N a multiple of 16); xs [nkb][nf][64] 16-byte
+//   fragments; sc [nkb][nf][8] the factor 2^-s of each row's block.  Columns k >= N (the
+//   half k-block after an odd N / 16) are written as zero; slots of rows >= batch are not
+//   written (the product kernel never reads them).
 __global__ void __launch_bounds__(MatvecMfmaShape::kSplitBlock)
 matvec_split_x(const float* __restrict__ x, int N, int nkb, int batch, uint4* __restrict__ xs,
                float* __restrict__ sc)
 {
+    const int nf = MatvecMfmaShape::frags(batch);
     const int t = blockIdx.x * MatvecMfmaShape::kSplitBlock + threadIdx.x;
-    const int kb = t >> 6, l = t & 63, g = l >> 4, j = l & 15, i = j & 7;
-    // whole waves share kb, and the shuffle partners (l ^ 16, l ^ 32) share i: a lane
+    const int kf = t >> 6, l = t & 63, g = l >> 4, j = l & 15;
+    const int kb = kf / nf, i = 8 * (kf - kb * nf) + (j & 7);
+    // whole waves share (kb, f), and the shuffle partners (l ^ 16, l ^ 32) share i: a lane
     // that leaves here takes its partners with it
     if (kb >= nkb || i >= batch) return;
     const int n0 = 32 * kb + 8 * g;
@@ -129,8 +137,8 @@ matvec_split_x(const float* __restrict__ x, int N, int nkb, int batch, uint4* __
         const _Float16 hh = (_Float16)xp;                  // round to nearest even
         h[e] = j < 8 ? hh : (_Float16)(xp - (float)hh);    // the difference is exact
     }
-    xs[(size_t)kb * 64 + l] = __builtin_bit_cast(uint4, h);
-    if (l < 8) sc[(size_t)kb * 8 + i] = __builtin_ldexpf(1.0f, -s);
+    xs[(size_t)kf * 64 + l] = __builtin_bit_cast(uint4, h);
+    if (l < 8) sc[(size_t)kf * 8 + l] = __builtin_ldexpf(1.0f, -s);
 }
 
 // A constant copied into a VGPR (opaque to the compiler, so it stays a VGPR operand).
@@ -176,9 +184,9 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
 }
 
 // grid.x = M / 16, block = MatvecMfmaShape::kThreads.  bits [(M/16)(N/16)][Wd] with
-// Wd = MatvecMfmaShape::stream_words<L, TB>();
-// xs, sc as written by matvec_split_x for this x; y [batch][M].
-template <int L, int CODE, bool TB>
+// Wd = MatvecMfmaShape::stream_words<L, TB>(); xs, sc as written by matvec_split_x for
+// this x; y [batch][M].  NF = frags(batch) B fragments per k-block.
+template <int L, int CODE, bool TB, int NF>
 __global__ void __launch_bounds__(MatvecMfmaShape::kThreads)
 decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
                    const uint4* __restrict__ xs, const float* __restrict__ sc, int batch,
@@ -186,7 +194,10 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
 {
     constexpr int NW = MatvecMfmaShape::kWaves;
     constexpr int Wd = MatvecMfmaShape::stream_words<L, TB>();
-    __shared__ float red[NW][8][16];
+    constexpr int FB = (int)MatvecMfmaShape::kBlockBytes;     // bytes of one fragment
+    constexpr int SB = (int)MatvecMfmaShape::kScaleBytes;     // bytes of its scales
+    static_assert(NF >= 1 && NF <= MatvecMfmaShape::kMaxFrags, "fragments");
+    __shared__ float red[NW][8 * NF][16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,35 +215,43 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     // the tile after the last one (the second half of the last k-block when N / 16 is
     // odd) decodes as the all-zero window, whose finite codes meet the zero columns
     // k >= N of the split x; the prefetch after a wave's last k-block reads zeros; and
-    // the lanes of batch rows beyond the batch start past the end of the split x.
+    // the lanes of the last fragment's rows beyond the batch start past the end.
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint4*>(xs), (short)0, nkb * (int)MatvecMfmaShape::kBlockBytes, kRawBufferWord3);
+        const_cast<uint4*>(xs), (short)0, nkb * NF * FB, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(sc), (short)0, nkb * (int)MatvecMfmaShape::kScaleBytes, kRawBufferWord3);
+        const_cast<float*>(sc), (short)0, nkb * NF * SB, kRawBufferWord3);
     // Byte offsets of k-block kb = wave + 2 NW j (tiles 2 kb and 2 kb + 1); the second
     // register set (kb + NW, 2 NW tiles further) adds a constant to the stream offsets
-    // and has its own B offset.
+    // and has its own B and scale offsets.  Fragment f of a k-block is f FB (f SB) bytes
+    // after fragment 0 (an immediate offset); the last fragment has offsets of its own,
+    // past the end for the lanes of rows beyond the batch.
     constexpr int dstr = 4 * NW * Wd * 4;        // stream bytes of 2 NW k-blocks
     constexpr int dstr1 = 2 * NW * Wd * 4;       // of NW k-blocks
-    const int dx = 2 * (int)MatvecMfmaShape::kBlockBytes * NW;
+    const int dx = 2 * NF * FB * NW, dsc = 2 * NF * SB * NW;
     int oh = ((2 * wave + (g >> 1)) * Wd + o_hi) * 4;
     int ol = ((2 * wave + (g >> 1)) * Wd + o_lo) * 4;
-    const bool live = (r & 7) < batch;
-    int ob0 = live ? wave * (int)MatvecMfmaShape::kBlockBytes + lane * 16
-                   : nkb * (int)MatvecMfmaShape::kBlockBytes;
-    int ob1 = ob0 + (int)MatvecMfmaShape::kBlockBytes * NW;
-    // the scale of this lane's batch row in k-block kb (zero past the end, like B)
-    constexpr int dsc = 2 * (int)MatvecMfmaShape::kScaleBytes * NW;
-    int os0 = live ? wave * (int)MatvecMfmaShape::kScaleBytes + (r & 7) * 4
-                   : nkb * (int)MatvecMfmaShape::kScaleBytes;
-    int os1 = os0 + (int)MatvecMfmaShape::kScaleBytes * NW;
-    auto load = [&](int d, int ob, int os, uint32_t& wh, uint32_t& wl, uint4& bx, float& scl) {
-        wh = __builtin_amdgcn_raw_buffer_load_b32(wr, oh + d, 0, 0);
-        wl = __builtin_amdgcn_raw_buffer_load_b32(wr, ol + d, 0, 0);
-        bx = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ob, 0, 0));
-        scl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, os, 0, 0));
+    const bool live_last = 8 * (NF - 1) + (r & 7) < batch;
+    int ob0 = wave * NF * FB + lane * 16;
+    int ob1 = ob0 + NF * FB * NW;
+    int obl0 = live_last ? ob0 + (NF - 1) * FB : nkb * NF * FB;
+    int obl1 = obl0 + NF * FB * NW;
+    int os0 = wave * NF * SB + (r & 7) * 4;
+    int os1 = os0 + NF * SB * NW;
+    int osl0 = live_last ? os0 + (NF - 1) * SB : nkb * NF * SB;
+    int osl1 = osl0 + NF * SB * NW;
+    struct Set { uint32_t wh, wl; uint4 b[NF]; float sc[NF]; };
+    auto load = [&](int d, int ob, int obl, int os, int osl, Set& q) {
+        q.wh = __builtin_amdgcn_raw_buffer_load_b32(wr, oh + d, 0, 0);
+        q.wl = __builtin_amdgcn_raw_buffer_load_b32(wr, ol + d, 0, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int o = f == NF - 1 ? obl : ob + f * FB;
+            const int os_ = f == NF - 1 ? osl : os + f * SB;
+            q.b[f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0));
+            q.sc[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, os_, 0, 0));
+        }
     };
     // loop-invariant operands held in VGPRs (an SGPR operand halves a VALU op's issue rate)
     const uint32_t k519 = vgpr_u32(519u);
@@ -240,60 +259,77 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     // Each MFMA's result, times its block's 2^-s (exact), is added to the accumulators
     // one k-block later, so its latency hides behind the next block's decode; the
     // additions stay in k-block order.
-    mv_float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    mv_float4 pend = {0.0f, 0.0f, 0.0f, 0.0f};
-    float pscl = 0.0f;
-    auto step = [&](uint32_t wh, uint32_t wl, const uint4& bx, float scl) {
-        const uint32_t f = __builtin_amdgcn_alignbit(wh, wl, sh);
+    mv_float4 acc[NF], pend[NF];
+    float pscl[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        acc[f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+        pend[f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+        pscl[f] = 0.0f;
+    }
+    auto settle = [&]() {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[f][v] = __builtin_fmaf(pend[f][v], pscl[f], acc[f][v]);
+    };
+    auto step = [&](const Set& q) {
+        const uint32_t fw = __builtin_amdgcn_alignbit(q.wh, q.wl, sh);
         uint32_t a[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t w0 = (f >> (32 - L - 4 * p)) & ((1u << L) - 1u);
-            const uint32_t w1 = (f >> (30 - L - 4 * p)) & ((1u << L) - 1u);
+            const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
+            const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
             a[p] = code_raw_pair_f16<CODE>(w0, w1, k519, kbias);
         }
         const mv_half8 av = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         const mv_float4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        settle();
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(pend[v], pscl, acc[v]);
-        pend = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(mv_half8, bx), zero, 0, 0, 0);
-        pscl = scl;
+        for (int f = 0; f < NF; ++f) {
+            pend[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(mv_half8, q.b[f]), zero, 0, 0, 0);
+            pscl[f] = q.sc[f];
+        }
     };
 
     // two register sets, k-blocks alternating between them; no load is conditional
     if (wave < nkb) {
-        uint32_t h0, l0, h1, l1;
-        uint4 b0, b1;
-        float s0, s1;
+        Set q0, q1;
         int kb = wave;
-        load(0, ob0, os0, h0, l0, b0, s0);
+        load(0, ob0, obl0, os0, osl0, q0);
         for (; kb + NW < nkb; kb += 2 * NW) {
-            load(dstr1, ob1, os1, h1, l1, b1, s1);
-            step(h0, l0, b0, s0);
+            load(dstr1, ob1, obl1, os1, osl1, q1);
+            step(q0);
             oh += dstr;
             ol += dstr;
             ob0 += dx;
             ob1 += dx;
+            obl0 += dx;
+            obl1 += dx;
             os0 += dsc;
             os1 += dsc;
-            load(0, ob0, os0, h0, l0, b0, s0);
-            step(h1, l1, b1, s1);
+            osl0 += dsc;
+            osl1 += dsc;
+            load(0, ob0, obl0, os0, osl0, q0);
+            step(q1);
         }
-        if (kb < nkb) step(h0, l0, b0, s0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(pend[v], pscl, acc[v]);
+        if (kb < nkb) step(q0);
+        settle();
     }
 
-    // lane l holds rows 4 g + v of column r: xh products of batch row r (r < 8) or xl
-    // products of batch row r - 8; add the two parts, then the waves in order
+    // lane l holds rows 4 g + v of column r of each fragment f: xh products of batch row
+    // 8 f + r (r < 8) or xl products of batch row 8 f + r - 8; add the two parts, then
+    // the waves in order
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const float s = acc[v] + __shfl_xor(acc[v], 8, 64);
-        if (r < batch) red[wave][r][4 * g + v] = s;
-    }
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float s = acc[f][v] + __shfl_xor(acc[f][v], 8, 64);
+            if (r < 8 && 8 * f + r < batch) red[wave][8 * f + r][4 * g + v] = s;
+        }
     __syncthreads();
-    if (tid < 16 * batch) {
-        const int i = tid >> 4, rr = tid & 15;
+    for (int o = tid; o < 16 * batch; o += MatvecMfmaShape::kThreads) {
+        const int i = o >> 4, rr = o & 15;
         float s = red[0][i][rr];
 #pragma unroll
         for (int q = 1; q < NW; ++q) s += red[q][i][rr];

@@ -340,19 +340,27 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
 {
     static_assert(MatvecMfmaShape::stream_words<L, TB>() == (TB ? 16 : 17), "stream words");
     const int nkb = MatvecMfmaShape::kblocks(N);
+    const int nf = MatvecMfmaShape::frags(batch);
     uint4* xs = static_cast<uint4*>(workspace);
-    float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)nkb * MatvecMfmaShape::kBlockBytes);
+    float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (size_t)nkb * nf * MatvecMfmaShape::kBlockBytes);
     if (nkb > 0) {
-        const int threads = nkb * 64;
+        const int threads = nkb * nf * 64;
         const int bs = MatvecMfmaShape::kSplitBlock;
         hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, st,
                            x, N, nkb, batch, xs, sc);
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
     }
-    hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB>), dim3((unsigned)(M / 16)),
-                       dim3(MatvecMfmaShape::kThreads), 0, st, bits, M, N,
-                       static_cast<const uint4*>(xs), static_cast<const float*>(sc), batch, y);
+    const dim3 grid((unsigned)(M / 16)), block(MatvecMfmaShape::kThreads);
+    const uint4* cxs = xs;
+    const float* csc = sc;
+    switch (nf) {
+    case 1: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
+    case 2: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
+    case 3: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 3>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
+    default: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
+    }
     return launch_status();
 }
 
