@@ -260,3 +260,13 @@ def test_matvec_mfma_full_size_sampled_bands(api, code, M, N):
     cols = np.concatenate([np.arange(16 * I, 16 * I + 16) for I in bands])
     err = np.abs(yh[:, cols].astype(np.float64) - y_o)
     assert np.all(err <= bound(x, Wm, N))
+
+
+@pytest.mark.parametrize("M,batch", [(16384, 9), (16400, 32), (16400, 16)])
+def test_matvec_mfma_two_bands_per_workgroup(api, M, batch):
+    """M / 16 >= 1024 with more than 8 rows: each workgroup takes two bands (the last one
+    alone when M / 16 is odd); every output against the oracle."""
+    N = 80
+    words = random_words(M, N, 16, True, M + batch)
+    x = inputs.targets(batch, N, 72)
+    check(api, words, M, N, 16, "3inst", True, x, "two bands")

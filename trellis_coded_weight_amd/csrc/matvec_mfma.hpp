@@ -183,10 +183,13 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
     }
 }
 
-// grid.x = M / 16, block = MatvecMfmaShape::kThreads.  bits [(M/16)(N/16)][Wd] with
-// Wd = MatvecMfmaShape::stream_words<L, TB>(); xs, sc as written by matvec_split_x for
-// this x; y [batch][M].  NF = frags(batch) B fragments per k-block.
-template <int L, int CODE, bool TB, int NF>
+// grid.x = ceil((M / 16) / BANDS), block = MatvecMfmaShape::kThreads.  bits
+// [(M/16)(N/16)][Wd] with Wd = MatvecMfmaShape::stream_words<L, TB>(); xs, sc as written
+// by matvec_split_x for this x; y [batch][M].  NF = frags(batch) B fragments per k-block.
+// BANDS = 2: a workgroup takes bands 2 blockIdx.x and 2 blockIdx.x + 1 (the second may be
+// absent when M / 16 is odd), and every B fragment it loads serves both, which halves
+// the split x's reads from L2 at wide batches.
+template <int L, int CODE, bool TB, int NF, int BANDS>
 __global__ void __launch_bounds__(MatvecMfmaShape::kThreads)
 decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
                    const uint4* __restrict__ xs, const float* __restrict__ sc, int batch,
@@ -197,27 +200,38 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     constexpr int FB = (int)MatvecMfmaShape::kBlockBytes;     // bytes of one fragment
     constexpr int SB = (int)MatvecMfmaShape::kScaleBytes;     // bytes of its scales
     static_assert(NF >= 1 && NF <= MatvecMfmaShape::kMaxFrags, "fragments");
-    __shared__ float red[NW][8 * NF][16];
+    static_assert(BANDS == 1 || BANDS == 2, "bands");
+    // one MFMA result per band and fragment held back a k-block (hides its latency)
+    // when there are few of them; with more, the later MFMAs cover the earlier ones
+    constexpr bool DEFER = NF * BANDS <= 2;
+    __shared__ float red[NW][BANDS * 8 * NF][16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int I = blockIdx.x;
     const int NTJ = N >> 4, nkb = (NTJ + 1) >> 1;
-    const uint32_t* band = bits + (size_t)I * NTJ * Wd;
+    const int nbands = M >> 4;
+    const int I0 = BANDS * blockIdx.x;
     // f = bits [16 (g & 1), + 32) of words (r, r + 1): alignbit(w_hi, w_lo, sh); for even
     // g the lane's "lo" word is word r itself and the shift is 0
     const uint32_t sh = (g & 1) ? 16u : 0u;
     const int o_hi = r;
     const int o_lo = (g & 1) ? ((TB && r == 15) ? 0 : r + 1) : r;
-    // Both operands are read through buffer descriptors sized to the band's streams and
+    // Both operands are read through buffer descriptors sized to each band's streams and
     // to the split x: an offset past the end reads as zero without touching memory.  So
     // the tile after the last one (the second half of the last k-block when N / 16 is
     // odd) decodes as the all-zero window, whose finite codes meet the zero columns
-    // k >= N of the split x; the prefetch after a wave's last k-block reads zeros; and
-    // the lanes of the last fragment's rows beyond the batch start past the end.
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, kRawBufferWord3);
+    // k >= N of the split x; the prefetch after a wave's last k-block reads zeros; the
+    // lanes of the last fragment's rows beyond the batch start past the end; and an
+    // absent second band has an empty descriptor.
+    __amdgpu_buffer_rsrc_t wr[BANDS];
+#pragma unroll
+    for (int b = 0; b < BANDS; ++b) {
+        const bool has = I0 + b < nbands;
+        wr[b] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t*>(bits + (size_t)(has ? I0 + b : 0) * NTJ * Wd), (short)0,
+            has ? NTJ * Wd * 4 : 0, kRawBufferWord3);
+    }
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint4*>(xs), (short)0, nkb * NF * FB, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
@@ -241,10 +255,13 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     int os1 = os0 + NF * SB * NW;
     int osl0 = live_last ? os0 + (NF - 1) * SB : nkb * NF * SB;
     int osl1 = osl0 + NF * SB * NW;
-    struct Set { uint32_t wh, wl; uint4 b[NF]; float sc[NF]; };
+    struct Set { uint32_t wh[BANDS], wl[BANDS]; uint4 b[NF]; float sc[NF]; };
     auto load = [&](int d, int ob, int obl, int os, int osl, Set& q) {
-        q.wh = __builtin_amdgcn_raw_buffer_load_b32(wr, oh + d, 0, 0);
-        q.wl = __builtin_amdgcn_raw_buffer_load_b32(wr, ol + d, 0, 0);
+#pragma unroll
+        for (int b = 0; b < BANDS; ++b) {
+            q.wh[b] = __builtin_amdgcn_raw_buffer_load_b32(wr[b], oh + d, 0, 0);
+            q.wl[b] = __builtin_amdgcn_raw_buffer_load_b32(wr[b], ol + d, 0, 0);
+        }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             const int o = f == NF - 1 ? obl : ob + f * FB;
@@ -257,39 +274,51 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     const uint32_t k519 = vgpr_u32(519u);
     const uint32_t kbias = vgpr_u32(0xE5FEE5FEu);   // fp16 -1534 in both halves
     // Each MFMA's result, times its block's 2^-s (exact), is added to the accumulators
-    // one k-block later, so its latency hides behind the next block's decode; the
-    // additions stay in k-block order.
-    mv_float4 acc[NF], pend[NF];
+    // by FMA, in k-block order (DEFER: one k-block later, so its latency hides behind the
+    // next block's decode).
+    mv_float4 acc[BANDS][NF], pend[BANDS][NF];
     float pscl[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-        acc[f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
-        pend[f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < BANDS; ++b) {
+            acc[b][f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+            pend[b][f] = mv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
         pscl[f] = 0.0f;
     }
     auto settle = [&]() {
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+        for (int b = 0; b < BANDS; ++b)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[f][v] = __builtin_fmaf(pend[f][v], pscl[f], acc[f][v]);
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[b][f][v] = __builtin_fmaf(pend[b][f][v], pscl[f], acc[b][f][v]);
     };
     auto step = [&](const Set& q) {
-        const uint32_t fw = __builtin_amdgcn_alignbit(q.wh, q.wl, sh);
-        uint32_t a[4];
+        mv_half8 av[BANDS];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
-            const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
-            a[p] = code_raw_pair_f16<CODE>(w0, w1, k519, kbias);
+        for (int b = 0; b < BANDS; ++b) {
+            const uint32_t fw = __builtin_amdgcn_alignbit(q.wh[b], q.wl[b], sh);
+            uint32_t a[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
+                const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
+                a[p] = code_raw_pair_f16<CODE>(w0, w1, k519, kbias);
+            }
+            av[b] = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         }
-        const mv_half8 av = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         const mv_float4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        settle();
+        if constexpr (DEFER) settle();
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            pend[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(mv_half8, q.b[f]), zero, 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < BANDS; ++b)
+                pend[b][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[b], __builtin_bit_cast(mv_half8, q.b[f]), zero, 0, 0, 0);
             pscl[f] = q.sc[f];
         }
+        if constexpr (!DEFER) settle();
     };
 
     // two register sets, k-blocks alternating between them; no load is conditional
@@ -314,26 +343,30 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
             step(q1);
         }
         if (kb < nkb) step(q0);
-        settle();
+        if constexpr (DEFER) settle();
     }
 
-    // lane l holds rows 4 g + v of column r of each fragment f: xh products of batch row
-    // 8 f + r (r < 8) or xl products of batch row 8 f + r - 8; add the two parts, then
-    // the waves in order
+    // lane l holds rows 4 g + v of column r of each band's fragment f: xh products of
+    // batch row 8 f + r (r < 8) or xl products of batch row 8 f + r - 8; add the two
+    // parts, then the waves in order
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int b = 0; b < BANDS; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float s = acc[f][v] + __shfl_xor(acc[f][v], 8, 64);
-            if (r < 8 && 8 * f + r < batch) red[wave][8 * f + r][4 * g + v] = s;
-        }
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float s = acc[b][f][v] + __shfl_xor(acc[b][f][v], 8, 64);
+                if (r < 8 && 8 * f + r < batch) red[wave][b * 8 * NF + 8 * f + r][4 * g + v] = s;
+            }
     __syncthreads();
-    for (int o = tid; o < 16 * batch; o += MatvecMfmaShape::kThreads) {
-        const int i = o >> 4, rr = o & 15;
-        float s = red[0][i][rr];
+    for (int o = tid; o < BANDS * 16 * batch; o += MatvecMfmaShape::kThreads) {
+        const int b = o / (16 * batch), io = o - b * 16 * batch;
+        const int i = io >> 4, rr = io & 15;
+        if (I0 + b >= nbands) continue;
+        float s = red[0][b * 8 * NF + i][rr];
 #pragma unroll
-        for (int q = 1; q < NW; ++q) s += red[q][i][rr];
-        y[(size_t)i * M + 16 * I + rr] = code_rescale<CODE>(s);
+        for (int q = 1; q < NW; ++q) s += red[q][b * 8 * NF + i][rr];
+        y[(size_t)i * M + 16 * (I0 + b) + rr] = code_rescale<CODE>(s);
     }
 }
 

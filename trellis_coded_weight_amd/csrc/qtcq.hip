@@ -352,15 +352,24 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
     }
-    const dim3 grid((unsigned)(M / 16)), block(MatvecMfmaShape::kThreads);
+    // Two bands per workgroup once the batch spans three or four fragments (reading the
+    // split x then dominates: each fragment costs a kilobyte per k-block and wave) and
+    // M / 16 >= 1024, so the grid keeps >= 512 workgroups (two per CU).  Results do not
+    // depend on the choice (same arithmetic, same order).
+    const int nb = M / 16;
+    const bool two = nf >= 3 && nb >= 1024;
+    const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
     const uint4* cxs = xs;
     const float* csc = sc;
+#define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \
+                                               bits, M, N, cxs, csc, batch, y)
     switch (nf) {
-    case 1: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
-    case 2: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
-    case 3: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 3>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
-    default: hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, cxs, csc, batch, y); break;
+    case 1: QTCQ_MV(1, 1, grid1); break;
+    case 2: if (two) QTCQ_MV(2, 2, grid2); else QTCQ_MV(2, 1, grid1); break;
+    case 3: if (two) QTCQ_MV(3, 2, grid2); else QTCQ_MV(3, 1, grid1); break;
+    default: if (two) QTCQ_MV(4, 2, grid2); else QTCQ_MV(4, 1, grid1); break;
     }
+#undef QTCQ_MV
     return launch_status();
 }
 
