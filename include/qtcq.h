@@ -270,8 +270,9 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
  * to first order, without underflow (blocks of x whose largest magnitude is below
  * 2^-111 keep less precision).  A row of x holding inf or NaN gives non-finite outputs
  * in that row.
- * Arguments as qtcq_decode_matvec, except that batch may be 0..32 (rows are taken 8 at a
- * time by one matrix instruction per 8 rows, so a wider batch adds little time), plus
+ * Arguments as qtcq_decode_matvec, except that batch may be 0..32 (each group of 8 rows
+ * adds one matrix instruction per 16 output rows and 32 columns; the decode is shared),
+ * plus
  *   workspace  device scratch, 16-byte aligned, >= qtcq_decode_matvec_mfma_workspace_bytes(N)
  *              (the split x and its block scales; contents on entry are ignored)
  * Two kernels are enqueued on `stream` (the split, then the product).
