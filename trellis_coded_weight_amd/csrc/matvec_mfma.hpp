@@ -13,10 +13,11 @@
 // a power of two 2^s (chosen from the block's largest magnitude, which lands in
 // [2^14, 2^15)) and split into two fp16 parts, x' = x 2^s = xh + xl + d with
 // xh = rn16(x'), xl = rn16(x' - xh) (the difference is exact in fp32) and
-// |d| <= 2^-22 |x'| + 2^-25.  The 16 columns of the MFMA's B operand hold xh of batch
-// rows 0..7 (columns 0..7) and xl (columns 8..15), so one MFMA multiplies 16 rows x 32
-// columns of W by both parts of all eight rows.  A small first kernel writes the split,
-// in the B operand's lane order, and the factors 2^-s to the workspace.
+// |d| <= 2^-22 |x'| + 2^-25.  The 16 columns of one B operand (a fragment) hold xh of 8
+// batch rows (columns 0..7) and their xl (columns 8..15), so one MFMA multiplies 16 rows
+// x 32 columns of W by both parts of eight rows; up to four fragments (32 rows) share
+// each decoded A operand.  A small first kernel writes the split, in the B operand's
+// lane order, and the factors 2^-s to the workspace.
 //
 // Layout of v_mfma_f32_16x16x32_f16 (checked on the device): lane l holds
 //   A[l % 16][8 (l / 16) + e], B[8 (l / 16) + e][l % 16] for e = 0..7, and
@@ -27,8 +28,9 @@
 // words r and r + 1 (word 16 of a tail-biting stream is word 0): one funnel shift and
 // one bit-field extract per weight.
 //
-// Mapping.  One workgroup of 16 waves per band of 16 output rows (tile row I); wave w
-// takes k-blocks w, w + 16, ...  Each MFMA starts from zero; its 4 outputs per lane,
+// Mapping.  One workgroup of 16 waves per band of 16 output rows (tile row I), or per two
+// bands at wide batches on tall matrices; wave w takes k-blocks w, w + 16, ...  Each MFMA
+// starts from zero; its 4 outputs per lane,
 // times the block's 2^-s (exact), are added to the lane's accumulators in k-block order
 // by FMA; then hi + lo (lanes l and l ^ 8), the 16 waves in sequence and the code's
 // rescale.  Results are bit-deterministic and a one-hot x (its block scaled to 2^14,
