@@ -236,16 +236,18 @@ def test_matvec_mfma_encoded_4096x4096(api, tb):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("batch", [8, 32])
 @pytest.mark.parametrize("code,M,N", [("1mad", 28672, 8192), ("3inst", 4096, 14336)])
-def test_matvec_mfma_full_size_sampled_bands(api, code, M, N):
-    """The benchmark's tail-biting shapes at batch 8 (random streams): 16 sampled bands of
-    16 output rows (first, last and seeded) against the oracle on those bands' streams."""
+def test_matvec_mfma_full_size_sampled_bands(api, code, M, N, batch):
+    """The benchmark's tail-biting shapes at batch 8 and 32 (random streams; 28672x8192 at
+    batch 32 runs two bands per workgroup): 16 sampled bands of 16 output rows (first,
+    last and seeded) against the oracle on those bands' streams."""
     import torch
     L, W = 16, 16
     rng = np.random.default_rng(60 + M)
     words = rng.integers(0, 1 << 32, size=((M // 16) * (N // 16), W), dtype=np.uint32)
-    x = inputs.targets(8, N, 61)
-    say("matvec_mfma full size %dx%d %s" % (M, N, code))
+    x = inputs.targets(batch, N, 61)
+    say("matvec_mfma full size %dx%d %s batch %d" % (M, N, code, batch))
     y = api.decode_matvec_mfma(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x),
                                L=L, code=code, tailbiting=True)
     sync()
