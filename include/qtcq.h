@@ -284,6 +284,23 @@ qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, i
                                     int tailbiting, const float* x, int batch, float* y,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two halves of qtcq_decode_matvec_mfma, for several matrices that multiply the same
+ * x (in inference, projections that share their input): the split once, then one product
+ * per matrix [same passage].  qtcq_matvec_mfma_split_x writes the split of x ([batch][N],
+ * as above) into `workspace`; qtcq_decode_matvec_mfma_presplit multiplies the matrix of
+ * `bits` (M, L, k, code, tailbiting as above) by it and writes y [batch][M], reading
+ * `split` only (it is the workspace of a split of the same N and batch, enqueued earlier
+ * on this stream or otherwise ordered before it).  Results equal those of
+ * qtcq_decode_matvec_mfma bit for bit.
+ * Errors: as qtcq_decode_matvec_mfma; QTCQ_ERR_WORKSPACE for a workspace or split NULL,
+ * misaligned or below qtcq_decode_matvec_mfma_workspace_bytes(N). */
+qtcq_status qtcq_matvec_mfma_split_x(const float* x, int N, int batch, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+qtcq_status qtcq_decode_matvec_mfma_presplit(const uint32_t* bits, int M, int N, int L, int k,
+                                             int code, int tailbiting, const void* split,
+                                             size_t split_bytes, int batch, float* y,
+                                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,6 +212,39 @@ def test_decode_matvec_mfma_validation(nat):
     assert call(batch=0, bits=None, x=None, y=None, ws=None) == nat.QTCQ_OK
 
 
+def test_matvec_mfma_split_and_presplit_validation(nat):
+    need = nat.qtcq_decode_matvec_mfma_workspace_bytes(64)
+    sp = lambda *a: nat.raw_status("qtcq_matvec_mfma_split_x", *a)
+    # x, N, batch, workspace, workspace_bytes, stream
+    assert sp(FAKE, 24, 1, FAKE, need, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert sp(FAKE, 64, -1, FAKE, need, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert sp(FAKE, 64, 33, FAKE, need, None) == nat.QTCQ_ERR_UNSUPPORTED
+    assert sp(FAKE, 64, 1, None, need, None) == nat.QTCQ_ERR_WORKSPACE
+    assert sp(FAKE, 64, 1, FAKE, need - 1, None) == nat.QTCQ_ERR_WORKSPACE
+    assert sp(None, 64, 1, FAKE, need, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert sp(FAKE + 4, 64, 1, FAKE, need, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert sp(None, 64, 0, FAKE, need, None) == nat.QTCQ_OK
+    pp = lambda *a: nat.raw_status("qtcq_decode_matvec_mfma_presplit", *a)
+    # bits, M, N, L, k, code, tb, split, split_bytes, batch, y, stream
+    ok = [FAKE, 32, 64, 16, 2, 0, 0, FAKE, need, 1, FAKE, None]
+    names = ["bits", "M", "N", "L", "k", "code", "tb", "split", "sb", "batch", "y", "stream"]
+
+    def call(**kw):
+        a = list(ok)
+        for kk, v in kw.items():
+            a[names.index(kk)] = v
+        return pp(*a)
+
+    assert call(M=24) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(batch=33) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(split=None) == nat.QTCQ_ERR_WORKSPACE
+    assert call(sb=need - 1) == nat.QTCQ_ERR_WORKSPACE
+    assert call(y=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(bits=None) == nat.QTCQ_ERR_INVALID_ARG
+    assert call(M=0, bits=None, y=None) == nat.QTCQ_OK
+
+
 def test_tailbiting_sizes(nat):
     assert nat.qtcq_tailbiting_words(16, 2, 256) == 16     # exactly 2T bits, word-aligned
     assert nat.qtcq_tailbiting_words(16, 2, 8) == 1

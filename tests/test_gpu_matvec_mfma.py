@@ -272,3 +272,25 @@ def test_matvec_mfma_two_bands_per_workgroup(api, M, batch):
     words = random_words(M, N, 16, True, M + batch)
     x = inputs.targets(batch, N, 72)
     check(api, words, M, N, 16, "3inst", True, x, "two bands")
+
+
+@pytest.mark.parametrize("batch", [1, 8, 20, 32])
+def test_matvec_mfma_presplit_equals_one_call(api, batch):
+    """One split of x serves three matrices of different heights (plain and tail-biting,
+    both codes): each product equals the one-call product bit for bit, and the split is
+    not modified by the products."""
+    import torch
+    N = 1040
+    x = dev(inputs.targets(batch, N, 80 + batch))
+    say("matvec_mfma presplit batch=%d" % batch)
+    split = api.matvec_mfma_split_x(x)
+    sync()
+    before = split.clone()
+    for M, code, tb, seed in [(48, "1mad", False, 1), (16400, "3inst", True, 2), (4096, "1mad", True, 3)]:
+        words = random_words(M, N, 16, tb, 300 + seed)
+        bd = torch.from_numpy(words.view(np.int32)).cuda()
+        y1 = api.decode_matvec_mfma_presplit(bd, M, N, split, batch, code=code, tailbiting=tb)
+        y2 = api.decode_matvec_mfma(bd, M, N, x, code=code, tailbiting=tb)
+        sync()
+        assert torch.equal(y1, y2), "M=%d" % M
+    assert torch.equal(split, before)

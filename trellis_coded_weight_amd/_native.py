@@ -60,6 +60,9 @@ _SIGS = {
     "qtcq_decode_matvec_mfma_workspace_bytes": (_sz, [_int]),
     "qtcq_decode_matvec_mfma": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp,
                                        _vp, _sz, _vp]),
+    "qtcq_matvec_mfma_split_x": (_int, [_vp, _int, _int, _vp, _sz, _vp]),
+    "qtcq_decode_matvec_mfma_presplit": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp,
+                                                _sz, _int, _vp, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
     "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
@@ -188,3 +191,18 @@ def qtcq_decode_matvec_mfma(bits: int, M: int, N: int, L: int, k: int, code: int
                                         _ptr(x), batch, _ptr(y), _ptr(workspace),
                                         workspace_bytes, _ptr(stream)),
            "qtcq_decode_matvec_mfma")
+
+
+def qtcq_matvec_mfma_split_x(x: int, N: int, batch: int, workspace: int, workspace_bytes: int,
+                             stream: int = 0) -> None:
+    _check(_lib.qtcq_matvec_mfma_split_x(_ptr(x), N, batch, _ptr(workspace), workspace_bytes,
+                                         _ptr(stream)), "qtcq_matvec_mfma_split_x")
+
+
+def qtcq_decode_matvec_mfma_presplit(bits: int, M: int, N: int, L: int, k: int, code: int,
+                                     tailbiting: bool, split: int, split_bytes: int, batch: int,
+                                     y: int, stream: int = 0) -> None:
+    _check(_lib.qtcq_decode_matvec_mfma_presplit(_ptr(bits), M, N, L, k, code,
+                                                 1 if tailbiting else 0, _ptr(split), split_bytes,
+                                                 batch, _ptr(y), _ptr(stream)),
+           "qtcq_decode_matvec_mfma_presplit")

@@ -292,3 +292,40 @@ def decode_matvec_mfma(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: i
                                 x2.data_ptr(), x2.shape[0], y.data_ptr(), workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), _stream())
     return y[0] if one else y
+
+
+def matvec_mfma_split_x(x: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The split of x [batch][N] (or [N]) for decode_matvec_mfma_presplit, written into
+    `workspace` (matvec_mfma_workspace(N), allocated when not given), which is returned."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    _dev_f32(x2, "x")
+    N = x2.shape[1]
+    if workspace is None:
+        workspace = matvec_mfma_workspace(N)
+    elif not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    else:
+        _on_current_device(workspace, "workspace")
+    nat.qtcq_matvec_mfma_split_x(x2.data_ptr(), N, x2.shape[0], workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    return workspace
+
+
+def decode_matvec_mfma_presplit(bits: torch.Tensor, M: int, N: int, split: torch.Tensor,
+                                batch: int, L: int = 16, k: int = 2, code="1mad",
+                                tailbiting: bool = False) -> torch.Tensor:
+    """y [batch][M] = W x from a split made by matvec_mfma_split_x for this N and batch
+    (equal to decode_matvec_mfma bit for bit)."""
+    W = tailbiting_words(L, k, 256) if tailbiting else bitstream_words(L, k, 256)
+    if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
+            and bits.numel() == (M // 16) * (N // 16) * W):
+        raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
+    _on_current_device(bits, "bits")
+    if not (split.is_cuda and split.is_contiguous()):
+        raise ValueError("split must be a contiguous device tensor")
+    _on_current_device(split, "split")
+    y = torch.empty((batch, M), dtype=torch.float32, device=bits.device)
+    nat.qtcq_decode_matvec_mfma_presplit(bits.data_ptr(), M, N, L, k, _code(code), tailbiting,
+                                         split.data_ptr(), split.numel() * split.element_size(),
+                                         batch, y.data_ptr(), _stream())
+    return y

@@ -333,25 +333,39 @@ qtcq_status matvec_dispatch_code(int code, bool tb, const uint32_t* bits, int M,
               : matvec_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, st);
 }
 
-// the same product with the decoded weights and the split x on the matrix cores
+// the split x of the matrix-core product: fragments, then block scales, in the workspace
+uint4* split_frags(void* ws) { return static_cast<uint4*>(ws); }
+float* split_scales(void* ws, int N, int batch)
+{
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + (size_t)MatvecMfmaShape::kblocks(N) *
+                                    MatvecMfmaShape::frags(batch) * MatvecMfmaShape::kBlockBytes);
+}
+
+qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream_t st)
+{
+    const int nkb = MatvecMfmaShape::kblocks(N);
+    if (nkb == 0) return QTCQ_OK;
+    const int threads = nkb * MatvecMfmaShape::frags(batch) * 64;
+    const int bs = MatvecMfmaShape::kSplitBlock;
+    hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, st,
+                       x, N, nkb, batch, split_frags(ws), split_scales(ws, N, batch));
+    return launch_status();
+}
+
+// the same product with the decoded weights and the split x on the matrix cores; x ==
+// nullptr: the workspace already holds the split of this (N, batch)
 template <int L, int CODE, bool TB>
 qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x, int batch,
                              float* y, void* workspace, hipStream_t st)
 {
     static_assert(MatvecMfmaShape::stream_words<L, TB>() == (TB ? 16 : 17), "stream words");
-    const int nkb = MatvecMfmaShape::kblocks(N);
     const int nf = MatvecMfmaShape::frags(batch);
-    uint4* xs = static_cast<uint4*>(workspace);
-    float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         (size_t)nkb * nf * MatvecMfmaShape::kBlockBytes);
-    if (nkb > 0) {
-        const int threads = nkb * nf * 64;
-        const int bs = MatvecMfmaShape::kSplitBlock;
-        hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, st,
-                           x, N, nkb, batch, xs, sc);
-        qtcq_status rc = launch_status();
+    if (x) {
+        const qtcq_status rc = split_x_launch(x, N, batch, workspace, st);
         if (rc != QTCQ_OK) return rc;
     }
+    const uint4* xs = split_frags(workspace);
+    const float* sc = split_scales(workspace, N, batch);
     // Two bands per workgroup once the batch spans three or four fragments (reading the
     // split x then dominates: each fragment costs a kilobyte per k-block and wave) and
     // M / 16 >= 1024, so the grid keeps >= 512 workgroups (two per CU).  Results do not
@@ -359,10 +373,8 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
     const int nb = M / 16;
     const bool two = nf >= 3 && nb >= 1024;
     const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
-    const uint4* cxs = xs;
-    const float* csc = sc;
 #define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \
-                                               bits, M, N, cxs, csc, batch, y)
+                                               bits, M, N, xs, sc, batch, y)
     switch (nf) {
     case 1: QTCQ_MV(1, 1, grid1); break;
     case 2: if (two) QTCQ_MV(2, 2, grid2); else QTCQ_MV(2, 1, grid1); break;
@@ -607,6 +619,34 @@ qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, i
         return QTCQ_ERR_WORKSPACE;
     return by_L<MatvecMfmaF>(L, code, tailbiting != 0, bits, M, N, x, batch, y, workspace,
                              as_stream(stream));
+}
+
+qtcq_status qtcq_matvec_mfma_split_x(const float* x, int N, int batch, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    if (N < 0 || (N % 16) != 0 || batch < 0) return QTCQ_ERR_INVALID_ARG;
+    if (batch > MatvecMfmaShape::kMaxBatch || N > MatvecMfmaShape::kMaxN) return QTCQ_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < MatvecMfmaShape::workspace_bytes(N))
+        return QTCQ_ERR_WORKSPACE;
+    if (batch == 0 || N == 0) return QTCQ_OK;
+    if (!x || !aligned16(x)) return QTCQ_ERR_INVALID_ARG;
+    return split_x_launch(x, N, batch, workspace, as_stream(stream));
+}
+
+qtcq_status qtcq_decode_matvec_mfma_presplit(const uint32_t* bits, int M, int N, int L, int k,
+                                             int code, int tailbiting, const void* split,
+                                             size_t split_bytes, int batch, float* y,
+                                             void* stream)
+{
+    if (M < 0 || N < 0 || (M % 16) != 0 || (N % 16) != 0 || batch < 0) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k) || !valid_code(code)) return QTCQ_ERR_UNSUPPORTED;
+    if (batch > MatvecMfmaShape::kMaxBatch || N > MatvecMfmaShape::kMaxN) return QTCQ_ERR_UNSUPPORTED;
+    if (!split || !aligned16(split) || split_bytes < MatvecMfmaShape::workspace_bytes(N))
+        return QTCQ_ERR_WORKSPACE;
+    if (M == 0 || batch == 0) return QTCQ_OK;
+    if (!y || (N > 0 && !bits)) return QTCQ_ERR_INVALID_ARG;
+    return by_L<MatvecMfmaF>(L, code, tailbiting != 0, bits, M, N, (const float*)nullptr, batch, y,
+                             const_cast<void*>(split), as_stream(stream));
 }
 
 }  // extern "C"
