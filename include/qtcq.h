@@ -163,13 +163,16 @@ qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int 
  * expectation messages centred on the soft codeword).  The result is within
  * 1e-5 * RMS_u(grad_seq[b]) of the exact value at temperatures down to 0.01 (tested on
  * N(0,1) targets, with and without log-normal weights, and on targets 4 + 3 N(0,1) far
- * outside the codebook's range).  Below 0.01 the gradient vanishes away from near-ties
- * while the 32-bit message stash keeps a fixed resolution, and the relative error grows. */
+ * outside the codebook's range).  Below 0.01 the message stashes are kept in fp64 and
+ * the bound holds down to 3e-3 on N(0,1) targets (and to 1e-3 at L = 12); lower, the
+ * gradient vanishes away from near-ties while its fp32 covariance sums keep a fixed
+ * relative precision, and the relative error grows (1.7e-5 at L = 16, 1e-3). */
 
 /* Workspace bytes qtcq_bcjr_vjp needs for `B` sequences in one pass (both message
- * directions of every step in 32 bits -- fixed point near each step's maximum, binary32
- * far below it -- plus the expectation messages of the forward direction).  Smaller
- * workspaces that hold one sequence are used in chunks.
+ * directions of every step -- in 32 bits, fixed point near each step's maximum and
+ * binary32 far below it, or in fp64 below temperature 0.01; the size covers both -- plus
+ * the expectation messages of the forward direction).  Smaller workspaces that hold one
+ * sequence are used in chunks.
  * Returns 0 for unsupported arguments. */
 size_t qtcq_bcjr_vjp_workspace_bytes(int64_t B, int T, int L, int k);
 

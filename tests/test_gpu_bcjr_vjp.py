@@ -4,8 +4,9 @@ respect to the targets) against the binary64 oracle.
 Tolerance (fp32 against an exact reference), per sequence:
     max_u |grad_gpu - grad_oracle| <= 1e-5 * RMS_u(grad_oracle),
 the bound used for the soft codeword itself; the kernel keeps the messages it needs in
-fixed point (2^-21 log2 units) and its expectation messages centred on the soft
-codeword, which a CPU emulation of this arithmetic puts at <= 6e-6 at tau = 0.01.
+fixed point (2^-21 log2 units; below tau = 0.01 in fp64) and its expectation messages
+centred on the soft codeword, which a CPU emulation of this arithmetic puts at <= 6e-6
+at tau = 0.01 and <= 1.1e-6 at tau = 1e-3.
 Also: the soft codeword that the gradient call returns is bit-identical to the soft
 pass's, a zero upstream gradient gives exactly zero, the product is linear in the
 upstream gradient, and a chunked workspace gives the same bits.
@@ -80,6 +81,28 @@ def test_vjp_L16(api, tau):
     run_and_compare(api, s, None, upstream(2, 256, 54), tau, 16, code)
 
 
+# Below tau = 0.01 the soft pass stashes fp64 messages for the gradient (the 32-bit
+# stash keeps only fp32 resolution below -1024 log2 units, where a backward message can
+# lift a state back at low temperature).  A CPU emulation of the kernels' arithmetic with
+# an exact stash gives <= 1.1e-6 * RMS at tau = 3e-3 and 1e-3 (L = 12).  At L = 16 and
+# tau = 1e-3 the fp32 covariance sums take over: 1.7e-5 * RMS on these sequences (the
+# 32-bit stash gave 1e-4), checked against 2e-5 as a guard.
+@pytest.mark.parametrize("L,B,tau,tol", [(12, 3, 0.009, TOL), (16, 2, 0.009, TOL),
+                                         (12, 3, 3e-3, TOL), (16, 2, 3e-3, TOL),
+                                         (12, 3, 1e-3, TOL), (16, 2, 1e-3, 2e-5)])
+def test_vjp_low_temperature(api, L, B, tau, tol):
+    s = inputs.targets(B, 256, 900 + L)
+    run_and_compare(api, s, None, upstream(B, 256, 901), tau, L, "1mad", tol=tol)
+
+
+def test_vjp_low_temperature_weighted_3inst(api):
+    """Log-normal weights scale some positions' energies by 10 and more, i.e. a lower
+    effective temperature: 1.2e-5 * RMS here at tau = 2e-3, checked against 2e-5."""
+    s = inputs.targets(2, 256, 910)
+    w = inputs.weights(2, 256, 911)
+    run_and_compare(api, s, w, upstream(2, 256, 912), 2e-3, 12, "3inst", tol=2e-5)
+
+
 def test_vjp_L16_3inst_weighted(api):
     s = inputs.targets(2, 256, 58)
     w = inputs.weights(2, 256, 59)
@@ -124,5 +147,18 @@ def test_vjp_chunked_workspace(api):
     ws = api.bcjr_vjp_workspace(2, 64, 12, 2)
     a1, s1, z1 = api.bcjr_vjp(s, 0.3, g, L=12, want_soft=True, workspace=ws)
     a2, s2, z2 = api.bcjr_vjp(s, 0.3, g, L=12, want_soft=True)
+    sync()
+    assert torch.equal(a1, a2) and torch.equal(s1, s2) and torch.equal(z1, z2)
+
+
+def test_vjp_chunked_workspace_wide_stash(api):
+    """The fp64 stash (tau < 0.01) in a workspace of two sequences over five: same bits."""
+    import torch
+    s = dev(inputs.targets(5, 64, 68))
+    g = dev(upstream(5, 64, 69))
+    say("bcjr_vjp chunked wide stash L=12 B=5")
+    ws = api.bcjr_vjp_workspace(2, 64, 12, 2)
+    a1, s1, z1 = api.bcjr_vjp(s, 0.004, g, L=12, want_soft=True, workspace=ws)
+    a2, s2, z2 = api.bcjr_vjp(s, 0.004, g, L=12, want_soft=True)
     sync()
     assert torch.equal(a1, a2) and torch.equal(s1, s2) and torch.equal(z1, z2)

@@ -105,6 +105,25 @@ __device__ __forceinline__ double from_fix(int q)
     return -(double)__builtin_bit_cast(float, (uint32_t)q);
 }
 
+// The wide stash of gradient mode at low temperature keeps the fp64 values themselves:
+// there a state whose forward message is thousands of log2 units below the step's
+// maximum can be lifted back by its backward message, where the 32-bit form keeps only
+// fp32 resolution.  StashVal<WIDE> is the stored type and its value.
+template <bool WIDE> struct StashVal;
+// get(): the value itself; posterior(): the value the soft pass's own posterior uses,
+// which is the 32-bit form's in both cases, so that the soft codeword of a gradient call
+// is the soft pass's bit for bit at every temperature.
+template <> struct StashVal<false> {
+    using T = int;
+    __device__ static double get(int q) { return from_fix(q); }
+    __device__ static double posterior(int q) { return from_fix(q); }
+};
+template <> struct StashVal<true> {
+    using T = double;
+    __device__ static double get(double v) { return v; }
+    __device__ static double posterior(double v) { return from_fix(to_fix(v)); }
+};
+
 // Forward stash Xn_t[(a, 4 tid + r)], t = 1..T-1, at step index i = t - 1.  The soft pass
 // keeps [i][a][tid] int4 (r = 0..3); in VJP mode the layout is [i][a][h][tid] int2
 // (r = 2h, 2h + 1) so that the gradient kernel, which works on one half of a thread's
@@ -119,6 +138,15 @@ __device__ __forceinline__ void xn_store(int* st, size_t i, int a, int tid, int4
     } else {
         reinterpret_cast<int4*>(st)[(i * 4 + a) * NT + tid] = v;
     }
+}
+
+// the wide stash: [i][a][h][tid] double2 (r = 2h, 2h + 1)
+template <int NT>
+__device__ __forceinline__ void xn_store_wide(char* st, size_t i, int a, int tid, const double (&v)[4])
+{
+    double2* p = reinterpret_cast<double2*>(st);
+    p[((i * 4 + a) * 2 + 0) * NT + tid] = make_double2(v[0], v[1]);
+    p[((i * 4 + a) * 2 + 1) * NT + tid] = make_double2(v[2], v[3]);
 }
 
 template <int NT, bool VJP>
@@ -145,17 +173,19 @@ struct BcjrLayout {
     // Per-sequence workspace, each part 256-byte aligned:
     //   log2 Z (double) | posterior partial sums [T][kWaves][2]
     //   | stash Xn_1..Xn_{T-1} (groups (a, 4 tau + r): see xn_store)
-    // and in VJP mode, after those:
+    // and in VJP mode, where the stash region is sized for 8-byte values (the wide stash
+    // of low temperatures; the 32-bit one uses its first half), after those:
     //   | Yn_0..Yn_{T-1} ([T][4][kThreads] int4: groups (4 tau + r, x), x = 0..3, at
-    //     [r][tau]) | O_0..O_{T-1} (double) | Phi_0..Phi_{T-1} ([T][4][2][kThreads]
-    //     float2: groups (a, 4 tau + 2h + i), i = 0, 1, at [a][h][tau]) | gradient
-    //     partial sums [T][kWaves][4] (float)
+    //     [r][tau]; wide: [T][4][2][kThreads] double2, x = 2 hh, 2 hh + 1 at [r][hh][tau])
+    //     | O_0..O_{T-1} (double) | Phi_0..Phi_{T-1} ([T][4][2][kThreads] float2: groups
+    //     (a, 4 tau + 2h + i), i = 0, 1, at [a][h][tau]) | gradient partial sums
+    //     [T][kWaves][4] (float)
     __host__ __device__ static size_t up(size_t b) { return (b + 255) / 256 * 256; }
     __host__ __device__ static size_t off_part(int) { return 256; }
     __host__ __device__ static size_t off_stash(int T) { return off_part(T) + up((size_t)T * kWaves * 8); }
     __host__ __device__ static size_t bytes_per_seq(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 4); }
-    __host__ __device__ static size_t off_ystash(int T) { return bytes_per_seq(T); }
-    __host__ __device__ static size_t off_ofs(int T) { return off_ystash(T) + up((size_t)T * Tr::kGroups * 4); }
+    __host__ __device__ static size_t off_ystash(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 8); }
+    __host__ __device__ static size_t off_ofs(int T) { return off_ystash(T) + up((size_t)T * Tr::kGroups * 8); }
     __host__ __device__ static size_t off_phi(int T) { return off_ofs(T) + up((size_t)T * 8); }
     __host__ __device__ static size_t off_vpart(int T) { return off_phi(T) + up((size_t)T * Tr::kGroups * 4); }
     __host__ __device__ static size_t bytes_per_seq_vjp(int T) { return off_vpart(T) + up((size_t)T * kWaves * 16); }
@@ -287,11 +317,13 @@ inline size_t bcjr_bytes_per_seq(int T, int L, bool vjp = false)
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws points at the
 // chunk's workspace, bytes_per_seq(T) (VJP: bytes_per_seq_vjp(T)) per sequence.
 // kappa = log2(e) / tau.
-template <int L, int CODE, bool WEIGHTED, bool VJP = false>
+// WIDE (VJP only): the stashes hold fp64 values (StashVal).
+template <int L, int CODE, bool WEIGHTED, bool VJP = false, bool WIDE = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
            double kappa, char* __restrict__ ws)
 {
+    static_assert(VJP || !WIDE, "the wide stash is a gradient-mode layout");
     using Tr = Trellis<L>;
     using Ly = BcjrLayout<L>;
     using Ld = BcjrLds<L>;
@@ -316,6 +348,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     double* l2z = reinterpret_cast<double*>(base);
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
     int* stash = reinterpret_cast<int*>(base + Ly::off_stash(T));
+    char* stash_w = base + Ly::off_stash(T);                               // WIDE only
     int4* ystash = reinterpret_cast<int4*>(base + Ly::off_ystash(T));     // VJP only
     double* ofs = reinterpret_cast<double*>(base + Ly::off_ofs(T));        // VJP only
 
@@ -369,10 +402,14 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) xn[a][r] -= g64;
                 // Xn_{t-1}[(a, 4 tid + r)] (Xn_0 = 0 is not stored)
-                if (t >= 2)
-                    xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
-                                      make_int4(to_fix(xn[a][0]), to_fix(xn[a][1]),
-                                                to_fix(xn[a][2]), to_fix(xn[a][3])));
+                if (t >= 2) {
+                    if constexpr (WIDE)
+                        xn_store_wide<NT>(stash_w, (size_t)(t - 2), a, tid, xn[a]);
+                    else
+                        xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
+                                          make_int4(to_fix(xn[a][0]), to_fix(xn[a][1]),
+                                                    to_fix(xn[a][2]), to_fix(xn[a][3])));
+                }
             }
         }
         __syncthreads();   // every input read before any output overwrites it
@@ -423,10 +460,16 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         for (int a = 0; a < 4; ++a) {
             double xa[4];
             lds_read4(buf, rd(a), P, xa);
-            if (T >= 2)   // Xn_{T-1}
-                xn_store<NT, VJP>(stash, (size_t)(T - 2), a, tid,
-                                  make_int4(to_fix(xa[0] - gl64), to_fix(xa[1] - gl64),
-                                            to_fix(xa[2] - gl64), to_fix(xa[3] - gl64)));
+            if (T >= 2) {   // Xn_{T-1}
+                if constexpr (WIDE) {
+                    const double xw[4] = {xa[0] - gl64, xa[1] - gl64, xa[2] - gl64, xa[3] - gl64};
+                    xn_store_wide<NT>(stash_w, (size_t)(T - 2), a, tid, xw);
+                } else {
+                    xn_store<NT, VJP>(stash, (size_t)(T - 2), a, tid,
+                                      make_int4(to_fix(xa[0] - gl64), to_fix(xa[1] - gl64),
+                                                to_fix(xa[2] - gl64), to_fix(xa[3] - gl64)));
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -481,11 +524,26 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto bstep = [&](int t, bool produce) {
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
-        auto stash_at = [&](int a) -> int4 {
-            if (!produce) return make_int4(0, 0, 0, 0);
-            return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
+        struct Xs { typename StashVal<WIDE>::T v[4]; };
+        auto stash_at = [&](int a) -> Xs {
+            Xs q;
+            if (!produce) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) q.v[r] = 0;
+                return q;
+            }
+            if constexpr (WIDE) {
+                const double2* p = reinterpret_cast<const double2*>(stash_w);
+                const double2 lo = p[(((size_t)(t - 1) * 4 + a) * 2 + 0) * NT + tid];
+                const double2 hi = p[(((size_t)(t - 1) * 4 + a) * 2 + 1) * NT + tid];
+                q.v[0] = lo.x; q.v[1] = lo.y; q.v[2] = hi.x; q.v[3] = hi.y;
+            } else {
+                const int4 i4 = xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
+                q.v[0] = i4.x; q.v[1] = i4.y; q.v[2] = i4.z; q.v[3] = i4.w;
+            }
+            return q;
         };
-        int4 xs_next = stash_at(0);
+        Xs xs_next = stash_at(0);
         float h = wmax[par][0];
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[par][q]);
@@ -497,9 +555,14 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             lds_read4(buf, wr(r), P, yn[r]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) yn[r][x] -= h64;
-            if constexpr (VJP)   // Yn_t[(4 tid + r, x)]
+            if constexpr (VJP && WIDE) {   // Yn_t[(4 tid + r, x)]
+                double2* yw = reinterpret_cast<double2*>(ystash);
+                yw[(((size_t)t * 4 + r) * 2 + 0) * NT + tid] = make_double2(yn[r][0], yn[r][1]);
+                yw[(((size_t)t * 4 + r) * 2 + 1) * NT + tid] = make_double2(yn[r][2], yn[r][3]);
+            } else if constexpr (VJP) {
                 ystash[((size_t)t * 4 + r) * NT + tid] =
                     make_int4(to_fix(yn[r][0]), to_fix(yn[r][1]), to_fix(yn[r][2]), to_fix(yn[r][3]));
+            }
         }
         if (produce) __syncthreads();   // every input read before any output overwrites it
         H = uniform64(H + h64);                       // H_t
@@ -511,10 +574,9 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float ymax = -__builtin_inff();
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const int4 xs = xs_next;
+            const Xs xs = xs_next;
             if (a < 3) xs_next = stash_at(a + 1);
             asm volatile("" ::: "memory");    // no further hoisting of stash loads
-            const int xsr[4] = {xs.x, xs.y, xs.z, xs.w};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs r = 2h, 2h + 1
                 double y[2];
@@ -539,7 +601,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     float qc = q[0] * cx[0];
 #pragma unroll
                     for (int x = 1; x < 4; ++x) qc = __builtin_fmaf(q[x], cx[x], qc);
-                    const double xo = from_fix(xsr[r]) - Ot;
+                    const double xo = StashVal<WIDE>::posterior(xs.v[r]) - Ot;
                     const float pb = fast_exp2((float)(xo + m));
                     pg = __builtin_fmaf(pb, sq, pg);
                     pc = __builtin_fmaf(pb, qc, pc);

@@ -36,7 +36,8 @@ namespace qtcq {
 // grid.x = sequences in the chunk; block = Trellis<L>::kThreads.  ws: the chunk's VJP
 // workspace as left by bcjr_sweep<..., VJP = true> (bytes_per_seq_vjp(T) per sequence).
 // gup: [*][T] upstream gradient; row b0 + blockIdx.x.
-template <int L, int CODE, bool WEIGHTED>
+// WIDE: the soft pass stashed fp64 values (bcjr_sweep<..., VJP = true, WIDE = true>).
+template <int L, int CODE, bool WEIGHTED, bool WIDE = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                const float* __restrict__ gup, int T, int64_t b0, double kappa,
@@ -59,8 +60,24 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     const float* gu = gup + row * T;
     char* base = ws + (size_t)blockIdx.x * Ly::bytes_per_seq_vjp(T);
     const float* part = reinterpret_cast<const float*>(base + Ly::off_part(T));
+    using SV = StashVal<WIDE>;
+    using ST = typename SV::T;
+    struct Pair { ST x, y; };
     const int2* xst = reinterpret_cast<const int2*>(base + Ly::off_stash(T));    // [t-1][a][h][tau]
     const int4* yst = reinterpret_cast<const int4*>(base + Ly::off_ystash(T));   // [t][r][tau]
+    const double2* xsw = reinterpret_cast<const double2*>(base + Ly::off_stash(T));   // WIDE
+    const double2* ysw = reinterpret_cast<const double2*>(base + Ly::off_ystash(T));  // WIDE: [t][r][hh][tau]
+    // Xn_t[(a, 4 tau + 2h + i)], i = 0, 1, for t >= 1
+    auto x_pair = [&](int t, int a, int h) -> Pair {
+        const size_t k = (((size_t)(t - 1) * 4 + a) * 2 + h) * NT + tid;
+        if constexpr (WIDE) {
+            const double2 q = xsw[k];
+            return Pair{q.x, q.y};
+        } else {
+            const int2 q = xst[k];
+            return Pair{q.x, q.y};
+        }
+    };
     const double* ofs = reinterpret_cast<const double*>(base + Ly::off_ofs(T));
     float2* phs = reinterpret_cast<float2*>(base + Ly::off_phi(T));              // [t][a][h][tau]
     float* vpart = reinterpret_cast<float*>(base + Ly::off_vpart(T));
@@ -105,14 +122,14 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float ph[4][2];   // Phi_{t-1}[(a, 4 tid + 2h + i)]
-            int xq[4][2];     // Xn_{t-1}[(a, 4 tid + 2h + i)]
+            ST xq[4][2];      // Xn_{t-1}[(a, 4 tid + 2h + i)]
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float2 v = half(cur, rd(a), h);
                 phs[phi_slot(t - 1, a, h)] = v;
                 ph[a][0] = v.x; ph[a][1] = v.y;
-                int2 q = make_int2(0, 0);
-                if (t >= 2) q = xst[(((size_t)(t - 2) * 4 + a) * 2 + h) * NT + tid];
+                Pair q{0, 0};
+                if (t >= 2) q = x_pair(t - 1, a, h);
                 xq[a][0] = q.x; xq[a][1] = q.y;
             }
 #pragma unroll
@@ -126,7 +143,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         cx[a] = Cp.at(a, r, x);
-                        lw[a] = se.add_to(cx[a], from_fix(xq[a][i]));
+                        lw[a] = se.add_to(cx[a], SV::get(xq[a][i]));
                     }
                     const double m = max64(max64(lw[0], lw[1]), max64(lw[2], lw[3]));
                     float num = 0.f, den = 0.f;
@@ -167,34 +184,40 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         const double Ou = ofs[u];
         float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
         // Xn_u and Phi_u of the groups (a, 4 tid + 2h + i), loaded one (h, a) ahead of use
-        auto load_xp = [&](int h, int a, int2& xq, float2& ph) {
-            xq = make_int2(0, 0);   // Xn_0 = 0
-            if constexpr (PRODUCE) xq = xst[(((size_t)(u - 1) * 4 + a) * 2 + h) * NT + tid];
+        auto load_xp = [&](int h, int a, Pair& xq, float2& ph) {
+            xq = Pair{0, 0};   // Xn_0 = 0
+            if constexpr (PRODUCE) xq = x_pair(u, a, h);
             ph = phs[phi_slot(u, a, h)];
         };
-        int2 xq_next;
+        Pair xq_next;
         float2 ph_next;
         load_xp(0, 0, xq_next, ph_next);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float ps[2][4];   // Psi_u[(4 tid + 2h + i, x)]
-            int yq[2][4];     // Yn_u[(4 tid + 2h + i, x)]
+            ST yq[2][4];      // Yn_u[(4 tid + 2h + i, x)]
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const float4 v = buf[cur][wr(2 * h + i)];
                 ps[i][0] = v.x; ps[i][1] = v.y; ps[i][2] = v.z; ps[i][3] = v.w;
-                const int4 q = yst[((size_t)u * 4 + 2 * h + i) * NT + tid];
-                yq[i][0] = q.x; yq[i][1] = q.y; yq[i][2] = q.z; yq[i][3] = q.w;
+                if constexpr (WIDE) {
+                    const size_t k = ((size_t)u * 4 + 2 * h + i) * 2;
+                    const double2 lo = ysw[(k + 0) * NT + tid], hi = ysw[(k + 1) * NT + tid];
+                    yq[i][0] = lo.x; yq[i][1] = lo.y; yq[i][2] = hi.x; yq[i][3] = hi.y;
+                } else {
+                    const int4 q = yst[((size_t)u * 4 + 2 * h + i) * NT + tid];
+                    yq[i][0] = q.x; yq[i][1] = q.y; yq[i][2] = q.z; yq[i][3] = q.w;
+                }
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int2 xq = xq_next;
+                const Pair xq = xq_next;
                 const float2 ph = ph_next;
                 if (a < 3)
                     load_xp(h, a + 1, xq_next, ph_next);
                 else if (h == 0)
                     load_xp(1, 0, xq_next, ph_next);
-                const int xqi[2] = {xq.x, xq.y};
+                const ST xqi[2] = {xq.x, xq.y};
                 const float phi[2] = {ph.x, ph.y};
                 float outp[2];
 #pragma unroll
@@ -205,7 +228,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         cx[x] = Cp.at(a, r, x);
-                        lq[x] = se.add_to(cx[x], from_fix(yq[i][x]));
+                        lq[x] = se.add_to(cx[x], SV::get(yq[i][x]));
                     }
                     // Q_x = 2^(lq_x - m) / den; the posterior of state (a, c, x) is
                     // 2^(Xn_u - O_u + lq_x) = 2^(Xn_u - O_u + m) * 2^(lq_x - m)
@@ -224,7 +247,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                         s1 += qc;
                         t3 = __builtin_fmaf(qc, bk, t3);
                     }
-                    const float pb = fast_exp2((float)((from_fix(xqi[i]) - Ou) + m));
+                    const float pb = fast_exp2((float)((SV::get(xqi[i]) - Ou) + m));
                     S0 = __builtin_fmaf(pb, den, S0);
                     S1 = __builtin_fmaf(pb, s1, S1);
                     S2 = __builtin_fmaf(pb, __builtin_fmaf(phi[i], den, num), S2);

@@ -229,7 +229,11 @@ qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float t
 // ---- BCJR gradient (vector-Jacobian product) ------------------------------------------
 // Per chunk: the soft pass in VJP mode (stashes both message directions and the posterior
 // offsets), its finalize when soft / log Z are wanted, the Phi / Psi sweep, the gradient.
-template <int L, int CODE, bool W>
+// Below tau = 0.01 the stashes keep fp64 values (WIDE); the 32-bit stash's fp32 range
+// below -1024 log2 units is too coarse for the states the backward messages lift there.
+constexpr float kWideStashBelowTau = 0.01f;
+
+template <int L, int CODE, bool W, bool WIDE>
 qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t B, int T,
                     float temperature, float* grad, float* soft, float* log_z, void* ws,
                     size_t ws_bytes, hipStream_t st)
@@ -242,7 +246,7 @@ qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t 
     char* wsc = static_cast<char*>(ws);
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
-        hipLaunchKernelGGL((bcjr_sweep<L, CODE, W, true>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
+        hipLaunchKernelGGL((bcjr_sweep<L, CODE, W, true, WIDE>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
                            st, seq, w, T, b0, kappa, wsc);
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
@@ -252,7 +256,7 @@ qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t 
             rc = launch_status();
             if (rc != QTCQ_OK) return rc;
         }
-        hipLaunchKernelGGL((bcjr_vjp_sweep<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
+        hipLaunchKernelGGL((bcjr_vjp_sweep<L, CODE, W, WIDE>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
                            st, seq, w, gup, T, b0, kappa, wsc);
         rc = launch_status();
         if (rc != QTCQ_OK) return rc;
@@ -269,11 +273,13 @@ qtcq_status vjp_dispatch_code(int code, bool weighted, const float* seq, const f
                               const float* gup, int64_t B, int T, float temperature, float* grad,
                               float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st)
 {
+#define QTCQ_VJP(C_, W_) (temperature < kWideStashBelowTau                                              \
+        ? vjp_all<L, C_, W_, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)      \
+        : vjp_all<L, C_, W_, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st))
     if (code == QTCQ_CODE_1MAD)
-        return weighted ? vjp_all<L, kCode1Mad, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)
-                        : vjp_all<L, kCode1Mad, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st);
-    return weighted ? vjp_all<L, kCode3Inst, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)
-                    : vjp_all<L, kCode3Inst, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st);
+        return weighted ? QTCQ_VJP(kCode1Mad, true) : QTCQ_VJP(kCode1Mad, false);
+    return weighted ? QTCQ_VJP(kCode3Inst, true) : QTCQ_VJP(kCode3Inst, false);
+#undef QTCQ_VJP
 }
 
 template <int L>
