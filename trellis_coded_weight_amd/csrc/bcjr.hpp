@@ -110,18 +110,16 @@ __device__ __forceinline__ double from_fix(int q)
 // maximum can be lifted back by its backward message, where the 32-bit form keeps only
 // fp32 resolution.  StashVal<WIDE> is the stored type and its value.
 template <bool WIDE> struct StashVal;
-// get(): the value itself; posterior(): the value the soft pass's own posterior uses,
-// which is the 32-bit form's in both cases, so that the soft codeword of a gradient call
-// is the soft pass's bit for bit at every temperature.
+// The soft pass itself always reads the 32-bit form (so the soft codeword of a gradient
+// call is the soft pass's bit for bit at every temperature); the wide copy is written
+// alongside it for the gradient sweep.
 template <> struct StashVal<false> {
     using T = int;
     __device__ static double get(int q) { return from_fix(q); }
-    __device__ static double posterior(int q) { return from_fix(q); }
 };
 template <> struct StashVal<true> {
     using T = double;
     __device__ static double get(double v) { return v; }
-    __device__ static double posterior(double v) { return from_fix(to_fix(v)); }
 };
 
 // Forward stash Xn_t[(a, 4 tid + r)], t = 1..T-1, at step index i = t - 1.  The soft pass
@@ -173,8 +171,9 @@ struct BcjrLayout {
     // Per-sequence workspace, each part 256-byte aligned:
     //   log2 Z (double) | posterior partial sums [T][kWaves][2]
     //   | stash Xn_1..Xn_{T-1} (groups (a, 4 tau + r): see xn_store)
-    // and in VJP mode, where the stash region is sized for 8-byte values (the wide stash
-    // of low temperatures; the 32-bit one uses its first half), after those:
+    // and in VJP mode, after those:
+    //   | the same Xn in fp64 (the wide stash of low temperatures: xn_store_wide; unused
+    //     otherwise)
     //   | Yn_0..Yn_{T-1} ([T][4][kThreads] int4: groups (4 tau + r, x), x = 0..3, at
     //     [r][tau]; wide: [T][4][2][kThreads] double2, x = 2 hh, 2 hh + 1 at [r][hh][tau])
     //     | O_0..O_{T-1} (double) | Phi_0..Phi_{T-1} ([T][4][2][kThreads] float2: groups
@@ -184,7 +183,8 @@ struct BcjrLayout {
     __host__ __device__ static size_t off_part(int) { return 256; }
     __host__ __device__ static size_t off_stash(int T) { return off_part(T) + up((size_t)T * kWaves * 8); }
     __host__ __device__ static size_t bytes_per_seq(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 4); }
-    __host__ __device__ static size_t off_ystash(int T) { return off_stash(T) + up((size_t)(T - 1) * Tr::kGroups * 8); }
+    __host__ __device__ static size_t off_xwide(int T) { return bytes_per_seq(T); }
+    __host__ __device__ static size_t off_ystash(int T) { return off_xwide(T) + up((size_t)(T - 1) * Tr::kGroups * 8); }
     __host__ __device__ static size_t off_ofs(int T) { return off_ystash(T) + up((size_t)T * Tr::kGroups * 8); }
     __host__ __device__ static size_t off_phi(int T) { return off_ofs(T) + up((size_t)T * 8); }
     __host__ __device__ static size_t off_vpart(int T) { return off_phi(T) + up((size_t)T * Tr::kGroups * 4); }
@@ -348,7 +348,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     double* l2z = reinterpret_cast<double*>(base);
     float* part = reinterpret_cast<float*>(base + Ly::off_part(T));
     int* stash = reinterpret_cast<int*>(base + Ly::off_stash(T));
-    char* stash_w = base + Ly::off_stash(T);                               // WIDE only
+    char* stash_w = base + Ly::off_xwide(T);                               // WIDE only
     int4* ystash = reinterpret_cast<int4*>(base + Ly::off_ystash(T));     // VJP only
     double* ofs = reinterpret_cast<double*>(base + Ly::off_ofs(T));        // VJP only
 
@@ -403,12 +403,10 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 for (int r = 0; r < 4; ++r) xn[a][r] -= g64;
                 // Xn_{t-1}[(a, 4 tid + r)] (Xn_0 = 0 is not stored)
                 if (t >= 2) {
-                    if constexpr (WIDE)
-                        xn_store_wide<NT>(stash_w, (size_t)(t - 2), a, tid, xn[a]);
-                    else
-                        xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
-                                          make_int4(to_fix(xn[a][0]), to_fix(xn[a][1]),
-                                                    to_fix(xn[a][2]), to_fix(xn[a][3])));
+                    xn_store<NT, VJP>(stash, (size_t)(t - 2), a, tid,
+                                      make_int4(to_fix(xn[a][0]), to_fix(xn[a][1]),
+                                                to_fix(xn[a][2]), to_fix(xn[a][3])));
+                    if constexpr (WIDE) xn_store_wide<NT>(stash_w, (size_t)(t - 2), a, tid, xn[a]);
                 }
             }
         }
@@ -461,14 +459,10 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             double xa[4];
             lds_read4(buf, rd(a), P, xa);
             if (T >= 2) {   // Xn_{T-1}
-                if constexpr (WIDE) {
-                    const double xw[4] = {xa[0] - gl64, xa[1] - gl64, xa[2] - gl64, xa[3] - gl64};
-                    xn_store_wide<NT>(stash_w, (size_t)(T - 2), a, tid, xw);
-                } else {
-                    xn_store<NT, VJP>(stash, (size_t)(T - 2), a, tid,
-                                      make_int4(to_fix(xa[0] - gl64), to_fix(xa[1] - gl64),
-                                                to_fix(xa[2] - gl64), to_fix(xa[3] - gl64)));
-                }
+                const double xw[4] = {xa[0] - gl64, xa[1] - gl64, xa[2] - gl64, xa[3] - gl64};
+                xn_store<NT, VJP>(stash, (size_t)(T - 2), a, tid,
+                                  make_int4(to_fix(xw[0]), to_fix(xw[1]), to_fix(xw[2]), to_fix(xw[3])));
+                if constexpr (WIDE) xn_store_wide<NT>(stash_w, (size_t)(T - 2), a, tid, xw);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -524,26 +518,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto bstep = [&](int t, bool produce) {
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
-        struct Xs { typename StashVal<WIDE>::T v[4]; };
-        auto stash_at = [&](int a) -> Xs {
-            Xs q;
-            if (!produce) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) q.v[r] = 0;
-                return q;
-            }
-            if constexpr (WIDE) {
-                const double2* p = reinterpret_cast<const double2*>(stash_w);
-                const double2 lo = p[(((size_t)(t - 1) * 4 + a) * 2 + 0) * NT + tid];
-                const double2 hi = p[(((size_t)(t - 1) * 4 + a) * 2 + 1) * NT + tid];
-                q.v[0] = lo.x; q.v[1] = lo.y; q.v[2] = hi.x; q.v[3] = hi.y;
-            } else {
-                const int4 i4 = xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
-                q.v[0] = i4.x; q.v[1] = i4.y; q.v[2] = i4.z; q.v[3] = i4.w;
-            }
-            return q;
+        auto stash_at = [&](int a) -> int4 {
+            if (!produce) return make_int4(0, 0, 0, 0);
+            return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
         };
-        Xs xs_next = stash_at(0);
+        int4 xs_next = stash_at(0);
         float h = wmax[par][0];
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) h = __builtin_fmaxf(h, wmax[par][q]);
@@ -574,9 +553,10 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         float ymax = -__builtin_inff();
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const Xs xs = xs_next;
+            const int4 xs = xs_next;
             if (a < 3) xs_next = stash_at(a + 1);
             asm volatile("" ::: "memory");    // no further hoisting of stash loads
+            const int xsr[4] = {xs.x, xs.y, xs.z, xs.w};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {        // output pairs r = 2h, 2h + 1
                 double y[2];
@@ -601,7 +581,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     float qc = q[0] * cx[0];
 #pragma unroll
                     for (int x = 1; x < 4; ++x) qc = __builtin_fmaf(q[x], cx[x], qc);
-                    const double xo = StashVal<WIDE>::posterior(xs.v[r]) - Ot;
+                    const double xo = from_fix(xsr[r]) - Ot;
                     const float pb = fast_exp2((float)(xo + m));
                     pg = __builtin_fmaf(pb, sq, pg);
                     pc = __builtin_fmaf(pb, qc, pc);

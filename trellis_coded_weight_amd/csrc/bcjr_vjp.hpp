@@ -65,7 +65,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     struct Pair { ST x, y; };
     const int2* xst = reinterpret_cast<const int2*>(base + Ly::off_stash(T));    // [t-1][a][h][tau]
     const int4* yst = reinterpret_cast<const int4*>(base + Ly::off_ystash(T));   // [t][r][tau]
-    const double2* xsw = reinterpret_cast<const double2*>(base + Ly::off_stash(T));   // WIDE
+    const double2* xsw = reinterpret_cast<const double2*>(base + Ly::off_xwide(T));   // WIDE
     const double2* ysw = reinterpret_cast<const double2*>(base + Ly::off_ystash(T));  // WIDE: [t][r][hh][tau]
     // Xn_t[(a, 4 tau + 2h + i)], i = 0, 1, for t >= 1
     auto x_pair = [&](int t, int a, int h) -> Pair {
