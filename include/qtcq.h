@@ -165,8 +165,8 @@ qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int 
  * N(0,1) targets, with and without log-normal weights, and on targets 4 + 3 N(0,1) far
  * outside the codebook's range).  Below 0.01 the message stashes are kept in fp64 and
  * the bound holds down to 3e-3 on N(0,1) targets (and to 1e-3 at L = 12); lower, the
- * gradient vanishes away from near-ties while its fp32 covariance sums keep a fixed
- * relative precision, and the relative error grows (1.7e-5 at L = 16, 1e-3). */
+ * gradient vanishes away from near-ties while the fp32 parts of the arithmetic keep a
+ * fixed relative precision, and the relative error grows (1.7e-5 at L = 16, 1e-3). */
 
 /* Workspace bytes qtcq_bcjr_vjp needs for `B` sequences in one pass (both message
  * directions of every step -- in 32 bits, fixed point near each step's maximum and
