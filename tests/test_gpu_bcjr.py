@@ -69,6 +69,16 @@ def test_bcjr_L16(api, tau):
     run_and_compare(api, s, None, tau, 16, code)
 
 
+# Below the configurations' temperatures: the soft codeword and log Z keep the same bar
+# (measured <= 2e-6 * RMS and <= 1e-7 relative down to tau = 3e-4), although the messages
+# there carry ~1e-4 log2 of accumulated fp32 exp2/log2 rounding.
+@pytest.mark.parametrize("L", [12, 16])
+@pytest.mark.parametrize("tau", [3e-3, 1e-3, 3e-4])
+def test_bcjr_low_temperature(api, L, tau):
+    s = inputs.targets(3, 256, 920 + L)
+    run_and_compare(api, s, None, tau, L, "1mad")
+
+
 def test_bcjr_L16_3inst_weighted(api):
     s = inputs.targets(2, 256, 44)
     w = inputs.weights(2, 256, 45)
