@@ -112,3 +112,36 @@ def test_graph_decode_matvec_mfma(api):
         torch.cuda.synchronize()
         for y in out:
             assert torch.equal(y, ref), "replay %d differs from the eager call" % rep
+
+
+def test_graph_matvec_mfma_split_once_wide_batch(api):
+    """One split and three products of 32 rows (four fragments; the tall matrix runs two
+    bands per workgroup) captured together; replays equal the eager one-call products."""
+    import torch
+    N, L = 1040, 16
+    rng = np.random.default_rng(88)
+    shapes = [(16400, True), (64, False), (4096, True)]
+    mats = []
+    for M, tb in shapes:
+        W = 16 if tb else 17
+        words = rng.integers(0, 1 << 32, size=((M // 16) * (N // 16), W), dtype=np.uint32)
+        mats.append((torch.from_numpy(words.view(np.int32)).cuda(), M, tb))
+    x = dev(inputs.targets(32, N, 89))
+    ws = api.matvec_mfma_workspace(N)
+
+    def step():
+        api.matvec_mfma_split_x(x, workspace=ws)
+        return [api.decode_matvec_mfma_presplit(b, M, N, ws, 32, L=L, tailbiting=tb)
+                for b, M, tb in mats]
+
+    say("graph: split + 3 x decode_matvec_mfma_presplit batch 32")
+    g, out = capture(step)
+    for rep in range(3):
+        x.copy_(dev(inputs.targets(32, N, 90 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        refs = [api.decode_matvec_mfma(b, M, N, x, L=L, tailbiting=tb) for b, M, tb in mats]
+        torch.cuda.synchronize()
+        for y, ref in zip(out, refs):
+            assert torch.equal(y, ref), "replay %d differs from the eager call" % rep
