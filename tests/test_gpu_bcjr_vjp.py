@@ -85,8 +85,10 @@ def test_vjp_L16(api, tau):
 # stash keeps only fp32 resolution below -1024 log2 units, where a backward message can
 # lift a state back at low temperature).  A CPU emulation of the kernels' arithmetic with
 # an exact stash gives <= 1.1e-6 * RMS at tau = 3e-3 and 1e-3 (L = 12).  At L = 16 and
-# tau = 1e-3 the GPU gives 1.7e-5 * RMS on these sequences (the 32-bit stash gave 1e-4),
-# checked against 2e-5 as a guard.
+# tau = 1e-3 the gradient of the first sequence has collapsed onto positions 0 and 1
+# (14x and 7x its RMS), so the RMS bar asks for ~1e-6 relative there; the GPU gives
+# 1.2e-6 relative on them, 1.7e-5 * RMS (the 32-bit stash gave 1e-4), checked against
+# 2e-5 as a guard.
 @pytest.mark.parametrize("L,B,tau,tol", [(12, 3, 0.009, TOL), (16, 2, 0.009, TOL),
                                          (12, 3, 3e-3, TOL), (16, 2, 3e-3, TOL),
                                          (12, 3, 1e-3, TOL), (16, 2, 1e-3, 2e-5)])
