@@ -10,8 +10,9 @@
 // makes v * r_hi exact and one FMA adds v * r_lo with a single rounding.  Over the whole
 // input domain of each code (byte sums 0..1020; every finite fp16 value below 4 in
 // magnitude) this rounds to the same binary32 value as the binary64 quotient -- checked
-// exhaustively on the host with exact rational arithmetic.  The LCG product uses 24-bit
-// multiplies (states have at most 24 bits), and v_sad_u8 forms the byte sum.
+// exhaustively on the host with exact rational arithmetic.  The LCG product uses a 24-bit
+// multiply-add and a shift-add (states have at most 24 bits), and v_sad_u8 forms the
+// byte sum.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,16 +22,18 @@ namespace qtcq {
 
 enum : int { kCode1Mad = 0, kCode3Inst = 1 };
 
-// LCG of a state x < 2^24: (34038481 x + 76625530) mod 2^32, with the multiplier split
-// as 519 * 2^16 + 25297 so that both partial products are 24-bit multiplies.
-// (Written as instructions: the compiler would fold the two products back into one
-// 32-bit v_mul_lo_u32, a multi-pass instruction.)
+// LCG of a state x < 2^24: (34038481 x + 76625530) mod 2^32.  The multiplier is
+// 2^25 + 484049, so one 24-bit multiply-add forms 484049 x + 76625530 and one shift-add
+// adds x << 25; both are exact modulo 2^32.  Both constants are VGPR operands (an SGPR
+// operand halves a VALU op's issue rate here).
+// (Written as instructions: the compiler would fold the two back into one 32-bit
+// v_mul_lo_u32, a multi-pass instruction.)
 __device__ __forceinline__ uint32_t lcg_step(uint32_t x)
 {
-    uint32_t lo, hi;
-    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(lo) : "v"(x), "s"(25297u), "v"(76625530u));
-    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(hi) : "s"(519u), "v"(x));
-    return lo + (hi << 16);
+    uint32_t lo, u;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(lo) : "v"(x), "v"(484049u), "v"(76625530u));
+    asm("v_lshl_add_u32 %0, %1, 25, %2" : "=v"(u) : "v"(x), "v"(lo));
+    return u;
 }
 
 // Binary32 split of 1/147.8 and 1/1.244 (the binary64 divisors): r_hi has 13 significant

@@ -151,34 +151,24 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t c)
     return v;
 }
 
-// lcg_step with the 519 multiplier in a VGPR
-__device__ __forceinline__ uint32_t lcg_step_v(uint32_t x, uint32_t k519)
-{
-    uint32_t lo, hi;
-    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(lo) : "v"(x), "s"(25297u), "v"(76625530u));
-    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(hi) : "v"(k519), "v"(x));
-    return lo + (hi << 16);
-}
-
 // Two windows' codes before their rescale, as one packed pair of fp16.
-//   k519: 519 in a VGPR; kbias: fp16 -1534 in both halves, in a VGPR
+//   kbias: fp16 -1534 in both halves, in a VGPR
 template <int CODE>
-__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, uint32_t k519,
-                                                      uint32_t kbias)
+__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, uint32_t kbias)
 {
     if constexpr (CODE == kCode1Mad) {
         // byte sums into both halves of an accumulator 0x64006400 (fp16 1024 twice):
         // v_sad_u8 adds S0 to the low half, v_sad_hi_u8 adds S1 << 16, so the halves read
         // 1024 + S0 and 1024 + S1 exactly (S <= 1020, no carry between them); one packed
         // fp16 subtraction of 1534 gives S - 510
-        const uint32_t t0 = __builtin_amdgcn_sad_u8(lcg_step_v(w0, k519), 0u, 0x64006400u);
-        const uint32_t t = __builtin_amdgcn_sad_hi_u8(lcg_step_v(w1, k519), 0u, t0);
+        const uint32_t t0 = __builtin_amdgcn_sad_u8(lcg_step(w0), 0u, 0x64006400u);
+        const uint32_t t = __builtin_amdgcn_sad_hi_u8(lcg_step(w1), 0u, t0);
         return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mv_half2, t) + __builtin_bit_cast(mv_half2, kbias));
     } else {
         // the two halves of each (u & 0x8FFF8FFF) ^ 0x3B603B60, gathered as (lo0, lo1)
         // and (hi0, hi1), added by one packed fp16 add (round to nearest even)
-        const uint32_t v0 = (lcg_step_v(w0, k519) & 0x8FFF8FFFu) ^ 0x3B603B60u;
-        const uint32_t v1 = (lcg_step_v(w1, k519) & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const uint32_t v0 = (lcg_step(w0) & 0x8FFF8FFFu) ^ 0x3B603B60u;
+        const uint32_t v1 = (lcg_step(w1) & 0x8FFF8FFFu) ^ 0x3B603B60u;
         const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
         const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
         return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mv_half2, hi) + __builtin_bit_cast(mv_half2, lo));
@@ -273,7 +263,6 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
         }
     };
     // loop-invariant operands held in VGPRs (an SGPR operand halves a VALU op's issue rate)
-    const uint32_t k519 = vgpr_u32(519u);
     const uint32_t kbias = vgpr_u32(0xE5FEE5FEu);   // fp16 -1534 in both halves
     // Each MFMA's result, times its block's 2^-s (exact), is added to the accumulators
     // by FMA, in k-block order (DEFER: one k-block later, so its latency hides behind the
@@ -307,7 +296,7 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
             for (int p = 0; p < 4; ++p) {
                 const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
                 const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
-                a[p] = code_raw_pair_f16<CODE>(w0, w1, k519, kbias);
+                a[p] = code_raw_pair_f16<CODE>(w0, w1, kbias);
             }
             av[b] = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         }
