@@ -141,3 +141,100 @@ def test_high_temperature_uniform_covariance():
     cov1 = np.mean([(C[x] - mean) @ (C[((x << k) | b) & (N - 1)] - mean) / N
                     for b in range(1 << k)])
     assert np.allclose(np.diag(K, 1), cov1, rtol=1e-4, atol=1e-5 * var)
+
+
+# ---- low temperatures: the range where the GPU gradient is compared with this oracle --
+# At tau <= 0.01 the walk distribution concentrates on a few walks and the covariance is
+# a small difference of large products; these pins check the expectation-message form
+# there against the explicit enumeration (both codes, weighted and unweighted) and
+# against differences of the separately pinned soft codeword.
+
+@pytest.mark.parametrize("tau", [0.01, 3e-3, 1e-3])
+@pytest.mark.parametrize("T", [2, 4, 6])
+@pytest.mark.parametrize("code", ["1mad", "3inst"])
+def test_bruteforce_L6_low_temperature(code, T, tau):
+    L, k = 6, 2
+    C = oracle.code_table(code, L)
+    for seed in range(3):
+        s = inputs.targets(1, T, 700 + seed)[0]
+        g = _g(T, 710 + seed)
+        grad, soft = oracle.bcjr_vjp(C, s, tau, g, L=L, k=k)
+        ref = oracle.brute_bcjr_vjp(C, s, tau, g, L=L, k=k)
+        bsoft, _ = oracle.brute_bcjr(C, s, tau, L=L, k=k)
+        scale = np.abs(ref).max() + 1e-300
+        assert np.allclose(grad, ref, rtol=1e-9, atol=1e-9 * scale), (seed, grad, ref)
+        assert np.allclose(soft, bsoft, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("tau", [0.01, 3e-3, 1e-3])
+def test_bruteforce_weighted_L6_low_temperature(tau):
+    L, k, T = 6, 2, 5
+    for code in ("1mad", "3inst"):
+        C = oracle.code_table(code, L)
+        s = inputs.targets(1, T, 720)[0]
+        w = inputs.weights(1, T, 721)[0]
+        g = _g(T, 722)
+        grad, _ = oracle.bcjr_vjp(C, s, tau, g, w, L=L, k=k)
+        ref = oracle.brute_bcjr_vjp(C, s, tau, g, w, L=L, k=k)
+        assert np.allclose(grad, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+
+def test_bruteforce_near_tie_low_temperature():
+    """Two walks a hair apart in energy: the covariance is then carried by the pair alone
+    (a two-point distribution), the case where the gradient collapses onto few entries."""
+    L, k, T, tau = 6, 2, 4, 1e-3
+    C = oracle.code_table("1mad", L)
+    # targets halfway between two code values at every step give near-ties
+    vals = np.unique(C)
+    s = np.array([(vals[20] + vals[21]) / 2, vals[30], (vals[10] + vals[11]) / 2, vals[40]],
+                 dtype=np.float32)
+    g = _g(T, 730)
+    grad, _ = oracle.bcjr_vjp(C, s, tau, g, L=L, k=k)
+    ref = oracle.brute_bcjr_vjp(C, s, tau, g, L=L, k=k)
+    assert np.abs(ref).max() > 0
+    assert np.allclose(grad, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+
+def _richardson_fd(C, s, tau, w, g, u, h, L):
+    """d(g . soft)/d s_u by central differences at h and h/2, Richardson-combined
+    (error O(h^4)); every perturbed target is exact in binary32."""
+    def cd(hh):
+        hh = np.float32(hh)
+        sp = s.copy(); sp[u] += hh
+        sm = s.copy(); sm[u] -= hh
+        assert sp[u] - s[u] == hh and s[u] - sm[u] == hh
+        fp, _ = oracle.bcjr(C, sp, tau, w, L=L, k=2)
+        fm, _ = oracle.bcjr(C, sm, tau, w, L=L, k=2)
+        return (g @ fp - g @ fm) / (2.0 * float(hh))
+    return (4.0 * cd(h / 2) - cd(h)) / 3.0
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_central_differences_low_temperature(weighted):
+    L, T, tau = 8, 16, 0.01
+    C = oracle.code_table("1mad", L)
+    s = inputs.targets(1, T, 740)[0]
+    w = inputs.weights(1, T, 741)[0] if weighted else None
+    g = _g(T, 742)
+    grad, _ = oracle.bcjr_vjp(C, s, tau, g, w, L=L, k=2)
+    scale = np.abs(grad).max()
+    for u in range(T):
+        fd = _richardson_fd(C, s, tau, w, g, u, 2.0 ** -14, L)
+        assert abs(fd - grad[u]) <= 1e-6 * scale, (u, fd, grad[u])
+
+
+def test_central_differences_tau_1e3():
+    """Targets at midpoints between neighbouring code values (near-ties at every step),
+    so that the gradient at tau = 1e-3 is carried by competing walks, not ~0."""
+    L, T, tau = 6, 10, 1e-3
+    C = oracle.code_table("3inst", L)
+    vals = np.unique(C.astype(np.float64))
+    pick = np.random.default_rng(752).integers(0, len(vals) - 1, T)
+    s = ((vals[pick] + vals[pick + 1]) / 2).astype(np.float32)
+    g = _g(T, 751)
+    grad, _ = oracle.bcjr_vjp(C, s, tau, g, L=L, k=2)
+    scale = np.abs(grad).max()
+    assert scale > 1e-3
+    for u in range(T):
+        fd = _richardson_fd(C, s, tau, None, g, u, 2.0 ** -18, L)
+        assert abs(fd - grad[u]) <= 1e-6 * scale, (u, fd, grad[u])
