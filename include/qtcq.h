@@ -144,7 +144,15 @@ qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, in
  *         messages combined in binary64, exponentials in binary32; within
  *         1e-5 * RMS_t(soft[b]) of the exact value at temperatures down to 0.01);
  *   log_z [B] float32 (or NULL): natural log of sum over walks of exp(-E / temperature).
- * temperature: finite, > 0.  As it tends to 0 soft tends to the Viterbi code.
+ * temperature: finite, > 0.  As it tends to 0 soft tends to the Viterbi code.  The
+ * forward messages are stashed in 32 bits -- fixed point (2^-21 log2 units) within 1024
+ * log2 units of each step's maximum, binary32 of the distance below that -- so the soft
+ * codeword is resolved while the messages stay within about 1e10 log2 units of their
+ * step's maximum (energy / temperature up to ~7e9 per sequence: temperatures down to
+ * 1e-9 on N(0,1) targets of 48 steps were tested); beyond that the far states' binary32
+ * precision is coarser than a posterior's exponent range and soft is unspecified (it
+ * comes out NaN), while log_z stays accurate -- the Viterbi code of qtcq_viterbi_encode
+ * is the limit there.
  * workspace: 16-byte aligned, >= qtcq_bcjr_workspace_bytes(1, T, L, k); larger
  * workspaces let more sequences run per pass.
  * Errors: as qtcq_viterbi_encode. */

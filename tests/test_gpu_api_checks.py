@@ -64,3 +64,56 @@ def test_matvec_mfma_rejects_small_workspace(api):
         api.decode_matvec_mfma(torch.zeros((16, 17), dtype=torch.int32, device=dev), 64, 64,
                                torch.zeros(64, dtype=torch.float32, device=dev), workspace=small)
     torch.cuda.synchronize()
+
+
+def test_wrappers_reject_foreign_workspaces(api):
+    """A caller-supplied workspace that is not a contiguous tensor on the current device is
+    refused before any launch (a host pointer would reach the kernels), and a workspace of
+    any dtype is measured in bytes."""
+    import torch
+    from trellis_coded_weight_amd import _native as nat
+    dev = "cuda"
+    s = torch.zeros((2, 256), dtype=torch.float32, device=dev)
+    g = torch.zeros_like(s)
+    host_ws = torch.empty(nat.qtcq_encode_workspace_bytes(2, 256, 16, 2), dtype=torch.uint8)
+    strided = torch.empty((2, nat.qtcq_encode_workspace_bytes(2, 256, 16, 2)), dtype=torch.uint8,
+                          device=dev)[:, ::2]
+    for bad in (host_ws, strided):
+        with pytest.raises(ValueError):
+            api.encode(s, workspace=bad)
+        with pytest.raises(ValueError):
+            api.tailbiting_encode(s, workspace=bad)
+        with pytest.raises(ValueError):
+            api.bcjr_soft(s, 0.1, workspace=bad)
+        with pytest.raises(ValueError):
+            api.bcjr_vjp(s, 0.1, g, workspace=bad)
+        with pytest.raises(ValueError):
+            api.decode_matvec_mfma(torch.zeros((16, 17), dtype=torch.int32, device=dev), 64, 64,
+                                   torch.zeros(64, dtype=torch.float32, device=dev), workspace=bad)
+        with pytest.raises(ValueError):
+            api.matvec_mfma_split_x(torch.zeros(64, dtype=torch.float32, device=dev), workspace=bad)
+    # a float32 workspace of the right byte size is accepted for the encode: numel * 4 bytes
+    n = nat.qtcq_encode_workspace_bytes(2, 256, 16, 2)
+    ws32 = torch.empty((n + 3) // 4, dtype=torch.float32, device=dev)
+    bits, mse, _ = api.encode(s, workspace=ws32)
+    ref_bits, ref_mse, _ = api.encode(s)
+    torch.cuda.synchronize()
+    assert torch.equal(bits, ref_bits) and torch.equal(mse, ref_mse)
+
+
+def test_presplit_checks_its_split(api):
+    """The split handle carries (N, batch): a split of another N is refused, and the
+    product takes the batch the split was made for."""
+    import torch
+    dev = "cuda"
+    x = torch.ones((8, 64), dtype=torch.float32, device=dev)
+    sp = api.matvec_mfma_split_x(x)
+    bits = torch.zeros((4 * 4, 17), dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        api.decode_matvec_mfma_presplit(torch.zeros((4 * 2, 17), dtype=torch.int32, device=dev),
+                                        64, 32, sp)
+    with pytest.raises(ValueError):
+        api.decode_matvec_mfma_presplit(bits, 64, 64, sp.workspace)
+    y = api.decode_matvec_mfma_presplit(bits, 64, 64, sp)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (8, 64)

@@ -130,8 +130,8 @@ def test_graph_matvec_mfma_split_once_wide_batch(api):
     ws = api.matvec_mfma_workspace(N)
 
     def step():
-        api.matvec_mfma_split_x(x, workspace=ws)
-        return [api.decode_matvec_mfma_presplit(b, M, N, ws, 32, L=L, tailbiting=tb)
+        sp = api.matvec_mfma_split_x(x, workspace=ws)
+        return [api.decode_matvec_mfma_presplit(b, M, N, sp, L=L, tailbiting=tb)
                 for b, M, tb in mats]
 
     say("graph: split + 3 x decode_matvec_mfma_presplit batch 32")

@@ -284,13 +284,14 @@ def test_matvec_mfma_presplit_equals_one_call(api, batch):
     x = dev(inputs.targets(batch, N, 80 + batch))
     say("matvec_mfma presplit batch=%d" % batch)
     split = api.matvec_mfma_split_x(x)
+    assert (split.N, split.batch) == (N, batch)
     sync()
-    before = split.clone()
+    before = split.workspace.clone()
     for M, code, tb, seed in [(48, "1mad", False, 1), (16400, "3inst", True, 2), (4096, "1mad", True, 3)]:
         words = random_words(M, N, 16, tb, 300 + seed)
         bd = torch.from_numpy(words.view(np.int32)).cuda()
-        y1 = api.decode_matvec_mfma_presplit(bd, M, N, split, batch, code=code, tailbiting=tb)
+        y1 = api.decode_matvec_mfma_presplit(bd, M, N, split, code=code, tailbiting=tb)
         y2 = api.decode_matvec_mfma(bd, M, N, x, code=code, tailbiting=tb)
         sync()
         assert torch.equal(y1, y2), "M=%d" % M
-    assert torch.equal(split, before)
+    assert torch.equal(split.workspace, before)

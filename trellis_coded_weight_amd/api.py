@@ -34,6 +34,15 @@ def _dev_f32(x: torch.Tensor, name: str) -> torch.Tensor:
     return x
 
 
+def _dev_workspace(ws, name: str = "workspace") -> int:
+    """A caller-supplied device scratch tensor: contiguous and on the current device (the
+    kernels write through its pointer).  Returns its size in bytes, whatever its dtype."""
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.is_contiguous()):
+        raise ValueError("%s must be a contiguous device tensor" % name)
+    _on_current_device(ws, name)
+    return ws.numel() * ws.element_size()
+
+
 def _like_seq(x: torch.Tensor | None, seq: torch.Tensor, name: str) -> None:
     """An optional per-weight tensor (error weights, upstream gradient) shaped as seq."""
     if x is not None:
@@ -120,10 +129,11 @@ def encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16, 
     states = torch.empty((B, T), dtype=torch.int32, device=seq.device) if want_states else None
     if workspace is None:
         workspace = encode_workspace(B, T, L, k)
+    ws_bytes = _dev_workspace(workspace)
     nat.qtcq_viterbi_encode(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T,
                             L, k, _code(code), bits.data_ptr(), mse.data_ptr(),
                             None if states is None else states.data_ptr(), workspace.data_ptr(),
-                            workspace.numel(), _stream())
+                            ws_bytes, _stream())
     return bits, mse, states
 
 
@@ -152,9 +162,10 @@ def bcjr_soft(seq: torch.Tensor, temperature: float, weights: torch.Tensor | Non
     logz = torch.empty(B, dtype=torch.float32, device=seq.device)
     if workspace is None:
         workspace = bcjr_workspace(B, T, L, k)
+    ws_bytes = _dev_workspace(workspace)
     nat.qtcq_bcjr_soft(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
                        _code(code), temperature, soft.data_ptr(), logz.data_ptr(),
-                       workspace.data_ptr(), workspace.numel(), _stream())
+                       workspace.data_ptr(), ws_bytes, _stream())
     return soft, logz
 
 
@@ -178,11 +189,12 @@ def bcjr_vjp(seq: torch.Tensor, temperature: float, grad_soft: torch.Tensor,
     logz = torch.empty(B, dtype=torch.float32, device=seq.device) if want_soft else None
     if workspace is None:
         workspace = bcjr_vjp_workspace(B, T, L, k)
+    ws_bytes = _dev_workspace(workspace)
     nat.qtcq_bcjr_vjp(seq.data_ptr(), None if weights is None else weights.data_ptr(), B, T, L, k,
                       _code(code), temperature, grad_soft.data_ptr(), grad.data_ptr(),
                       None if soft is None else soft.data_ptr(),
                       None if logz is None else logz.data_ptr(), workspace.data_ptr(),
-                      workspace.numel(), _stream())
+                      ws_bytes, _stream())
     return grad, soft, logz
 
 
@@ -212,10 +224,11 @@ def tailbiting_encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L:
     states = torch.empty((B, T), dtype=torch.int32, device=seq.device) if want_states else None
     if workspace is None:
         workspace = tailbiting_workspace(B, T, L, k)
+    ws_bytes = _dev_workspace(workspace)
     nat.qtcq_tailbiting_encode(seq.data_ptr(), None if weights is None else weights.data_ptr(), B,
                                T, L, k, _code(code), bits.data_ptr(), mse.data_ptr(),
                                None if states is None else states.data_ptr(),
-                               workspace.data_ptr(), workspace.numel(), _stream())
+                               workspace.data_ptr(), ws_bytes, _stream())
     return bits, mse, states
 
 
@@ -260,7 +273,7 @@ def matvec_mfma_workspace(N: int) -> torch.Tensor:
     stream)."""
     n = nat.qtcq_decode_matvec_mfma_workspace_bytes(N)
     if n == 0:
-        raise ValueError("N must be a multiple of 16 in [0, 2^24]")
+        raise ValueError("N must be a multiple of 16 in [0, 2^22]")
     return torch.empty(n, dtype=torch.uint8, device="cuda")
 
 
@@ -283,49 +296,55 @@ def decode_matvec_mfma(bits: torch.Tensor, M: int, N: int, x: torch.Tensor, L: i
     _on_current_device(bits, "bits")
     if workspace is None:
         workspace = matvec_mfma_workspace(N)
-    elif not (workspace.is_cuda and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous device tensor")
-    else:
-        _on_current_device(workspace, "workspace")
+    ws_bytes = _dev_workspace(workspace)
     y = torch.empty((x2.shape[0], M), dtype=torch.float32, device=x.device)
     nat.qtcq_decode_matvec_mfma(bits.data_ptr(), M, N, L, k, _code(code), tailbiting,
                                 x2.data_ptr(), x2.shape[0], y.data_ptr(), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream())
+                                ws_bytes, _stream())
     return y[0] if one else y
 
 
-def matvec_mfma_split_x(x: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+class SplitX:
+    """The split of x made by matvec_mfma_split_x: the device workspace holding it and the
+    (N, batch) it was made for.  The product reads the fragments and block scales at
+    offsets that depend on both, so decode_matvec_mfma_presplit checks them."""
+    __slots__ = ("workspace", "N", "batch")
+
+    def __init__(self, workspace: torch.Tensor, N: int, batch: int):
+        self.workspace, self.N, self.batch = workspace, N, batch
+
+
+def matvec_mfma_split_x(x: torch.Tensor, workspace: torch.Tensor | None = None) -> SplitX:
     """The split of x [batch][N] (or [N]) for decode_matvec_mfma_presplit, written into
-    `workspace` (matvec_mfma_workspace(N), allocated when not given), which is returned."""
+    `workspace` (matvec_mfma_workspace(N), allocated when not given)."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     _dev_f32(x2, "x")
     N = x2.shape[1]
     if workspace is None:
         workspace = matvec_mfma_workspace(N)
-    elif not (workspace.is_cuda and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous device tensor")
-    else:
-        _on_current_device(workspace, "workspace")
-    nat.qtcq_matvec_mfma_split_x(x2.data_ptr(), N, x2.shape[0], workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(), _stream())
-    return workspace
+    ws_bytes = _dev_workspace(workspace)
+    nat.qtcq_matvec_mfma_split_x(x2.data_ptr(), N, x2.shape[0], workspace.data_ptr(), ws_bytes,
+                                 _stream())
+    return SplitX(workspace, N, x2.shape[0])
 
 
-def decode_matvec_mfma_presplit(bits: torch.Tensor, M: int, N: int, split: torch.Tensor,
-                                batch: int, L: int = 16, k: int = 2, code="1mad",
+def decode_matvec_mfma_presplit(bits: torch.Tensor, M: int, N: int, split: SplitX,
+                                L: int = 16, k: int = 2, code="1mad",
                                 tailbiting: bool = False) -> torch.Tensor:
-    """y [batch][M] = W x from a split made by matvec_mfma_split_x for this N and batch
-    (equal to decode_matvec_mfma bit for bit)."""
+    """y [split.batch][M] = W x from a split made by matvec_mfma_split_x for this N (equal to
+    decode_matvec_mfma bit for bit)."""
+    if not isinstance(split, SplitX):
+        raise ValueError("split must be the SplitX that matvec_mfma_split_x returned")
+    if split.N != N:
+        raise ValueError("split was made for N = %d, not %d" % (split.N, N))
     W = tailbiting_words(L, k, 256) if tailbiting else bitstream_words(L, k, 256)
     if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
             and bits.numel() == (M // 16) * (N // 16) * W):
         raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
     _on_current_device(bits, "bits")
-    if not (split.is_cuda and split.is_contiguous()):
-        raise ValueError("split must be a contiguous device tensor")
-    _on_current_device(split, "split")
-    y = torch.empty((batch, M), dtype=torch.float32, device=bits.device)
+    sp_bytes = _dev_workspace(split.workspace, "split")
+    y = torch.empty((split.batch, M), dtype=torch.float32, device=bits.device)
     nat.qtcq_decode_matvec_mfma_presplit(bits.data_ptr(), M, N, L, k, _code(code), tailbiting,
-                                         split.data_ptr(), split.numel() * split.element_size(),
-                                         batch, y.data_ptr(), _stream())
+                                         split.workspace.data_ptr(), sp_bytes, split.batch,
+                                         y.data_ptr(), _stream())
     return y

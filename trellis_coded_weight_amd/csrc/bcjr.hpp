@@ -28,10 +28,10 @@
 // Normalisation: stored X_t = A_t - G_{t-1}; the next step subtracts g_t = max X_t
 // (from per-wave maxima) and G accumulates the g's, likewise h/H for the backward.
 // Stash: while step t + 1 reads X_t it also writes Xn_t = X_t - g_t = A_t - G_t (every
-// value <= 0 up to rounding, the maximum at 0) to HBM in 32 bits (to_fix): fixed point
-// with a uniform 2.4e-7 log2 resolution down to -1024, fp32 below.  Plain fp32 would
-// lose precision on the moderately negative values that still matter once the
-// backward message is added.
+// value <= 0, the maximum just below 0) to HBM in 32 bits (to_fix): fixed point with a
+// uniform 2.4e-7 log2 resolution down to -1024, binary32 of the distance below -1024
+// further down.  Plain fp32 would lose precision on the moderately negative values that
+// still matter once the backward message is added.
 // Posterior at t: gamma_t(j) = 2^( la_t(j) + lb_t(j) - log2 Z ), computed in the backward
 // sweep from the stashed Xn_t[(a, c)], the normalised backward input Yn_t[(c, x)] =
 // Y_t - h_t and the step energy, with the exact offset O_t = log2 Z - G_t - H_t.  The
@@ -79,6 +79,14 @@ __device__ __forceinline__ float wave_max(float x)
 }
 
 template <int WIDTH>
+__device__ __forceinline__ double wave_max64(double x)
+{
+#pragma unroll
+    for (int off = WIDTH / 2; off >= 1; off >>= 1) x = max64(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+template <int WIDTH>
 __device__ __forceinline__ float wave_sum(float x)
 {
 #pragma unroll
@@ -86,23 +94,37 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-// Stash values (normalised messages, <= 0 up to the rounding of the normaliser) in 32
-// bits: v >= -1024 as int32 units of 2^-21 log2 (codes below 2^30), v < -1024 as the
-// binary32 bit pattern of -v, whose codes are >= 0x44800000 (= 1024.0f).  Near the
-// maximum, where a posterior term depends on them, values keep a uniform 2.4e-7
-// resolution; far below it they keep fp32's relative precision, so that at low
-// temperature a state whose forward message is far below the step's maximum but whose
-// backward message lifts it still gets the right (finite) posterior exponent.
+// The smallest binary32 value above x (x itself for +inf and NaN).  The per-step
+// normalisers are binary32 maxima of fp64 messages; rounding each wave's maximum up once
+// makes the normaliser an upper bound of every message of its step, so a normalised
+// message X - g is <= 0 exactly (fp64 subtraction keeps the sign), however large |X| is.
+__host__ __device__ __forceinline__ float next_up(float x)
+{
+    if (!(x < __builtin_inff())) return x;
+    if (x == 0.0f) return __builtin_bit_cast(float, 1u);
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    return __builtin_bit_cast(float, x > 0.0f ? b + 1u : b - 1u);
+}
+
+// Stash values (normalised messages, <= 0 since the normaliser rounds up) in 32 bits:
+//   v >= -1024: int32 units of 2^-21 log2, codes in [-2^31, 0] -- a uniform 2.4e-7
+//               resolution near the step's maximum, where a posterior term depends on it;
+//   v <  -1024: the binary32 bit pattern of -1024 - v (> 0), codes in [1, 0x7F800000] --
+//               an absolute precision of 2^-24 (-1024 - v), continuous with the fixed
+//               point at the boundary and fp32's relative precision far below it.
+// Far below the maximum a state can still matter at low temperature: its backward
+// message can lift it back, so the tail keeps finite, smoothly degrading values rather
+// than a clamp.
 constexpr double kFixScale = 2097152.0;
-__device__ __forceinline__ int to_fix(double v)
+__host__ __device__ __forceinline__ int to_fix(double v)
 {
     if (v >= -1024.0) return (int)__builtin_rint(v * kFixScale);
-    return (int)__builtin_bit_cast(uint32_t, (float)(-v));
+    return (int)__builtin_bit_cast(uint32_t, (float)(-1024.0 - v));
 }
-__device__ __forceinline__ double from_fix(int q)
+__host__ __device__ __forceinline__ double from_fix(int q)
 {
-    if (q < 0x40000000) return (double)q * (1.0 / kFixScale);
-    return -(double)__builtin_bit_cast(float, (uint32_t)q);
+    if (q <= 0) return (double)q * (1.0 / kFixScale);
+    return -1024.0 - (double)__builtin_bit_cast(float, (uint32_t)q);
 }
 
 // The wide stash of gradient mode at low temperature keeps the fp64 values themselves:
@@ -334,7 +356,8 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     constexpr int P = Ld::P;
     __shared__ __align__(16) char buf[Ld::kBytes];
     __shared__ float wmax[2][kWaves];
-    __shared__ float redm[kWaves], reds[kWaves];
+    __shared__ double redm[kWaves];
+    __shared__ float reds[kWaves];
     __shared__ float gsh[kBcjrMaxT];   // the forward normalisers g_0 .. g_{T-1}
 
     const int tid = threadIdx.x;
@@ -436,7 +459,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             }
         }
         lmax = wave_max<WID>(lmax);
-        if (lane == 0) wmax[par ^ 1][wave] = lmax;
+        if (lane == 0) wmax[par ^ 1][wave] = next_up(lmax);
         par ^= 1;
         __syncthreads();
     }
@@ -470,13 +493,15 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 for (int x = 0; x < 4; ++x)
                     m = max64(m, se.add_to(Cv[a][r][x], xa[r] - gl64));
         }
-        float wm = wave_max<WID>((float)m);
+        // the exact fp64 maximum (once per sequence): a binary32-rounded one can sit
+        // hundreds of log2 units below the largest term once the messages reach ~1e10,
+        // and its power of two would overflow
+        const double wm = wave_max64<WID>(m);
         if (lane == 0) redm[wave] = wm;
         __syncthreads();
-        float bm = redm[0];
+        double bm64 = redm[0];
 #pragma unroll
-        for (int qq = 1; qq < kWaves; ++qq) bm = __builtin_fmaxf(bm, redm[qq]);
-        const double bm64 = (double)bm;
+        for (int qq = 1; qq < kWaves; ++qq) bm64 = max64(bm64, redm[qq]);
         float sum = 0.f;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -602,7 +627,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         }
         if (produce) {
             ymax = wave_max<WID>(ymax);
-            if (lane == 0) wmax[par ^ 1][wave] = ymax;
+            if (lane == 0) wmax[par ^ 1][wave] = next_up(ymax);
             par ^= 1;
             __syncthreads();
         }

@@ -1,0 +1,141 @@
+// launch_matvec.hip -- launches of the decode -> matrix-vector products (matvec.hpp,
+// matvec_mfma.hpp).
+#include "host.hpp"
+#include "codes.hpp"
+#include "matvec.hpp"
+#include "matvec_mfma.hpp"
+
+namespace qtcq {
+namespace host {
+namespace {
+
+template <int L, int CODE, bool TB>
+qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int batch, float* y,
+                        hipStream_t st)
+{
+    const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
+    const dim3 grid((unsigned)(M / 16)), block(MatvecShape::kThreads);
+    if (batch <= 1)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else if (batch <= 2)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else if (batch <= 4)
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    else
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 8>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+    return launch_status();
+}
+
+template <int L>
+qtcq_status matvec_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
+                                 const float* x, int batch, float* y, hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return tb ? matvec_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, st)
+                  : matvec_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, st);
+    return tb ? matvec_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, st)
+              : matvec_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, st);
+}
+
+// the split x of the matrix-core product: fragments, then block scales, in the workspace
+uint4* split_frags(void* ws) { return static_cast<uint4*>(ws); }
+float* split_scales(void* ws, int N, int batch)
+{
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + (size_t)MatvecMfmaShape::kblocks(N) *
+                                    MatvecMfmaShape::frags(batch) * MatvecMfmaShape::kBlockBytes);
+}
+
+qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream_t st)
+{
+    const int nkb = MatvecMfmaShape::kblocks(N);
+    if (nkb == 0) return QTCQ_OK;
+    const int threads = nkb * MatvecMfmaShape::frags(batch) * 64;
+    const int bs = MatvecMfmaShape::kSplitBlock;
+    hipLaunchKernelGGL(matvec_split_x, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, st,
+                       x, N, nkb, batch, split_frags(ws), split_scales(ws, N, batch));
+    return launch_status();
+}
+
+// the same product with the decoded weights and the split x on the matrix cores; x ==
+// nullptr: the workspace already holds the split of this (N, batch)
+template <int L, int CODE, bool TB>
+qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x, int batch,
+                             float* y, void* workspace, hipStream_t st)
+{
+    static_assert(MatvecMfmaShape::stream_words<L, TB>() == (TB ? 16 : 17), "stream words");
+    const int nf = MatvecMfmaShape::frags(batch);
+    if (x) {
+        const qtcq_status rc = split_x_launch(x, N, batch, workspace, st);
+        if (rc != QTCQ_OK) return rc;
+    }
+    const uint4* xs = split_frags(workspace);
+    const float* sc = split_scales(workspace, N, batch);
+    // Two bands per workgroup once the batch spans three or four fragments (reading the
+    // split x then dominates: each fragment costs a kilobyte per k-block and wave) and
+    // M / 16 >= 1024, so the grid keeps >= 512 workgroups (two per CU).  Results do not
+    // depend on the choice (same arithmetic, same order).
+    const int nb = M / 16;
+    const bool two = nf >= 3 && nb >= 1024;
+    const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
+#define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \
+                                               bits, M, N, xs, sc, batch, y)
+    switch (nf) {
+    case 1: QTCQ_MV(1, 1, grid1); break;
+    case 2: if (two) QTCQ_MV(2, 2, grid2); else QTCQ_MV(2, 1, grid1); break;
+    case 3: if (two) QTCQ_MV(3, 2, grid2); else QTCQ_MV(3, 1, grid1); break;
+    default: if (two) QTCQ_MV(4, 2, grid2); else QTCQ_MV(4, 1, grid1); break;
+    }
+#undef QTCQ_MV
+    return launch_status();
+}
+
+template <int L>
+qtcq_status matvec_mfma_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
+                                      const float* x, int batch, float* y, void* workspace,
+                                      hipStream_t st)
+{
+    if (code == QTCQ_CODE_1MAD)
+        return tb ? matvec_mfma_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, workspace, st)
+                  : matvec_mfma_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, workspace, st);
+    return tb ? matvec_mfma_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, workspace, st)
+              : matvec_mfma_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, workspace, st);
+}
+
+template <int L>
+struct MatvecMfmaF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return matvec_mfma_dispatch_code<L>(a...); }
+};
+
+template <int L>
+struct MatvecF {
+    template <typename... A>
+    static qtcq_status run(A... a) { return matvec_dispatch_code<L>(a...); }
+};
+
+}  // namespace
+
+int matvec_max_batch() { return MatvecShape::kMaxBatch; }
+int matvec_mfma_max_batch() { return MatvecMfmaShape::kMaxBatch; }
+int matvec_mfma_max_n() { return MatvecMfmaShape::kMaxN; }
+size_t matvec_mfma_workspace_bytes(int N) { return MatvecMfmaShape::workspace_bytes(N); }
+
+qtcq_status launch_decode_matvec(int L, int code, bool tb, const uint32_t* bits, int M, int N,
+                          const float* x, int batch, float* y, hipStream_t st)
+{
+    return by_L<MatvecF>(L, code, tb, bits, M, N, x, batch, y, st);
+}
+
+qtcq_status launch_decode_matvec_mfma(int L, int code, bool tb, const uint32_t* bits, int M, int N,
+                               const float* x, int batch, float* y, void* ws, hipStream_t st)
+{
+    return by_L<MatvecMfmaF>(L, code, tb, bits, M, N, x, batch, y, ws, st);
+}
+
+qtcq_status launch_split_x(const float* x, int N, int batch, void* ws, hipStream_t st)
+{
+    return split_x_launch(x, N, batch, ws, st);
+}
+
+}  // namespace host
+}  // namespace qtcq

@@ -89,9 +89,12 @@ __device__ __forceinline__ uint32_t shift_in_bit(uint32_t word, uint64_t mask)
 // groups between a group's compares and the add-with-carry that packs its bits
 constexpr int kBitDelay = 1;
 
-// Forward pass over a pair of sequences per workgroup.
-//   grid.x = ceil(n / 2) for the n sequences of the chunk, block = Trellis<L>::kThreads.
-//   seq, wts : [*][T]; the workgroup takes rows b0 + 2*blockIdx.x (+1 if < b0 + n)
+// Forward pass over a pair of sequences per workgroup (or one, for batches that fit in
+// one round of compute units).
+//   grid.x = ceil(n / per_wg) for the n sequences of the chunk, block = Trellis<L>::kThreads.
+//   per_wg   : sequences per workgroup, 2 (interleaved pair) or 1
+//   seq, wts : [*][T]; the workgroup takes rows b0 + per_wg*blockIdx.x (+1 if per_wg = 2
+//              and < b0 + n)
 //   rot      : the search runs over the rotated targets s'[t] = s[(t + rot) mod T]
 //              (0 <= rot < T; the tail-biting encoder's first search uses T/2)
 //   pin      : PINNED only -- [n] overlap o per sequence (an (L-2)-bit value): the walk
@@ -110,8 +113,9 @@ constexpr int kBitDelay = 1;
 template <int L, int CODE, bool WEIGHTED, bool PINNED = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
-                int64_t n, int rot, const uint32_t* __restrict__ pin, uint32_t* __restrict__ bp,
-                uint32_t* __restrict__ fin, float* __restrict__ fin_cost, float* __restrict__ mse)
+                int64_t n, int per_wg, int rot, const uint32_t* __restrict__ pin,
+                uint32_t* __restrict__ bp, uint32_t* __restrict__ fin, float* __restrict__ fin_cost,
+                float* __restrict__ mse)
 {
     using Tr = Trellis<L>;
     constexpr int NB = Tr::kButterflies;
@@ -121,8 +125,8 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
     __shared__ float4 muB[Tr::kChunks];   // and of sequence B
 
     const int tid = threadIdx.x;
-    const int64_t qa = 2 * (int64_t)blockIdx.x;          // index within the chunk
-    const bool has_b = qa + 1 < n;                        // uniform over the workgroup
+    const int64_t qa = per_wg * (int64_t)blockIdx.x;     // index within the chunk
+    const bool has_b = per_wg == 2 && qa + 1 < n;         // uniform over the workgroup
     const int64_t qb = has_b ? qa + 1 : qa;
     const float* sa = seq + (b0 + qa) * T;
     const float* sb = seq + (b0 + qb) * T;
@@ -308,7 +312,11 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
                     float c = in + step_err<WEIGHTED>(Cv[a][r][x], sp, wp);
                     // pinned: only the end states whose low L-2 bits are o take part
                     if (PINNED && (uint32_t)(4 * (tid + r * NT) + x) != o) continue;
-                    if (c < best) {   // states visited in increasing order
+                    // states are visited in increasing order; the first one is taken
+                    // whatever its cost, so a row whose costs are all +inf (finite inputs
+                    // whose squared errors overflow binary32) still ends in its lowest
+                    // allowed state
+                    if (c < best || bi == 0xFFFFFFFFu) {
                         best = c;
                         bi = (uint32_t)(a * M + 4 * (tid + r * NT) + x);
                     }
