@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
             "oracle_code_3inst": (ctypes.c_float, [c_u32]),
             "oracle_code_3inst_raw": (c_dbl, [c_u32]),
             "oracle_code_table": (c_int, [c_int, c_int, f32p]),
+            "oracle_code_xor": (ctypes.c_float, [c_u32, u32p]),
+            "oracle_code_table_xor": (c_int, [c_int, u32p, f32p]),
             "oracle_viterbi": (c_int, [f32p, f32p, f32p, c_int, c_int, c_int, u32p, f32p]),
             "oracle_viterbi_batch": (c_int, [f32p, f32p, f32p, c_i64, c_int, c_int, c_int,
                                              u32p, f32p, f32p]),
@@ -132,9 +134,21 @@ def code_3inst_raw(x: int) -> float:
 
 
 def code_table(code, L: int) -> np.ndarray:
+    """Code value of every L-bit state: code "1mad", "3inst", or ("xor", masks) for the
+    XOR-Trellis palette code with parity masks (m0, m1, m2, m3)."""
     out = np.empty(1 << L, dtype=np.float32)
+    if isinstance(code, tuple) and code[0] == "xor":
+        m = np.ascontiguousarray(np.array(code[1], dtype=np.uint32))
+        _check(lib().oracle_code_table_xor(L, _p(m, ctypes.c_uint32), _p(out, ctypes.c_float)),
+               "code_table_xor")
+        return out
     _check(lib().oracle_code_table(_CODES[code], L, _p(out, ctypes.c_float)), "code_table")
     return out
+
+
+def code_xor(x: int, masks) -> float:
+    m = np.ascontiguousarray(np.array(masks, dtype=np.uint32))
+    return lib().oracle_code_xor(x, _p(m, ctypes.c_uint32))
 
 
 # ---------------------------------------------------------------------------------

@@ -45,6 +45,12 @@
  * other 3INST choice above is pinned by the printed raw sigma, the LCG choice is not
  * (sigma is insensitive to it).
  *
+ * XOR-Trellis palette code [XOR "The sign at each junction has to be cheap"]: the
+ * state's newest 2 bits are the branch and the L-2 bits above them the branch history;
+ * four masked parities of the history pick a palette (first two) and a branch shuffle
+ * (last two), the shuffle XORed into the branch to pick the entry; the values are the
+ * four printed FP4 palettes, unscaled.  The masks are not printed: they are inputs.
+ *
  * Return codes: 0 = ok, 1 = invalid argument, 2 = out of memory.
  */
 #include <math.h>
@@ -130,6 +136,46 @@ float oracle_code_3inst(uint32_t x)
 }
 
 /* Fill C[0 .. 2^L) with the code value of every L-bit state. */
+/* XOR-Trellis palette code [XOR "The sign at each junction has to be cheap"]: the four
+ * FP4 palettes as printed, the parity of a masked history read bit by bit. */
+static const double XOR_PALETTE[4][4] = {
+    {-6.0, -1.5, 0.0, 2.0},
+    {-4.0, -1.0, 0.5, 3.0},
+    {-3.0, -0.5, 1.0, 4.0},
+    {-2.0, 0.0, 1.5, 6.0},
+};
+
+static uint32_t parity_of(uint32_t v)
+{
+    uint32_t p = 0;
+    while (v) {
+        p ^= v & 1u;
+        v >>= 1;
+    }
+    return p;
+}
+
+float oracle_code_xor(uint32_t x, const uint32_t* masks)
+{
+    uint32_t branch = x & 3u;          /* the newest 2 bits: this step's branch */
+    uint32_t history = x >> 2;         /* the L-2 earlier branch bits */
+    uint32_t palette = 2u * parity_of(history & masks[0]) + parity_of(history & masks[1]);
+    uint32_t shuffle = 2u * parity_of(history & masks[2]) + parity_of(history & masks[3]);
+    return (float)XOR_PALETTE[palette][branch ^ shuffle];
+}
+
+/* Table of the XOR code at L (2 <= L <= 16, masks below 2^(L-2)). */
+int oracle_code_table_xor(int L, const uint32_t* masks, float* C)
+{
+    if (L < 2 || L > 16 || !C || !masks) return ORC_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if ((masks[i] >> (L - 2)) != 0) return ORC_EINVAL;
+    uint32_t n = 1u << L;
+    for (uint32_t j = 0; j < n; ++j)
+        C[j] = oracle_code_xor(j, masks);
+    return ORC_OK;
+}
+
 int oracle_code_table(int code, int L, float* C)
 {
     if (L < 1 || L > 24 || !C) return ORC_EINVAL;

@@ -51,3 +51,24 @@ def workload(name: str, B: int | None = None, T: int = T_DEFAULT):
     s = targets(nb, T, spec["seed"])
     w = weights(nb, T, spec["wseed"]) if spec["weighted"] else None
     return s, w, spec["code"]
+
+
+# XOR-Trellis palette code (workload parameters, not method arithmetic): the page prints
+# the palettes but not the four parity masks, so the workloads fix four 14-bit masks of
+# 8 history bits each, linearly independent over GF(2) (every palette and shuffle bit
+# depends on the history, and the four are jointly uniform over uniform histories).
+# Narrower trellises keep the masks' low L - 2 bits.
+XOR_MASKS = (0x2D35, 0x1ACB, 0x34AE, 0x0F53)
+# targets for the XOR code are N(0, 1) times the RMS of the 16 printed palette values,
+# sqrt(137 / 16), so that targets and code values have the same spread
+XOR_TARGET_SCALE = 2.9261749
+
+
+def xor_masks(L: int = 16) -> tuple:
+    keep = (1 << (L - 2)) - 1
+    return tuple(m & keep for m in XOR_MASKS)
+
+
+def xor_targets(B: int, T: int = T_DEFAULT, seed: int = 0) -> np.ndarray:
+    """[B][T] float32 N(0, 1) targets scaled to the XOR palettes' spread."""
+    return (targets(B, T, seed) * np.float32(XOR_TARGET_SCALE)).astype(np.float32)
