@@ -62,14 +62,37 @@ typedef enum {
     QTCQ_ERR_DEVICE = 4       /* a kernel launch failed (hipGetLastError) */
 } qtcq_status;
 
-/* Computed codes [QTIP "The codebook is computed"].  Both start from the LCG
- * u = 34038481 * x + 76625530 (mod 2^32) of the L-bit state x.
+/* Codes: the value of an L-bit trellis state x.
+ *  1MAD, 3INST [QTIP "The codebook is computed"] start from the LCG
+ *         u = 34038481 * x + 76625530 (mod 2^32).
  *  1MAD : value = float( (S - 510) / 147.8 ) with S the sum of u's four bytes and the
  *         division done in binary64 (one rounding to binary32 at the end).
  *  3INST: v = (u & 0x8FFF8FFF) ^ 0x3B603B60 (sign, 2 low exponent bits and mantissa of
  *         each half XORed into fp16(0.922)); h = fp16 sum of the two halves (RNE);
- *         value = float( h / 1.244 ) in binary64 -- unit variance. */
-typedef enum { QTCQ_CODE_1MAD = 0, QTCQ_CODE_3INST = 1 } qtcq_code_id;
+ *         value = float( h / 1.244 ) in binary64 -- unit variance.
+ *  XOR  : the XOR-Trellis palette code [XOR "The sign at each junction has to be
+ *         cheap"].  The newest k = 2 bits of x are the branch b = x & 3, the L - 2 bits
+ *         above them the history h = x >> 2.  Four masked parities p_i =
+ *         parity(h & m_i) pick the palette P = 2 p_0 + p_1 and the shuffle
+ *         S = 2 p_2 + p_3; value = palette[P][b XOR S] with the printed FP4 palettes
+ *         [-6, -1.5, 0, 2], [-4, -1, 0.5, 3], [-3, -0.5, 1, 4], [-2, 0, 1.5, 6] (as they
+ *         are; a per-group scale of the weights is the caller's).  The four successors of
+ *         a state share its history's low bits, so they offer the four distinct entries
+ *         of one palette.  The masks m_0..m_3 are not printed: they are the caller's, as
+ *         (L - 2)-bit history masks (14 bits at L = 16).
+ * A code is passed as a qtcq_code descriptor: the id in bits 0-7 and, for XOR, the four
+ * masks in 14-bit fields at bits 8, 22, 36 and 50 (qtcq_xor_code builds it).  1MAD and
+ * 3INST are their plain ids.  Entry points return QTCQ_ERR_UNSUPPORTED for an unknown id
+ * (or parameter bits on 1MAD/3INST) and QTCQ_ERR_INVALID_ARG for XOR masks with bits at
+ * or above L - 2. */
+typedef uint64_t qtcq_code;
+typedef enum { QTCQ_CODE_1MAD = 0, QTCQ_CODE_3INST = 1, QTCQ_CODE_XOR = 2 } qtcq_code_id;
+#define QTCQ_CODE_INVALID ((qtcq_code)0xFF)
+
+/* The XOR palette code with parity masks m0 (palette high bit), m1 (palette low bit),
+ * m2 (shuffle high bit), m3 (shuffle low bit); QTCQ_CODE_INVALID if a mask exceeds
+ * 14 bits. */
+qtcq_code qtcq_xor_code(uint32_t m0, uint32_t m1, uint32_t m2, uint32_t m3);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qtcq_status_string(qtcq_status s);
@@ -91,8 +114,9 @@ size_t qtcq_bcjr_workspace_bytes(int64_t B, int T, int L, int k);
 
 /* Code value of every L-bit state [QTIP "The codebook is computed"], evaluated by the
  * decode kernels' device code (the search kernels evaluate the same values in another
- * exact form once per workgroup).  out: [2^L] float32 (device).  L in 1..24. */
-qtcq_status qtcq_code_table(int code, int L, float* out, void* stream);
+ * exact form once per workgroup).  out: [2^L] float32 (device).  L in 1..24 (1MAD,
+ * 3INST) or 2..16 (XOR). */
+qtcq_status qtcq_code_table(qtcq_code code, int L, float* out, void* stream);
 
 /* Viterbi encoding [QTIP "The trellis: a stateful codebook"; XOR "Cliff edges"].
  * For each sequence b, finds the walk st[0..T) through the bitshift trellis (state j
@@ -107,7 +131,7 @@ qtcq_status qtcq_code_table(int code, int L, float* out, void* stream);
  *   seq       [B][T] float32 targets (in)
  *   err_w     [B][T] float32 positive error weights (in), or NULL for unweighted
  *   B         number of sequences (>= 0; 0 is a no-op)
- *   code      qtcq_code_id
+ *   code      qtcq_code (1MAD, 3INST or an XOR palette code)
  *   bits      [B][qtcq_bitstream_words(L,k,T)] uint32 (out) -- the layout above
  *   mse       [B] float32 (out) = cost / T, or NULL
  *   states    [B][T] uint32 (out) = st, or NULL
@@ -116,7 +140,7 @@ qtcq_status qtcq_code_table(int code, int L, float* out, void* stream);
  * Errors: QTCQ_ERR_INVALID_ARG, QTCQ_ERR_UNSUPPORTED, QTCQ_ERR_WORKSPACE (workspace
  * NULL, misaligned or below qtcq_encode_workspace_bytes(1, T, L, k)), QTCQ_ERR_DEVICE. */
 qtcq_status qtcq_viterbi_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
-                                int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                int k, qtcq_code code, uint32_t* bits, float* mse, uint32_t* states,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Window decode [QTIP "The trellis: a stateful codebook"]: recon[b][t] = code(window
@@ -131,7 +155,7 @@ qtcq_status qtcq_viterbi_encode(const float* seq, const float* err_w, int64_t B,
  *          bit for bit.
  * Errors: QTCQ_ERR_INVALID_ARG (also: mse requested without seq, or neither recon nor
  * mse requested), QTCQ_ERR_UNSUPPORTED, QTCQ_ERR_DEVICE. */
-qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, qtcq_code code,
                         float* recon, const float* seq, const float* err_w, float* mse,
                         void* stream);
 
@@ -157,7 +181,7 @@ qtcq_status qtcq_decode(const uint32_t* bits, int64_t B, int T, int L, int k, in
  * workspaces let more sequences run per pass.
  * Errors: as qtcq_viterbi_encode. */
 qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
-                           int code, float temperature, float* soft, float* log_z,
+                           qtcq_code code, float temperature, float* soft, float* log_z,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Gradient of the soft codeword [BCJR abstract: the relaxation is exactly
@@ -195,7 +219,7 @@ size_t qtcq_bcjr_vjp_workspace_bytes(int64_t B, int T, int L, int k);
  * Errors: QTCQ_ERR_INVALID_ARG (also grad_soft or grad_seq NULL), QTCQ_ERR_UNSUPPORTED,
  * QTCQ_ERR_WORKSPACE, QTCQ_ERR_DEVICE. */
 qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
-                          int code, float temperature, const float* grad_soft, float* grad_seq,
+                          qtcq_code code, float temperature, const float* grad_soft, float* grad_seq,
                           float* soft, float* log_z, void* workspace, size_t workspace_bytes,
                           void* stream);
 
@@ -235,14 +259,14 @@ size_t qtcq_tailbiting_workspace_bytes(int64_t B, int T, int L, int k);
  * Errors: QTCQ_ERR_INVALID_ARG (also k*T < L), QTCQ_ERR_UNSUPPORTED,
  * QTCQ_ERR_WORKSPACE, QTCQ_ERR_DEVICE. */
 qtcq_status qtcq_tailbiting_encode(const float* seq, const float* err_w, int64_t B, int T, int L,
-                                   int k, int code, uint32_t* bits, float* mse, uint32_t* states,
+                                   int k, qtcq_code code, uint32_t* bits, float* mse, uint32_t* states,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Window decode of tail-biting streams (cyclic windows, layout above); arguments,
  * outputs and errors as qtcq_decode, with bits [B][qtcq_tailbiting_words(L,k,T)] and
  * k*T >= L.  Decoding qtcq_tailbiting_encode's output with the same seq/err_w
  * reproduces its mse bit for bit. */
-qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L, int k, int code,
+qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L, int k, qtcq_code code,
                                    float* recon, const float* seq, const float* err_w, float* mse,
                                    void* stream);
 
@@ -266,7 +290,7 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
  * Errors: QTCQ_ERR_INVALID_ARG (M or N negative or not multiples of 16, NULL or
  * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8),
  * QTCQ_ERR_DEVICE. */
-qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, int code,
+qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, qtcq_code code,
                                int tailbiting, const float* x, int batch, float* y, void* stream);
 
 /* The same product with the multiplications on the matrix cores [same passage].  The
@@ -291,7 +315,7 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
  * QTCQ_ERR_UNSUPPORTED for N > 2^22, and QTCQ_ERR_WORKSPACE (workspace NULL, misaligned
  * or too small). */
 size_t qtcq_decode_matvec_mfma_workspace_bytes(int N);   /* 0 if N < 0, N % 16 != 0 or N > 2^22 */
-qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, int k, int code,
+qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, int k, qtcq_code code,
                                     int tailbiting, const float* x, int batch, float* y,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -308,7 +332,7 @@ qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, i
 qtcq_status qtcq_matvec_mfma_split_x(const float* x, int N, int batch, void* workspace,
                                      size_t workspace_bytes, void* stream);
 qtcq_status qtcq_decode_matvec_mfma_presplit(const uint32_t* bits, int M, int N, int L, int k,
-                                             int code, int tailbiting, const void* split,
+                                             qtcq_code code, int tailbiting, const void* split,
                                              size_t split_bytes, int batch, float* y,
                                              void* stream);
 

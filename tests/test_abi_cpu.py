@@ -78,7 +78,7 @@ def test_encode_validation(nat):
     assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(L=18) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(k=1) == nat.QTCQ_ERR_UNSUPPORTED
-    assert call(code=2) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(code=3) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(B=0, seq=None, bits=None, ws=None) == nat.QTCQ_OK
     assert call(seq=None) == nat.QTCQ_ERR_INVALID_ARG
     assert call(bits=None) == nat.QTCQ_ERR_INVALID_ARG
@@ -314,3 +314,32 @@ def test_header_is_plain_c_and_links(tmp_path):
            "-Wl,--unresolved-symbols=ignore-in-shared-libs"]
     subprocess.run(cmd, check=True, capture_output=True)
     assert exe.exists()
+
+
+def test_code_descriptors(nat):
+    """qtcq_code: 1MAD and 3INST are their ids; the XOR palette code carries four 14-bit
+    parity masks.  Unknown ids and parameter bits on 1MAD/3INST are unsupported; XOR masks
+    that reach beyond the L - 2 history bits are invalid arguments.  Each call below fails
+    after the code check (workspace too small), so nothing is launched."""
+    masks = (0x2D35, 0x1ACB, 0x34AE, 0x0F53)
+    xc = nat.qtcq_xor_code(*masks)
+    assert xc & 0xFF == nat.QTCQ_CODE_XOR
+    assert [(xc >> (8 + 14 * i)) & 0x3FFF for i in range(4)] == list(masks)
+    assert nat.qtcq_xor_code(1 << 14, 0, 0, 0) == nat.QTCQ_CODE_INVALID
+    st = lambda *a: nat.raw_status("qtcq_viterbi_encode", *a)
+    small = 16       # below one sequence's workspace: QTCQ_ERR_WORKSPACE once the code is accepted
+
+    def enc(code, L):
+        return st(FAKE, None, 4, 256, L, 2, code, FAKE, None, None, FAKE, small, None)
+    assert enc(xc, 16) == nat.QTCQ_ERR_WORKSPACE
+    assert enc(xc, 12) == nat.QTCQ_ERR_INVALID_ARG          # masks need 14 history bits
+    low = nat.qtcq_xor_code(*[m & 0x3FF for m in masks])
+    assert enc(low, 12) == nat.QTCQ_ERR_WORKSPACE
+    assert enc(nat.QTCQ_CODE_XOR, 6) == nat.QTCQ_ERR_WORKSPACE   # zero masks: palette 0
+    assert enc(nat.QTCQ_CODE_1MAD | (1 << 8), 16) == nat.QTCQ_ERR_UNSUPPORTED
+    assert enc(nat.QTCQ_CODE_INVALID, 16) == nat.QTCQ_ERR_UNSUPPORTED
+    assert enc(3, 16) == nat.QTCQ_ERR_UNSUPPORTED
+    tab = lambda *a: nat.raw_status("qtcq_code_table", *a)
+    assert tab(xc, 20, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG    # XOR: L <= 16
+    assert tab(xc, 1, FAKE, None) == nat.QTCQ_ERR_INVALID_ARG
+    assert tab(3, 16, FAKE, None) == nat.QTCQ_ERR_UNSUPPORTED

@@ -2,8 +2,10 @@
 respect to the targets) against the binary64 oracle.
 
 Tolerance (fp32 against an exact reference), per sequence:
-    max_u |grad_gpu - grad_oracle| <= 1e-5 * RMS_u(grad_oracle),
-the bound used for the soft codeword itself; the kernel keeps the messages it needs in
+    max_u |grad_gpu - grad_oracle| <= 1e-5 * RMS_u(grad_oracle) + 2^-126,
+the bound used for the soft codeword itself, plus binary32's normal-range floor (the
+output format keeps no relative precision below it; it decides only for gradients that
+are numerically zero); the kernel keeps the messages it needs in
 fixed point (2^-21 log2 units; below tau = 0.01 in fp64) and its expectation messages
 centred on the soft codeword, which a CPU emulation of this arithmetic puts at <= 6e-6
 at tau = 0.01 and <= 1.1e-6 at tau = 1e-3.
@@ -22,6 +24,7 @@ from helpers import bcjr_err, dev, oracle_vjp_par, say
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
+FLOOR = 2.0 ** -126
 
 
 @pytest.fixture(scope="module")
@@ -55,7 +58,12 @@ def run_and_compare(api, s, w, g, tau, L, code, tol=TOL):
     grad_o, soft_o = oracle_vjp_par(C, s, tau, g.astype(np.float64), w, L=L)
     assert bcjr_err(soft.cpu().numpy(), soft_o).max() <= TOL
     err = bcjr_err(grad.cpu().numpy(), grad_o)
-    assert err.max() <= tol, "max grad err/rms %g" % err.max()
+    # the output is binary32: below its normal range a value keeps no relative precision,
+    # so each sequence's bar is tol * RMS plus 2^-126 (it matters only for a gradient that
+    # is numerically zero, e.g. ~1e-48 at tau = 0.01 far from any near-tie)
+    dmax = np.abs(grad.cpu().numpy().astype(np.float64) - grad_o).max(axis=1)
+    rms = np.sqrt((grad_o ** 2).mean(axis=1))
+    assert np.all(dmax <= tol * rms + FLOOR), "max grad err/rms %g" % err.max()
     return err
 
 

@@ -23,6 +23,8 @@ QTCQ_ERR_DEVICE = 4
 
 QTCQ_CODE_1MAD = 0
 QTCQ_CODE_3INST = 1
+QTCQ_CODE_XOR = 2
+QTCQ_CODE_INVALID = 0xFF
 
 
 class QtcqError(RuntimeError):
@@ -41,33 +43,35 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _sz = ctypes.c_size_t
+_code = ctypes.c_uint64   # qtcq_code descriptor
 
 _SIGS = {
     "qtcq_status_string": (ctypes.c_char_p, [_int]),
     "qtcq_bitstream_words": (_i64, [_int, _int, _int]),
     "qtcq_encode_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
     "qtcq_bcjr_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
-    "qtcq_code_table": (_int, [_int, _int, _vp, _vp]),
-    "qtcq_viterbi_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+    "qtcq_xor_code": (_code, [ctypes.c_uint32] * 4),
+    "qtcq_code_table": (_int, [_code, _int, _vp, _vp]),
+    "qtcq_viterbi_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _code, _vp, _vp, _vp, _vp,
                                    _sz, _vp]),
-    "qtcq_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
-    "qtcq_bcjr_soft": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp,
+    "qtcq_decode": (_int, [_vp, _i64, _int, _int, _int, _code, _vp, _vp, _vp, _vp, _vp]),
+    "qtcq_bcjr_soft": (_int, [_vp, _vp, _i64, _int, _int, _int, _code, ctypes.c_float, _vp, _vp,
                               _vp, _sz, _vp]),
     "qtcq_bcjr_vjp_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
-    "qtcq_bcjr_vjp": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp,
+    "qtcq_bcjr_vjp": (_int, [_vp, _vp, _i64, _int, _int, _int, _code, ctypes.c_float, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
-    "qtcq_decode_matvec": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
+    "qtcq_decode_matvec": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp, _int, _vp, _vp]),
     "qtcq_decode_matvec_mfma_workspace_bytes": (_sz, [_int]),
-    "qtcq_decode_matvec_mfma": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp, _int, _vp,
+    "qtcq_decode_matvec_mfma": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp, _int, _vp,
                                        _vp, _sz, _vp]),
     "qtcq_matvec_mfma_split_x": (_int, [_vp, _int, _int, _vp, _sz, _vp]),
-    "qtcq_decode_matvec_mfma_presplit": (_int, [_vp, _int, _int, _int, _int, _int, _int, _vp,
+    "qtcq_decode_matvec_mfma_presplit": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp,
                                                 _sz, _int, _vp, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
     "qtcq_tailbiting_workspace_bytes": (_sz, [_i64, _int, _int, _int]),
-    "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp,
+    "qtcq_tailbiting_encode": (_int, [_vp, _vp, _i64, _int, _int, _int, _code, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
-    "qtcq_tailbiting_decode": (_int, [_vp, _i64, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+    "qtcq_tailbiting_decode": (_int, [_vp, _i64, _int, _int, _int, _code, _vp, _vp, _vp, _vp,
                                       _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -85,6 +89,15 @@ def _ptr(p):
 def _check(status: int, where: str) -> None:
     if status != QTCQ_OK:
         raise QtcqError(status, where)
+
+
+def qtcq_xor_code(m0: int, m1: int, m2: int, m3: int) -> int:
+    """The qtcq_code descriptor of the XOR palette code with parity masks m0..m3
+    (QTCQ_CODE_INVALID if a mask exceeds 14 bits)."""
+    ms = [int(m) for m in (m0, m1, m2, m3)]
+    if any(m < 0 or m > 0xFFFFFFFF for m in ms):
+        return QTCQ_CODE_INVALID
+    return _lib.qtcq_xor_code(*ms)
 
 
 def qtcq_status_string(status: int) -> str:

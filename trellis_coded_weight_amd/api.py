@@ -11,8 +11,22 @@ from . import _native as nat
 CODES = {"1mad": nat.QTCQ_CODE_1MAD, "3inst": nat.QTCQ_CODE_3INST}
 
 
+def xor_code(masks) -> int:
+    """The XOR-Trellis palette code with parity masks (m0, m1, m2, m3): m0 and m1 pick the
+    palette, m2 and m3 the branch shuffle; each an (L - 2)-bit history mask."""
+    code = nat.qtcq_xor_code(*masks)
+    if code == nat.QTCQ_CODE_INVALID:
+        raise ValueError("XOR parity masks must fit in 14 bits")
+    return code
+
+
 def _code(code) -> int:
-    return CODES[code] if isinstance(code, str) else int(code)
+    """A code name ("1mad", "3inst"), ("xor", masks), or a qtcq_code descriptor."""
+    if isinstance(code, str):
+        return CODES[code]
+    if isinstance(code, tuple) and len(code) == 2 and code[0] == "xor":
+        return xor_code(code[1])
+    return int(code)
 
 
 def _stream() -> int:

@@ -288,15 +288,15 @@ __device__ __forceinline__ void lds_write4(char* base, int addr, int P, double v
 }
 
 // The code values of a thread's 64 states (a, c = 4 tid + r, x) held as their raw values
-// (1MAD: S - 510, an integer of magnitude below 2^10; 3INST: the fp16 sum -- both exact
-// in fp16), two per register, and rescaled at each use (code_rescale: the same bits as
+// (1MAD: S - 510, an integer of magnitude below 2^10; 3INST: the fp16 sum; the XOR
+// palette values -- all exact in fp16), two per register, and rescaled at each use (code_rescale: the same bits as
 // code_value).  The widening is written as an instruction so that it stays at its use:
 // hoisted out of a step loop, the 64 decoded values would need 64 registers again.
 template <int L, int CODE>
 struct PackedCodes {
     uint32_t w[4][4][2];   // [a][r][x >> 1], x even in the low half
 
-    __device__ __forceinline__ void init(int tid)
+    __device__ __forceinline__ void init(int tid, const CodeArg& ca)
     {
         constexpr int M = Trellis<L>::kGroups;
 #pragma unroll
@@ -306,7 +306,7 @@ struct PackedCodes {
 #pragma unroll
                 for (int hx = 0; hx < 2; ++hx) {
                     const uint32_t j = (uint32_t)(a * M + 16 * tid + 4 * r + 2 * hx);
-                    const float lo = code_raw<CODE>(j), hi = code_raw<CODE>(j + 1);
+                    const float lo = code_raw<CODE>(j, ca), hi = code_raw<CODE>(j + 1, ca);
                     w[a][r][hx] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -343,7 +343,7 @@ inline size_t bcjr_bytes_per_seq(int T, int L, bool vjp = false)
 template <int L, int CODE, bool WEIGHTED, bool VJP = false, bool WIDE = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
-           double kappa, char* __restrict__ ws)
+           double kappa, char* __restrict__ ws, CodeArg ca)
 {
     static_assert(VJP || !WIDE, "the wide stash is a gradient-mode layout");
     using Tr = Trellis<L>;
@@ -382,7 +382,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x));
+                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x), ca);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
@@ -529,7 +529,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // it holds the code values packed (PackedCodes): 32 registers instead of 64, which
     // keeps the step loop free of spills.
     PackedCodes<L, CODE> Ch;
-    Ch.init(tid);
+    Ch.init(tid, ca);
     // Y_{T-1} = 0
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);

@@ -41,7 +41,7 @@ template <int L, int CODE, bool WEIGHTED, bool WIDE = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                const float* __restrict__ gup, int T, int64_t b0, double kappa,
-               char* __restrict__ ws)
+               char* __restrict__ ws, CodeArg ca)
 {
     using Tr = Trellis<L>;
     using Ly = BcjrLayout<L>;
@@ -92,7 +92,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         softs[t] = pc / pg;
     }
     PackedCodes<L, CODE> Cp;   // code values of the states (a, c = 4 tid + r, x)
-    Cp.init(tid);
+    Cp.init(tid, ca);
 
     auto opaque_tid = [&]() {
         int v = tid;

@@ -4,8 +4,11 @@
 // Computed codes follow QTIP blog, "The codebook is computed": an LCG of the L-bit
 // state, then either the byte sum of the LCG output (1MAD) or an fp16 bit trick with
 // one fp16 add (3INST; XOR-Trellis explainer, "The sign at each junction has to be
-// cheap").  The final rescale is a binary64 division rounded once to binary32, so every
-// code value is a fixed bit pattern.  The device gets the same bits with binary32 work
+// cheap").  The XOR-Trellis palette code (same explainer and section) reads four masked
+// parities of the state's history bits: two pick one of four printed FP4 palettes, two
+// permute which branch takes which entry (see code_xor).  The final rescale of 1MAD and
+// 3INST is a binary64 division rounded once to binary32, so every code value is a fixed
+// bit pattern.  The device gets the same bits with binary32 work
 // only: v * (1/D) is split as v * r_hi + v * r_lo, where r_hi (13 significant bits)
 // makes v * r_hi exact and one FMA adds v * r_lo with a single rounding.  Over the whole
 // input domain of each code (byte sums 0..1020; every finite fp16 value below 4 in
@@ -20,7 +23,13 @@
 
 namespace qtcq {
 
-enum : int { kCode1Mad = 0, kCode3Inst = 1 };
+enum : int { kCode1Mad = 0, kCode3Inst = 1, kCodeXor = 2 };
+
+// Run-time parameters of a code, passed by value to every kernel: the four parity masks
+// of the XOR-Trellis palette code (unused by 1MAD and 3INST).
+struct CodeArg {
+    uint32_t m[4];
+};
 
 // LCG of a state x < 2^24: (34038481 x + 76625530) mod 2^32.  The multiplier is
 // 2^25 + 484049, so one 24-bit multiply-add forms 484049 x + 76625530 and one shift-add
@@ -79,16 +88,41 @@ __device__ __forceinline__ float code_3inst(uint32_t x)
     return rescale((float)code_3inst_raw(x), k3InstRhi, k3InstRlo);
 }
 
+// XOR-Trellis palette code of an L-bit state x (L <= 16): the newest k = 2 bits are the
+// branch b = x & 3 and the L - 2 bits above them the branch history h = x >> 2.  Four
+// parities p_i = parity(h & m_i) of masked history bits give the palette index
+// 2 p_0 + p_1 and the shuffle 2 p_2 + p_3, which is XORed into the branch to pick the
+// entry.  The four successors of a state share its low history bits, hence the palette
+// and the shuffle, so their values are the four distinct entries of one palette.  The
+// palettes hold the FP4 values [-6, -1.5, 0, 2], [-4, -1, 0.5, 3], [-3, -0.5, 1, 4] and
+// [-2, 0, 1.5, 6], used as they are (exact in fp16 and binary32; a per-group scale of
+// the weights lies outside the trellis).  Here each value is stored doubled as a signed
+// byte, palette p in byte lanes 4p..4p+3 of a 128-bit constant.
+__device__ __forceinline__ float code_xor(uint32_t x, const CodeArg& ca)
+{
+    const uint32_t h = x >> 2;
+    const uint32_t p = ((__builtin_popcount(h & ca.m[0]) & 1u) << 1) | (__builtin_popcount(h & ca.m[1]) & 1u);
+    const uint32_t sh = ((__builtin_popcount(h & ca.m[2]) & 1u) << 1) | (__builtin_popcount(h & ca.m[3]) & 1u);
+    const uint32_t e = (x & 3u) ^ sh;
+    constexpr uint64_t kPal01 = 0x0601FEF80400FDF4ull;   // 2 x [-6, -1.5, 0, 2], 2 x [-4, -1, 0.5, 3]
+    constexpr uint64_t kPal23 = 0x0C0300FC0802FFFAull;   // 2 x [-3, -0.5, 1, 4], 2 x [-2, 0, 1.5, 6]
+    const uint64_t pair = (p & 2u) ? kPal23 : kPal01;
+    const int twice = (int)(int8_t)(uint8_t)(pair >> (8u * (4u * (p & 1u) + e)));
+    return (float)twice * 0.5f;
+}
+
 // The same values in the form the search kernels compute once per workgroup: the
 // 32-bit LCG product and the rescale by the binary64 reciprocal of the divisor (which
 // rounds to the same binary32 value as the binary64 quotient on the same domains, also
 // checked exhaustively on the host).  Their cost does not matter there, and with this
 // form the step loops keep their register allocation (no spills).
 template <int CODE>
-__device__ __forceinline__ float code_value_prologue(uint32_t x)
+__device__ __forceinline__ float code_value_prologue(uint32_t x, const CodeArg& ca)
 {
     const uint32_t u = x * 34038481u + 76625530u;
-    if constexpr (CODE == kCode1Mad) {
+    if constexpr (CODE == kCodeXor) {
+        return code_xor(x, ca);
+    } else if constexpr (CODE == kCode1Mad) {
         const int n = (int)__builtin_amdgcn_sad_u8(u, 0u, 0u) - 510;
         return (float)((double)n * (1.0 / 147.8));
     } else {
@@ -100,15 +134,18 @@ __device__ __forceinline__ float code_value_prologue(uint32_t x)
     }
 }
 
-// The code before its rescale (exact in binary32), and the rescale itself:
-// code_value(x) = code_rescale(code_raw(x)) bit for bit.
+// The code before its rescale (exact in binary32 and fp16), and the rescale itself:
+// code_value(x) = code_rescale(code_raw(x)) bit for bit.  The palette values need no
+// rescale.
 template <int CODE>
-__device__ __forceinline__ float code_raw(uint32_t x)
+__device__ __forceinline__ float code_raw(uint32_t x, const CodeArg& ca)
 {
     if constexpr (CODE == kCode1Mad)
         return code_1mad_raw(x);
-    else
+    else if constexpr (CODE == kCode3Inst)
         return (float)code_3inst_raw(x);
+    else
+        return code_xor(x, ca);
 }
 
 template <int CODE>
@@ -116,17 +153,21 @@ __device__ __forceinline__ float code_rescale(float v)
 {
     if constexpr (CODE == kCode1Mad)
         return rescale(v, k1MadRhi, k1MadRlo);
-    else
+    else if constexpr (CODE == kCode3Inst)
         return rescale(v, k3InstRhi, k3InstRlo);
+    else
+        return v;
 }
 
 template <int CODE>
-__device__ __forceinline__ float code_value(uint32_t x)
+__device__ __forceinline__ float code_value(uint32_t x, const CodeArg& ca)
 {
     if constexpr (CODE == kCode1Mad)
         return code_1mad(x);
-    else
+    else if constexpr (CODE == kCode3Inst)
         return code_3inst(x);
+    else
+        return code_xor(x, ca);
 }
 
 // Step error of the path cost: fl(fl(c - s)^2), optionally fl(w * that).  The build

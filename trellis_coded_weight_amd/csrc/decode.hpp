@@ -47,7 +47,7 @@ template <int L, int CODE, bool MSE_, bool WEIGHTED, bool TB = false>
 __global__ void __launch_bounds__(DecodeTile::kThreads)
 decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
             const float* __restrict__ wts, int64_t B, int T, int W, int SB,
-            float* __restrict__ recon, float* __restrict__ mse)
+            float* __restrict__ recon, float* __restrict__ mse, CodeArg ca)
 {
     constexpr int NT = DecodeTile::kThreads;
     // dynamic LDS, DecodeTile::lds_bytes: step errors [SB][err_stride] (MSE only), then
@@ -102,7 +102,7 @@ decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
                 win = ((((p & 31) ? top : hi) >> (32 - nf)) << (L - nf)) | (head >> (32 - (L - nf)));
             }
         }
-        const float c = code_value<CODE>(win);
+        const float c = code_value<CODE>(win, ca);
         if (recon) __builtin_nontemporal_store(c, recon + base + i);
         if constexpr (MSE_) lerr[r * ES + t] = step_err<WEIGHTED>(c, sv[u], wv[u]);
         r += dr;
@@ -131,10 +131,10 @@ decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
 // Code table: out[x] = code(x) for x < n.
 template <int CODE>
 __global__ void __launch_bounds__(256)
-code_table_kernel(float* __restrict__ out, int64_t n)
+code_table_kernel(float* __restrict__ out, int64_t n, CodeArg ca)
 {
     const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (x < n) out[x] = code_value<CODE>((uint32_t)x);
+    if (x < n) out[x] = code_value<CODE>((uint32_t)x, ca);
 }
 
 }  // namespace qtcq

@@ -8,7 +8,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qtcq.h"
+#include "codes.hpp"
 
 namespace qtcq {
 namespace host {
@@ -20,7 +23,6 @@ inline bool supported_trellis(int L, int k)
     return k == 2 && L >= 6 && L <= 16 && (L % 2) == 0;
 }
 
-inline bool valid_code(int code) { return code == QTCQ_CODE_1MAD || code == QTCQ_CODE_3INST; }
 
 inline int64_t stream_words(int L, int k, int T)
 {
@@ -64,40 +66,92 @@ inline size_t encode_bytes_per_seq(int T, int L)
 
 inline size_t tb_bytes_per_seq(int T, int L) { return encode_bytes_per_seq(T, L) + 4; }
 
-// L dispatch: instantiate every supported trellis size.
-template <template <int> class F, typename... Args>
-inline qtcq_status by_L(int L, Args&&... args)
+// A code as the launch units take it: its id (kCode1Mad, kCode3Inst, kCodeXor) and its
+// run-time parameters (the XOR palette code's parity masks).
+struct CodeSel {
+    int id;
+    CodeArg arg;
+};
+
+template <int V> using int_c = std::integral_constant<int, V>;
+template <bool V> using bool_c = std::integral_constant<bool, V>;
+
+// f(int_c<L>{}, int_c<CODE>{}) for every supported trellis size and code: the one place
+// where run-time (L, code) become template arguments.
+template <typename F>
+inline qtcq_status with_L_code(int L, int code, F&& f)
 {
+    auto by_code = [&](auto l) -> qtcq_status {
+        switch (code) {
+        case kCode1Mad: return f(l, int_c<kCode1Mad>{});
+        case kCode3Inst: return f(l, int_c<kCode3Inst>{});
+        case kCodeXor: return f(l, int_c<kCodeXor>{});
+        default: return QTCQ_ERR_UNSUPPORTED;
+        }
+    };
     switch (L) {
-    case 6: return F<6>::run(args...);
-    case 8: return F<8>::run(args...);
-    case 10: return F<10>::run(args...);
-    case 12: return F<12>::run(args...);
-    case 14: return F<14>::run(args...);
-    case 16: return F<16>::run(args...);
+    case 6: return by_code(int_c<6>{});
+    case 8: return by_code(int_c<8>{});
+    case 10: return by_code(int_c<10>{});
+    case 12: return by_code(int_c<12>{});
+    case 14: return by_code(int_c<14>{});
+    case 16: return by_code(int_c<16>{});
     default: return QTCQ_ERR_UNSUPPORTED;
     }
 }
 
+// f(bool_c<b>{})
+template <typename F>
+inline qtcq_status with_bool(bool b, F&& f)
+{
+    return b ? f(bool_c<true>{}) : f(bool_c<false>{});
+}
+
+// The code descriptor of the C ABI (qtcq.h): the id in bits 0-7 and, for the XOR
+// palette code, four 14-bit parity masks at bits 8, 22, 36 and 50.  Fills *out and
+// returns QTCQ_OK; QTCQ_ERR_UNSUPPORTED for an unknown id or parameter bits on a code
+// that takes none; QTCQ_ERR_INVALID_ARG for an XOR code whose masks reach beyond the
+// L - 2 history bits (or L < 2).
+inline qtcq_status parse_code(qtcq_code code, int L, CodeSel* out)
+{
+    const uint64_t id = code & 0xFFu;
+    const uint64_t params = code >> 8;
+    out->arg = CodeArg{{0u, 0u, 0u, 0u}};
+    if (id == QTCQ_CODE_1MAD || id == QTCQ_CODE_3INST) {
+        if (params != 0) return QTCQ_ERR_UNSUPPORTED;
+        out->id = id == QTCQ_CODE_1MAD ? kCode1Mad : kCode3Inst;
+        return QTCQ_OK;
+    }
+    if (id != QTCQ_CODE_XOR) return QTCQ_ERR_UNSUPPORTED;
+    if (L < 2) return QTCQ_ERR_INVALID_ARG;
+    out->id = kCodeXor;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t m = (uint32_t)((params >> (14 * i)) & 0x3FFFu);
+        if (L - 2 < 14 && (m >> (L - 2)) != 0) return QTCQ_ERR_INVALID_ARG;
+        out->arg.m[i] = m;
+    }
+    return QTCQ_OK;
+}
+
 // ---- launch entry points (arguments validated by the caller) -------------------------
 // launch_encode.hip
-qtcq_status launch_viterbi_encode(int L, int code, bool weighted, const float* seq, const float* w,
+qtcq_status launch_viterbi_encode(int L, const CodeSel& code, bool weighted, const float* seq, const float* w,
                            int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
                            void* ws, size_t wsb, hipStream_t st);
-qtcq_status launch_tailbiting_encode(int L, int code, bool weighted, const float* seq, const float* w,
+qtcq_status launch_tailbiting_encode(int L, const CodeSel& code, bool weighted, const float* seq, const float* w,
                               int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
                               void* ws, size_t wsb, hipStream_t st);
 // launch_decode.hip
-qtcq_status launch_decode(int L, int code, bool tb, const uint32_t* bits, int64_t B, int T, float* recon,
+qtcq_status launch_decode(int L, const CodeSel& code, bool tb, const uint32_t* bits, int64_t B, int T, float* recon,
                    const float* seq, const float* w, float* mse, hipStream_t st);
-qtcq_status launch_code_table(int code, int L, float* out, hipStream_t st);
+qtcq_status launch_code_table(const CodeSel& code, int L, float* out, hipStream_t st);
 // launch_bcjr.hip
 size_t bcjr_seq_bytes(int T, int L, bool vjp);
-qtcq_status launch_bcjr_soft(int L, int code, bool weighted, const float* seq, const float* w, int64_t B,
+qtcq_status launch_bcjr_soft(int L, const CodeSel& code, bool weighted, const float* seq, const float* w, int64_t B,
                       int T, float temperature, float* soft, float* log_z, void* ws, size_t wsb,
                       hipStream_t st);
 // launch_vjp.hip
-qtcq_status launch_bcjr_vjp(int L, int code, bool weighted, const float* seq, const float* w,
+qtcq_status launch_bcjr_vjp(int L, const CodeSel& code, bool weighted, const float* seq, const float* w,
                      const float* gup, int64_t B, int T, float temperature, float* grad,
                      float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st);
 // launch_matvec.hip
@@ -105,9 +159,9 @@ int matvec_max_batch();
 int matvec_mfma_max_batch();
 int matvec_mfma_max_n();
 size_t matvec_mfma_workspace_bytes(int N);
-qtcq_status launch_decode_matvec(int L, int code, bool tb, const uint32_t* bits, int M, int N,
+qtcq_status launch_decode_matvec(int L, const CodeSel& code, bool tb, const uint32_t* bits, int M, int N,
                           const float* x, int batch, float* y, hipStream_t st);
-qtcq_status launch_decode_matvec_mfma(int L, int code, bool tb, const uint32_t* bits, int M, int N,
+qtcq_status launch_decode_matvec_mfma(int L, const CodeSel& code, bool tb, const uint32_t* bits, int M, int N,
                                const float* x, int batch, float* y, void* ws, hipStream_t st);
 qtcq_status launch_split_x(const float* x, int N, int batch, void* ws, hipStream_t st);
 

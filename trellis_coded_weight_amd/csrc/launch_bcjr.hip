@@ -1,6 +1,5 @@
 // launch_bcjr.hip -- launches of the BCJR soft pass and its finalize (bcjr.hpp).
 #include "host.hpp"
-#include "codes.hpp"
 #include "viterbi.hpp"
 #include "bcjr.hpp"
 
@@ -12,7 +11,8 @@ static_assert(kMaxT <= kBcjrMaxT, "the BCJR kernels stage T per-step values in L
 
 template <int L, int CODE, bool W>
 qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float temperature,
-                     float* soft, float* log_z, void* ws, size_t ws_bytes, hipStream_t st)
+                     float* soft, float* log_z, void* ws, size_t ws_bytes, const CodeArg& ca,
+                     hipStream_t st)
 {
     using Tr = Trellis<L>;
     const size_t per = BcjrLayout<L>::bytes_per_seq(T);
@@ -22,7 +22,7 @@ qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float t
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
         hipLaunchKernelGGL((bcjr_sweep<L, CODE, W>), dim3((unsigned)n), dim3(Tr::kThreads), 0, st,
-                           seq, w, T, b0, kappa, wsc);
+                           seq, w, T, b0, kappa, wsc, ca);
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
         hipLaunchKernelGGL((bcjr_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
@@ -33,34 +33,20 @@ qtcq_status bcjr_all(const float* seq, const float* w, int64_t B, int T, float t
     return QTCQ_OK;
 }
 
-template <int L>
-qtcq_status bcjr_dispatch_code(int code, bool weighted, const float* seq, const float* w,
-                               int64_t B, int T, float temperature, float* soft, float* log_z,
-                               void* ws, size_t wsb, hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return weighted ? bcjr_all<L, kCode1Mad, true>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st)
-                        : bcjr_all<L, kCode1Mad, false>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st);
-    return weighted ? bcjr_all<L, kCode3Inst, true>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st)
-                    : bcjr_all<L, kCode3Inst, false>(seq, w, B, T, temperature, soft, log_z, ws, wsb, st);
-}
-
-
-template <int L>
-struct BcjrF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return bcjr_dispatch_code<L>(a...); }
-};
-
 }  // namespace
 
 size_t bcjr_seq_bytes(int T, int L, bool vjp) { return bcjr_bytes_per_seq(T, L, vjp); }
 
-qtcq_status launch_bcjr_soft(int L, int code, bool weighted, const float* seq, const float* w, int64_t B,
-                      int T, float temperature, float* soft, float* log_z, void* ws, size_t wsb,
-                      hipStream_t st)
+qtcq_status launch_bcjr_soft(int L, const CodeSel& code, bool weighted, const float* seq,
+                             const float* w, int64_t B, int T, float temperature, float* soft,
+                             float* log_z, void* ws, size_t wsb, hipStream_t st)
 {
-    return by_L<BcjrF>(L, code, weighted, seq, w, B, T, temperature, soft, log_z, ws, wsb, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(weighted, [&](auto wt) {
+            return bcjr_all<decltype(l)::value, decltype(c)::value, decltype(wt)::value>(
+                seq, w, B, T, temperature, soft, log_z, ws, wsb, code.arg, st);
+        });
+    });
 }
 
 }  // namespace host

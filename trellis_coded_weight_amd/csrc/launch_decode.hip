@@ -1,6 +1,5 @@
 // launch_decode.hip -- launches of the window decode and the code table (decode.hpp).
 #include "host.hpp"
-#include "codes.hpp"
 #include "decode.hpp"
 
 namespace qtcq {
@@ -9,7 +8,7 @@ namespace {
 
 template <int L, int CODE, bool TB>
 qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, const float* seq,
-                        const float* w, float* mse, hipStream_t st)
+                        const float* w, float* mse, const CodeArg& ca, hipStream_t st)
 {
     const int Wd = (int)(TB ? tb_stream_words(2, T) : stream_words(L, 2, T));
     const int SB = DecodeTile::seqs(T);
@@ -19,51 +18,47 @@ qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, co
     const size_t lds = DecodeTile::lds_bytes(T, Wd, mse != nullptr);
     if (!mse)
         hipLaunchKernelGGL((decode_tile<L, CODE, false, false, TB>), grid, block, lds, st, bits,
-                           seq, w, B, T, Wd, SB, recon, mse);
+                           seq, w, B, T, Wd, SB, recon, mse, ca);
     else if (w)
         hipLaunchKernelGGL((decode_tile<L, CODE, true, true, TB>), grid, block, lds, st, bits, seq,
-                           w, B, T, Wd, SB, recon, mse);
+                           w, B, T, Wd, SB, recon, mse, ca);
     else
         hipLaunchKernelGGL((decode_tile<L, CODE, true, false, TB>), grid, block, lds, st, bits,
-                           seq, w, B, T, Wd, SB, recon, mse);
+                           seq, w, B, T, Wd, SB, recon, mse, ca);
     return launch_status();
 }
 
-template <int L>
-qtcq_status decode_dispatch_code(int code, bool tb, const uint32_t* bits, int64_t B, int T,
-                                 float* recon, const float* seq, const float* w, float* mse,
-                                 hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return tb ? decode_impl<L, kCode1Mad, true>(bits, B, T, recon, seq, w, mse, st)
-                  : decode_impl<L, kCode1Mad, false>(bits, B, T, recon, seq, w, mse, st);
-    return tb ? decode_impl<L, kCode3Inst, true>(bits, B, T, recon, seq, w, mse, st)
-              : decode_impl<L, kCode3Inst, false>(bits, B, T, recon, seq, w, mse, st);
-}
-
-template <int L>
-struct DecodeF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return decode_dispatch_code<L>(a...); }
-};
-
 }  // namespace
 
-qtcq_status launch_decode(int L, int code, bool tb, const uint32_t* bits, int64_t B, int T, float* recon,
-                   const float* seq, const float* w, float* mse, hipStream_t st)
+qtcq_status launch_decode(int L, const CodeSel& code, bool tb, const uint32_t* bits, int64_t B,
+                          int T, float* recon, const float* seq, const float* w, float* mse,
+                          hipStream_t st)
 {
-    return by_L<DecodeF>(L, code, tb, bits, B, T, recon, seq, w, mse, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(tb, [&](auto t) {
+            return decode_impl<decltype(l)::value, decltype(c)::value, decltype(t)::value>(
+                bits, B, T, recon, seq, w, mse, code.arg, st);
+        });
+    });
 }
 
-qtcq_status launch_code_table(int code, int L, float* out, hipStream_t st)
+qtcq_status launch_code_table(const CodeSel& code, int L, float* out, hipStream_t st)
 {
     const int64_t n = (int64_t)1 << L;
-    if (code == QTCQ_CODE_1MAD)
-        hipLaunchKernelGGL((code_table_kernel<kCode1Mad>), dim3(blocks_for(n, 256)), dim3(256), 0, st,
-                           out, n);
-    else
-        hipLaunchKernelGGL((code_table_kernel<kCode3Inst>), dim3(blocks_for(n, 256)), dim3(256), 0, st,
-                           out, n);
+    const dim3 grid(blocks_for(n, 256)), block(256);
+    switch (code.id) {
+    case kCode1Mad:
+        hipLaunchKernelGGL((code_table_kernel<kCode1Mad>), grid, block, 0, st, out, n, code.arg);
+        break;
+    case kCode3Inst:
+        hipLaunchKernelGGL((code_table_kernel<kCode3Inst>), grid, block, 0, st, out, n, code.arg);
+        break;
+    case kCodeXor:
+        hipLaunchKernelGGL((code_table_kernel<kCodeXor>), grid, block, 0, st, out, n, code.arg);
+        break;
+    default:
+        return QTCQ_ERR_UNSUPPORTED;
+    }
     return launch_status();
 }
 

@@ -1,7 +1,6 @@
 // launch_encode.hip -- launches of the Viterbi search, its traceback and the
 // tail-biting encoder (viterbi.hpp): batch chunking over the caller's workspace.
 #include "host.hpp"
-#include "codes.hpp"
 #include "viterbi.hpp"
 
 namespace qtcq {
@@ -10,7 +9,8 @@ namespace {
 
 template <int L, int CODE, bool W>
 qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n, int T,
-                         uint32_t* bits, float* mse, uint32_t* states, char* ws, hipStream_t st)
+                         uint32_t* bits, float* mse, uint32_t* states, char* ws,
+                         const CodeArg& ca, hipStream_t st)
 {
     using Tr = Trellis<L>;
     uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
@@ -18,7 +18,7 @@ qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n
     float* fin_cost = reinterpret_cast<float*>(fin + n);
     const int per_wg = search_seqs_per_wg(n);
     hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3(blocks_for(n, per_wg)), dim3(Tr::kThreads),
-                       0, st, seq, w, T, b0, n, per_wg, 0, nullptr, bp, fin, fin_cost, mse);
+                       0, st, seq, w, T, b0, n, per_wg, 0, nullptr, bp, fin, fin_cost, mse, ca);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     const int Wd = (int)stream_words(L, 2, T);
@@ -29,13 +29,14 @@ qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n
 
 template <int L, int CODE, bool W>
 qtcq_status encode_all(const float* seq, const float* w, int64_t B, int T, uint32_t* bits,
-                       float* mse, uint32_t* states, void* ws, size_t ws_bytes, hipStream_t st)
+                       float* mse, uint32_t* states, void* ws, size_t ws_bytes, const CodeArg& ca,
+                       hipStream_t st)
 {
     const int64_t per_chunk = (int64_t)(ws_bytes / encode_bytes_per_seq(T, L));
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
         qtcq_status rc = encode_chunk<L, CODE, W>(seq, w, b0, n, T, bits, mse, states,
-                                                  static_cast<char*>(ws), st);
+                                                  static_cast<char*>(ws), ca, st);
         if (rc != QTCQ_OK) return rc;
     }
     return QTCQ_OK;
@@ -50,7 +51,8 @@ qtcq_status encode_all(const float* seq, const float* w, int64_t B, int T, uint3
 
 template <int L, int CODE, bool W>
 qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, int T,
-                     uint32_t* bits, float* mse, uint32_t* states, char* ws, hipStream_t st)
+                     uint32_t* bits, float* mse, uint32_t* states, char* ws, const CodeArg& ca,
+                     hipStream_t st)
 {
     using Tr = Trellis<L>;
     uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
@@ -61,7 +63,7 @@ qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, in
     const dim3 grid(blocks_for(n, per_wg)), block(Tr::kThreads);
     const int rot = T / 2;
     hipLaunchKernelGGL((viterbi_forward<L, CODE, W, false>), grid, block, 0, st, seq, w, T, b0, n,
-                       per_wg, rot, nullptr, bp, fin, fin_cost, nullptr);
+                       per_wg, rot, nullptr, bp, fin, fin_cost, nullptr, ca);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     hipLaunchKernelGGL((viterbi_seam<L>), dim3(blocks_for(n, 256)), dim3(256), 0, st, bp, fin, T, n,
@@ -69,7 +71,7 @@ qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, in
     rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     hipLaunchKernelGGL((viterbi_forward<L, CODE, W, true>), grid, block, 0, st, seq, w, T, b0, n,
-                       per_wg, 0, overlap, bp, fin, fin_cost, mse);
+                       per_wg, 0, overlap, bp, fin, fin_cost, mse, ca);
     rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     hipLaunchKernelGGL((viterbi_traceback<L, true>), dim3(blocks_for(n, 256)), dim3(256), 0, st,
@@ -79,68 +81,43 @@ qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, in
 
 template <int L, int CODE, bool W>
 qtcq_status tb_all(const float* seq, const float* w, int64_t B, int T, uint32_t* bits,
-                   float* mse, uint32_t* states, void* ws, size_t ws_bytes, hipStream_t st)
+                   float* mse, uint32_t* states, void* ws, size_t ws_bytes, const CodeArg& ca,
+                   hipStream_t st)
 {
     const int64_t per_chunk = (int64_t)(ws_bytes / tb_bytes_per_seq(T, L));
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
         qtcq_status rc = tb_chunk<L, CODE, W>(seq, w, b0, n, T, bits, mse, states,
-                                              static_cast<char*>(ws), st);
+                                              static_cast<char*>(ws), ca, st);
         if (rc != QTCQ_OK) return rc;
     }
     return QTCQ_OK;
 }
 
-template <int L>
-qtcq_status tb_dispatch_code(int code, bool weighted, const float* seq, const float* w,
-                             int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
-                             void* ws, size_t wsb, hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return weighted ? tb_all<L, kCode1Mad, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
-                        : tb_all<L, kCode1Mad, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
-    return weighted ? tb_all<L, kCode3Inst, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
-                    : tb_all<L, kCode3Inst, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
-}
-
-template <int L>
-qtcq_status encode_dispatch_code(int code, bool weighted, const float* seq, const float* w,
-                                 int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
-                                 void* ws, size_t wsb, hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return weighted ? encode_all<L, kCode1Mad, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
-                        : encode_all<L, kCode1Mad, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
-    return weighted ? encode_all<L, kCode3Inst, true>(seq, w, B, T, bits, mse, states, ws, wsb, st)
-                    : encode_all<L, kCode3Inst, false>(seq, w, B, T, bits, mse, states, ws, wsb, st);
-}
-
-template <int L>
-struct EncodeF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return encode_dispatch_code<L>(a...); }
-};
-
-template <int L>
-struct TailBitingF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return tb_dispatch_code<L>(a...); }
-};
-
 }  // namespace
 
-qtcq_status launch_viterbi_encode(int L, int code, bool weighted, const float* seq, const float* w,
-                           int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
-                           void* ws, size_t wsb, hipStream_t st)
+qtcq_status launch_viterbi_encode(int L, const CodeSel& code, bool weighted, const float* seq,
+                                  const float* w, int64_t B, int T, uint32_t* bits, float* mse,
+                                  uint32_t* states, void* ws, size_t wsb, hipStream_t st)
 {
-    return by_L<EncodeF>(L, code, weighted, seq, w, B, T, bits, mse, states, ws, wsb, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(weighted, [&](auto wt) {
+            return encode_all<decltype(l)::value, decltype(c)::value, decltype(wt)::value>(
+                seq, w, B, T, bits, mse, states, ws, wsb, code.arg, st);
+        });
+    });
 }
 
-qtcq_status launch_tailbiting_encode(int L, int code, bool weighted, const float* seq, const float* w,
-                              int64_t B, int T, uint32_t* bits, float* mse, uint32_t* states,
-                              void* ws, size_t wsb, hipStream_t st)
+qtcq_status launch_tailbiting_encode(int L, const CodeSel& code, bool weighted, const float* seq,
+                                     const float* w, int64_t B, int T, uint32_t* bits, float* mse,
+                                     uint32_t* states, void* ws, size_t wsb, hipStream_t st)
 {
-    return by_L<TailBitingF>(L, code, weighted, seq, w, B, T, bits, mse, states, ws, wsb, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(weighted, [&](auto wt) {
+            return tb_all<decltype(l)::value, decltype(c)::value, decltype(wt)::value>(
+                seq, w, B, T, bits, mse, states, ws, wsb, code.arg, st);
+        });
+    });
 }
 
 }  // namespace host

@@ -1,7 +1,6 @@
 // launch_matvec.hip -- launches of the decode -> matrix-vector products (matvec.hpp,
 // matvec_mfma.hpp).
 #include "host.hpp"
-#include "codes.hpp"
 #include "matvec.hpp"
 #include "matvec_mfma.hpp"
 
@@ -11,30 +10,19 @@ namespace {
 
 template <int L, int CODE, bool TB>
 qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int batch, float* y,
-                        hipStream_t st)
+                        const CodeArg& ca, hipStream_t st)
 {
     const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
     const dim3 grid((unsigned)(M / 16)), block(MatvecShape::kThreads);
     if (batch <= 1)
-        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, Wd, x, batch, y, ca);
     else if (batch <= 2)
-        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 2>), grid, block, 0, st, bits, M, N, Wd, x, batch, y, ca);
     else if (batch <= 4)
-        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 4>), grid, block, 0, st, bits, M, N, Wd, x, batch, y, ca);
     else
-        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 8>), grid, block, 0, st, bits, M, N, Wd, x, batch, y);
+        hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 8>), grid, block, 0, st, bits, M, N, Wd, x, batch, y, ca);
     return launch_status();
-}
-
-template <int L>
-qtcq_status matvec_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
-                                 const float* x, int batch, float* y, hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return tb ? matvec_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, st)
-                  : matvec_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, st);
-    return tb ? matvec_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, st)
-              : matvec_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, st);
 }
 
 // the split x of the matrix-core product: fragments, then block scales, in the workspace
@@ -60,7 +48,7 @@ qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream
 // nullptr: the workspace already holds the split of this (N, batch)
 template <int L, int CODE, bool TB>
 qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x, int batch,
-                             float* y, void* workspace, hipStream_t st)
+                             float* y, void* workspace, const CodeArg& ca, hipStream_t st)
 {
     static_assert(MatvecMfmaShape::stream_words<L, TB>() == (TB ? 16 : 17), "stream words");
     const int nf = MatvecMfmaShape::frags(batch);
@@ -78,7 +66,7 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
     const bool two = nf >= 3 && nb >= 1024;
     const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
 #define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \
-                                               bits, M, N, xs, sc, batch, y)
+                                               bits, M, N, xs, sc, batch, y, ca)
     switch (nf) {
     case 1: QTCQ_MV(1, 1, grid1); break;
     case 2: if (two) QTCQ_MV(2, 2, grid2); else QTCQ_MV(2, 1, grid1); break;
@@ -89,30 +77,6 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
     return launch_status();
 }
 
-template <int L>
-qtcq_status matvec_mfma_dispatch_code(int code, bool tb, const uint32_t* bits, int M, int N,
-                                      const float* x, int batch, float* y, void* workspace,
-                                      hipStream_t st)
-{
-    if (code == QTCQ_CODE_1MAD)
-        return tb ? matvec_mfma_impl<L, kCode1Mad, true>(bits, M, N, x, batch, y, workspace, st)
-                  : matvec_mfma_impl<L, kCode1Mad, false>(bits, M, N, x, batch, y, workspace, st);
-    return tb ? matvec_mfma_impl<L, kCode3Inst, true>(bits, M, N, x, batch, y, workspace, st)
-              : matvec_mfma_impl<L, kCode3Inst, false>(bits, M, N, x, batch, y, workspace, st);
-}
-
-template <int L>
-struct MatvecMfmaF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return matvec_mfma_dispatch_code<L>(a...); }
-};
-
-template <int L>
-struct MatvecF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return matvec_dispatch_code<L>(a...); }
-};
-
 }  // namespace
 
 int matvec_max_batch() { return MatvecShape::kMaxBatch; }
@@ -120,16 +84,27 @@ int matvec_mfma_max_batch() { return MatvecMfmaShape::kMaxBatch; }
 int matvec_mfma_max_n() { return MatvecMfmaShape::kMaxN; }
 size_t matvec_mfma_workspace_bytes(int N) { return MatvecMfmaShape::workspace_bytes(N); }
 
-qtcq_status launch_decode_matvec(int L, int code, bool tb, const uint32_t* bits, int M, int N,
-                          const float* x, int batch, float* y, hipStream_t st)
+qtcq_status launch_decode_matvec(int L, const CodeSel& code, bool tb, const uint32_t* bits, int M,
+                                 int N, const float* x, int batch, float* y, hipStream_t st)
 {
-    return by_L<MatvecF>(L, code, tb, bits, M, N, x, batch, y, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(tb, [&](auto t) {
+            return matvec_impl<decltype(l)::value, decltype(c)::value, decltype(t)::value>(
+                bits, M, N, x, batch, y, code.arg, st);
+        });
+    });
 }
 
-qtcq_status launch_decode_matvec_mfma(int L, int code, bool tb, const uint32_t* bits, int M, int N,
-                               const float* x, int batch, float* y, void* ws, hipStream_t st)
+qtcq_status launch_decode_matvec_mfma(int L, const CodeSel& code, bool tb, const uint32_t* bits,
+                                      int M, int N, const float* x, int batch, float* y, void* ws,
+                                      hipStream_t st)
 {
-    return by_L<MatvecMfmaF>(L, code, tb, bits, M, N, x, batch, y, ws, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(tb, [&](auto t) {
+            return matvec_mfma_impl<decltype(l)::value, decltype(c)::value, decltype(t)::value>(
+                bits, M, N, x, batch, y, ws, code.arg, st);
+        });
+    });
 }
 
 qtcq_status launch_split_x(const float* x, int N, int batch, void* ws, hipStream_t st)

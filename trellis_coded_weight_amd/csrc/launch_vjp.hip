@@ -1,7 +1,6 @@
 // launch_vjp.hip -- launches of the BCJR gradient: the soft pass in gradient mode,
 // the expectation-message sweep and the gradient finalize (bcjr.hpp, bcjr_vjp.hpp).
 #include "host.hpp"
-#include "codes.hpp"
 #include "viterbi.hpp"
 #include "bcjr.hpp"
 #include "bcjr_vjp.hpp"
@@ -10,17 +9,16 @@ namespace qtcq {
 namespace host {
 namespace {
 
-// ---- BCJR gradient (vector-Jacobian product) ------------------------------------------
 // Per chunk: the soft pass in VJP mode (stashes both message directions and the posterior
 // offsets), its finalize when soft / log Z are wanted, the Phi / Psi sweep, the gradient.
-// Below tau = 0.01 the stashes keep fp64 values (WIDE); the 32-bit stash's fp32 range
+// Below tau = 0.01 the stashes keep fp64 values (WIDE); the 32-bit stash's binary32 range
 // below -1024 log2 units is too coarse for the states the backward messages lift there.
 constexpr float kWideStashBelowTau = 0.01f;
 
 template <int L, int CODE, bool W, bool WIDE>
 qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t B, int T,
                     float temperature, float* grad, float* soft, float* log_z, void* ws,
-                    size_t ws_bytes, hipStream_t st)
+                    size_t ws_bytes, const CodeArg& ca, hipStream_t st)
 {
     using Tr = Trellis<L>;
     const size_t per = BcjrLayout<L>::bytes_per_seq_vjp(T);
@@ -31,7 +29,7 @@ qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t 
     for (int64_t b0 = 0; b0 < B; b0 += per_chunk) {
         const int64_t n = (B - b0 < per_chunk) ? B - b0 : per_chunk;
         hipLaunchKernelGGL((bcjr_sweep<L, CODE, W, true, WIDE>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
-                           st, seq, w, T, b0, kappa, wsc);
+                           st, seq, w, T, b0, kappa, wsc, ca);
         qtcq_status rc = launch_status();
         if (rc != QTCQ_OK) return rc;
         if (soft || log_z) {
@@ -41,7 +39,7 @@ qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t 
             if (rc != QTCQ_OK) return rc;
         }
         hipLaunchKernelGGL((bcjr_vjp_sweep<L, CODE, W, WIDE>), dim3((unsigned)n), dim3(Tr::kThreads), 0,
-                           st, seq, w, gup, T, b0, kappa, wsc);
+                           st, seq, w, gup, T, b0, kappa, wsc, ca);
         rc = launch_status();
         if (rc != QTCQ_OK) return rc;
         hipLaunchKernelGGL((bcjr_vjp_finalize<L>), dim3(blocks_for(n * T, 256)), dim3(256), 0, st,
@@ -52,34 +50,22 @@ qtcq_status vjp_all(const float* seq, const float* w, const float* gup, int64_t 
     return QTCQ_OK;
 }
 
-template <int L>
-qtcq_status vjp_dispatch_code(int code, bool weighted, const float* seq, const float* w,
-                              const float* gup, int64_t B, int T, float temperature, float* grad,
-                              float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st)
-{
-#define QTCQ_VJP(C_, W_) (temperature < kWideStashBelowTau                                              \
-        ? vjp_all<L, C_, W_, true>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st)      \
-        : vjp_all<L, C_, W_, false>(seq, w, gup, B, T, temperature, grad, soft, log_z, ws, wsb, st))
-    if (code == QTCQ_CODE_1MAD)
-        return weighted ? QTCQ_VJP(kCode1Mad, true) : QTCQ_VJP(kCode1Mad, false);
-    return weighted ? QTCQ_VJP(kCode3Inst, true) : QTCQ_VJP(kCode3Inst, false);
-#undef QTCQ_VJP
-}
-
-template <int L>
-struct VjpF {
-    template <typename... A>
-    static qtcq_status run(A... a) { return vjp_dispatch_code<L>(a...); }
-};
-
 }  // namespace
 
-qtcq_status launch_bcjr_vjp(int L, int code, bool weighted, const float* seq, const float* w,
-                     const float* gup, int64_t B, int T, float temperature, float* grad,
-                     float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st)
+qtcq_status launch_bcjr_vjp(int L, const CodeSel& code, bool weighted, const float* seq,
+                            const float* w, const float* gup, int64_t B, int T, float temperature,
+                            float* grad, float* soft, float* log_z, void* ws, size_t wsb,
+                            hipStream_t st)
 {
-    return by_L<VjpF>(L, code, weighted, seq, w, gup, B, T, temperature, grad, soft, log_z, ws,
-                      wsb, st);
+    return with_L_code(L, code.id, [&](auto l, auto c) {
+        return with_bool(weighted, [&](auto wt) {
+            return with_bool(temperature < kWideStashBelowTau, [&](auto wide) {
+                return vjp_all<decltype(l)::value, decltype(c)::value, decltype(wt)::value,
+                               decltype(wide)::value>(seq, w, gup, B, T, temperature, grad, soft,
+                                                      log_z, ws, wsb, code.arg, st);
+            });
+        });
+    });
 }
 
 }  // namespace host

@@ -53,7 +53,7 @@ struct MatvecShape {
 template <int L, int CODE, bool TB, int NB>
 __global__ void __launch_bounds__(MatvecShape::kThreads)
 decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
-              const float* __restrict__ x, int batch, float* __restrict__ y)
+              const float* __restrict__ x, int batch, float* __restrict__ y, CodeArg ca)
 {
     constexpr int NJS = MatvecShape::kJSlots;
     static_assert(NB >= 1 && NB <= MatvecShape::kMaxBatch, "batch width");
@@ -102,7 +102,7 @@ decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
             float wv[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                wv[b] = code_raw<CODE>((f >> (32 - L - 2 * b)) & ((1u << L) - 1u));
+                wv[b] = code_raw<CODE>((f >> (32 - L - 2 * b)) & ((1u << L) - 1u), ca);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 acc[a][i] = __builtin_fmaf(wv[0], xv[i].x, acc[a][i]);

@@ -154,9 +154,13 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t c)
 // Two windows' codes before their rescale, as one packed pair of fp16.
 //   kbias: fp16 -1534 in both halves, in a VGPR
 template <int CODE>
-__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, uint32_t kbias)
+__device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, uint32_t kbias,
+                                                      const CodeArg& ca)
 {
-    if constexpr (CODE == kCode1Mad) {
+    if constexpr (CODE == kCodeXor) {
+        // palette values, exact in fp16 (so the round-toward-zero pack is exact)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(code_xor(w0, ca), code_xor(w1, ca)));
+    } else if constexpr (CODE == kCode1Mad) {
         // byte sums into both halves of an accumulator 0x64006400 (fp16 1024 twice):
         // v_sad_u8 adds S0 to the low half, v_sad_hi_u8 adds S1 << 16, so the halves read
         // 1024 + S0 and 1024 + S1 exactly (S <= 1020, no carry between them); one packed
@@ -185,7 +189,7 @@ template <int L, int CODE, bool TB, int NF, int BANDS>
 __global__ void __launch_bounds__(MatvecMfmaShape::kThreads)
 decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
                    const uint4* __restrict__ xs, const float* __restrict__ sc, int batch,
-                   float* __restrict__ y)
+                   float* __restrict__ y, CodeArg ca)
 {
     constexpr int NW = MatvecMfmaShape::kWaves;
     constexpr int Wd = MatvecMfmaShape::stream_words<L, TB>();
@@ -296,7 +300,7 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
             for (int p = 0; p < 4; ++p) {
                 const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
                 const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
-                a[p] = code_raw_pair_f16<CODE>(w0, w1, kbias);
+                a[p] = code_raw_pair_f16<CODE>(w0, w1, kbias, ca);
             }
             av[b] = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         }

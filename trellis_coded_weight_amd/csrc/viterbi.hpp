@@ -104,6 +104,7 @@ constexpr int kBitDelay = 1;
 //   bp       : [n][T-1][kBpWords] 2-bit argmins of each step
 //   fin      : [n] final state (uint32) ; fin_cost [n]
 //   mse      : [*] (row b0 + q) or nullptr
+//   ca       : the code's run-time parameters
 // The two sequences A and B are interleaved so that LDS latency hides behind
 // arithmetic: each phase loads one sequence's inputs while it computes the other's
 // step, with one barrier per phase.  Each sequence has a single 64 KiB buffer of group
@@ -115,7 +116,7 @@ __global__ void __launch_bounds__(Trellis<L>::kThreads)
 viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
                 int64_t n, int per_wg, int rot, const uint32_t* __restrict__ pin,
                 uint32_t* __restrict__ bp, uint32_t* __restrict__ fin, float* __restrict__ fin_cost,
-                float* __restrict__ mse)
+                float* __restrict__ mse, CodeArg ca)
 {
     using Tr = Trellis<L>;
     constexpr int NB = Tr::kButterflies;
@@ -144,7 +145,7 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x));
+                Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x), ca);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
