@@ -23,7 +23,8 @@
  *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
  *    row-major and contiguous; [B][T] means sequence b's element t at b*T + t.
  *  - The caller owns every buffer.  The library allocates no device memory and keeps
- *    no mutable global state; calls on different streams may run concurrently as long
+ *    no mutable global state, with one exception (qtcq_decode_matvec_mfma_noalloc's
+ *    per-device scratch array); calls on different streams may run concurrently as long
  *    as their output and workspace buffers do not overlap.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued on it and the call returns without synchronising; outputs are valid
@@ -335,6 +336,29 @@ qtcq_status qtcq_decode_matvec_mfma_presplit(const uint32_t* bits, int M, int N,
                                              qtcq_code code, int tailbiting, const void* split,
                                              size_t split_bytes, int batch, float* y,
                                              void* stream);
+
+/* ---- Without allocation -------------------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace -- code under HIP
+ * graph capture with a fixed memory plan, tight serving loops, harnesses that forbid
+ * hipMalloc: qtcq_decode_matvec_mfma with the split x in a scratch array the library
+ * holds on each GPU instead of a caller workspace.  Same arguments, kernels and results
+ * (bit for bit) as qtcq_decode_matvec_mfma without the workspace; the caller still owns
+ * x and y.  The call itself allocates nothing: the array is a static device array of
+ * QTCQ_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU holds from the library's load until
+ * the process ends; its address on a device is looked up once, on the first call made
+ * with that device current.
+ *  - Limit: the split of x must fit the array, which holds N up to 63,520 columns at any
+ *    batch up to 32; larger N returns QTCQ_ERR_WORKSPACE before anything is launched.
+ *  - Every call on one GPU shares that GPU's array and leaves its split there: calls
+ *    that overlap on one GPU (different streams, or different host threads on one
+ *    stream without ordering) race and give undefined results.  Order them, or use
+ *    qtcq_decode_matvec_mfma with a workspace per stream.
+ * Errors: as qtcq_decode_matvec_mfma (no workspace errors besides the limit), and
+ * QTCQ_ERR_DEVICE if the array's address cannot be looked up. */
+#define QTCQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+qtcq_status qtcq_decode_matvec_mfma_noalloc(const uint32_t* bits, int M, int N, int L, int k,
+                                            qtcq_code code, int tailbiting, const float* x,
+                                            int batch, float* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,8 @@ _SIGS = {
     "qtcq_decode_matvec_mfma": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp, _int, _vp,
                                        _vp, _sz, _vp]),
     "qtcq_matvec_mfma_split_x": (_int, [_vp, _int, _int, _vp, _sz, _vp]),
+    "qtcq_decode_matvec_mfma_noalloc": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp,
+                                               _int, _vp, _vp]),
     "qtcq_decode_matvec_mfma_presplit": (_int, [_vp, _int, _int, _int, _int, _code, _int, _vp,
                                                 _sz, _int, _vp, _vp]),
     "qtcq_tailbiting_words": (_i64, [_int, _int, _int]),
@@ -219,3 +221,15 @@ def qtcq_decode_matvec_mfma_presplit(bits: int, M: int, N: int, L: int, k: int, 
                                                  1 if tailbiting else 0, _ptr(split), split_bytes,
                                                  batch, _ptr(y), _ptr(stream)),
            "qtcq_decode_matvec_mfma_presplit")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def qtcq_decode_matvec_mfma_noalloc(bits: int, M: int, N: int, L: int, k: int, code: int,
+                                    tailbiting: bool, x: int, batch: int, y: int,
+                                    stream: int = 0) -> None:
+    _check(_lib.qtcq_decode_matvec_mfma_noalloc(_ptr(bits), M, N, L, k, code,
+                                                1 if tailbiting else 0, _ptr(x), batch, _ptr(y),
+                                                _ptr(stream)),
+           "qtcq_decode_matvec_mfma_noalloc")

@@ -362,3 +362,28 @@ def decode_matvec_mfma_presplit(bits: torch.Tensor, M: int, N: int, split: Split
                                          split.workspace.data_ptr(), sp_bytes, split.batch,
                                          y.data_ptr(), _stream())
     return y
+
+
+def decode_matvec_mfma_noalloc(bits: torch.Tensor, M: int, N: int, x: torch.Tensor,
+                               out: torch.Tensor, L: int = 16, k: int = 2, code="1mad",
+                               tailbiting: bool = False) -> torch.Tensor:
+    """decode_matvec_mfma with the split x in the library's per-device scratch array: no
+    workspace, and nothing allocated here either -- the caller passes the output `out`
+    ([batch][M] float32, or [M] for a 1-D x).  Calls that overlap on one GPU race."""
+    one = x.dim() == 1
+    x2 = x.reshape(1, -1) if one else x
+    _dev_f32(x2, "x")
+    if x2.shape[1] != N:
+        raise ValueError("x must have N columns")
+    W = tailbiting_words(L, k, 256) if tailbiting else bitstream_words(L, k, 256)
+    if not (bits.is_cuda and bits.is_contiguous() and bits.element_size() == 4
+            and bits.numel() == (M // 16) * (N // 16) * W):
+        raise ValueError("bits must hold (M/16)*(N/16) contiguous streams of %d words" % W)
+    _on_current_device(bits, "bits")
+    o2 = out.reshape(1, -1) if one else out
+    _dev_f32(o2, "out")
+    if tuple(o2.shape) != (x2.shape[0], M):
+        raise ValueError("out must be [batch][M]")
+    nat.qtcq_decode_matvec_mfma_noalloc(bits.data_ptr(), M, N, L, k, _code(code), tailbiting,
+                                        x2.data_ptr(), x2.shape[0], o2.data_ptr(), _stream())
+    return out

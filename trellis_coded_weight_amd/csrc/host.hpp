@@ -163,6 +163,12 @@ qtcq_status launch_decode_matvec(int L, const CodeSel& code, bool tb, const uint
                           const float* x, int batch, float* y, hipStream_t st);
 qtcq_status launch_decode_matvec_mfma(int L, const CodeSel& code, bool tb, const uint32_t* bits, int M, int N,
                                const float* x, int batch, float* y, void* ws, hipStream_t st);
+// the same product with the split x in the library's per-device scratch array
+// (kNoAllocScratchBytes; QTCQ_ERR_WORKSPACE when the split of N needs more)
+constexpr size_t kNoAllocScratchBytes = QTCQ_NOALLOC_SCRATCH_BYTES;
+qtcq_status launch_decode_matvec_mfma_noalloc(int L, const CodeSel& code, bool tb,
+                                              const uint32_t* bits, int M, int N, const float* x,
+                                              int batch, float* y, hipStream_t st);
 qtcq_status launch_split_x(const float* x, int N, int batch, void* ws, hipStream_t st);
 
 }  // namespace host

@@ -1,5 +1,7 @@
 // launch_matvec.hip -- launches of the decode -> matrix-vector products (matvec.hpp,
 // matvec_mfma.hpp).
+#include <mutex>
+
 #include "host.hpp"
 #include "matvec.hpp"
 #include "matvec_mfma.hpp"
@@ -77,6 +79,39 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
     return launch_status();
 }
 
+// ---- the matrix-core product without allocation ---------------------------------------
+// For callers that cannot allocate device memory (graph capture with a fixed memory
+// plan, serving loops): the split x lives in this file-scope device array instead of a
+// caller workspace.  Every GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host it is a
+// stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, resolved once per device, with that device current, on the first
+// call there.
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kNoAllocMaxDevices];
+
+// the current device's scratch address, or nullptr (device index out of range, or the
+// symbol lookup failed)
+void* scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot]() {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess) slot.ptr = p;
+    });
+    return slot.err == hipSuccess ? slot.ptr : nullptr;
+}
+
 }  // namespace
 
 int matvec_max_batch() { return MatvecShape::kMaxBatch; }
@@ -105,6 +140,16 @@ qtcq_status launch_decode_matvec_mfma(int L, const CodeSel& code, bool tb, const
                 bits, M, N, x, batch, y, ws, code.arg, st);
         });
     });
+}
+
+qtcq_status launch_decode_matvec_mfma_noalloc(int L, const CodeSel& code, bool tb,
+                                              const uint32_t* bits, int M, int N, const float* x,
+                                              int batch, float* y, hipStream_t st)
+{
+    if (MatvecMfmaShape::workspace_bytes(N) > kNoAllocScratchBytes) return QTCQ_ERR_WORKSPACE;
+    void* ws = scratch_for_current_device();
+    if (!ws) return QTCQ_ERR_DEVICE;
+    return launch_decode_matvec_mfma(L, code, tb, bits, M, N, x, batch, y, ws, st);
 }
 
 qtcq_status launch_split_x(const float* x, int N, int batch, void* ws, hipStream_t st)

@@ -210,6 +210,22 @@ qtcq_status qtcq_decode_matvec_mfma(const uint32_t* bits, int M, int N, int L, i
                              as_stream(stream));
 }
 
+qtcq_status qtcq_decode_matvec_mfma_noalloc(const uint32_t* bits, int M, int N, int L, int k,
+                                            qtcq_code code, int tailbiting, const float* x,
+                                            int batch, float* y, void* stream)
+{
+    if (M < 0 || N < 0 || (M % 16) != 0 || (N % 16) != 0 || batch < 0) return QTCQ_ERR_INVALID_ARG;
+    if (!supported_trellis(L, k)) return QTCQ_ERR_UNSUPPORTED;
+    CodeSel cs;
+    if (const qtcq_status pc = parse_code(code, L, &cs); pc != QTCQ_OK) return pc;
+    if (batch > host::matvec_mfma_max_batch() || N > host::matvec_mfma_max_n()) return QTCQ_ERR_UNSUPPORTED;
+    if (host::matvec_mfma_workspace_bytes(N) > host::kNoAllocScratchBytes) return QTCQ_ERR_WORKSPACE;
+    if (M == 0 || batch == 0) return QTCQ_OK;
+    if (!y || (N > 0 && (!x || !aligned16(x) || !bits))) return QTCQ_ERR_INVALID_ARG;
+    return host::launch_decode_matvec_mfma_noalloc(L, cs, tailbiting != 0, bits, M, N, x, batch, y,
+                                                   as_stream(stream));
+}
+
 qtcq_status qtcq_matvec_mfma_split_x(const float* x, int N, int batch, void* workspace,
                                      size_t workspace_bytes, void* stream)
 {
