@@ -2,9 +2,12 @@
 // for the CPU by the test suite: the same inline functions the kernels call.
 //   - next_up(x) is the next binary32 above x (no float in between), for x of both signs,
 //     zero, subnormals and the largest finite values;
-//   - to_fix codes: fixed point (<= 0) exactly for v in [-1024, 0], tail codes (> 0) below;
+//   - to_fix codes, read as unsigned: fixed point (0 .. 2^31) exactly for v in [-1024, 0],
+//     tail codes (above 2^31) below; to_fix(0) = kFixZero;
 //   - round trip: |from_fix(to_fix(v)) - v| <= 2^-22 in the fixed range and
 //     <= 2^-24 (-1024 - v) (binary32 rounding of the distance) below it;
+//   - the kernels' decode from_fix_shifted is the value plus kStashShift (exactly in the
+//     fixed range, to one fp64 rounding in the tail);
 //   - from_fix(to_fix(.)) is non-decreasing across the boundary at -1024.
 // Prints "ok" and exits 0, or prints the first failure and exits 1.
 #include <hip/hip_runtime.h>
@@ -49,16 +52,23 @@ int main()
         vs.push_back(-1024.0 - std::ldexp(1.0, -(int)(rng() % 40)) * (double)(rng() >> 11) * 0x1p-53);
         vs.push_back(-1024.0 + std::ldexp(1.0, -(int)(rng() % 40)) * (double)(rng() >> 11) * 0x1p-53);
     }
+    if (to_fix(0.0) != qtcq::kFixZero || from_fix(qtcq::kFixZero) != 0.0)
+        return fail("zero", 0.0, from_fix(qtcq::kFixZero), 0.0);
     for (double v : vs) {
         const int q = to_fix(v);
+        const uint32_t u = (uint32_t)q;
         const double r = from_fix(q);
+        const double rs = qtcq::from_fix_shifted(q);
         if (v >= -1024.0) {
-            if (q > 0) return fail("fixed code sign", v, q, 0);
+            if (u > 0x80000000u) return fail("fixed code range", v, u, 0x80000000u);
             if (std::fabs(r - v) > 0x1p-22) return fail("fixed round trip", v, r, 0x1p-22);
+            if (rs - qtcq::kStashShift != r) return fail("fixed shifted decode", v, rs, r);
         } else {
-            if (q <= 0) return fail("tail code sign", v, q, 0);
+            if (u <= 0x80000000u) return fail("tail code range", v, u, 0x80000000u);
             const double bound = 0x1p-24 * (-1024.0 - v);
             if (std::fabs(r - v) > bound) return fail("tail round trip", v, r, bound);
+            if (std::fabs((rs - qtcq::kStashShift) - r) > 0x1p-52 * std::fabs(v))
+                return fail("tail shifted decode", v, rs, r);
         }
     }
     // monotone across the boundary

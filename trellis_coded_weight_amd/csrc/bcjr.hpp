@@ -107,25 +107,35 @@ __host__ __device__ __forceinline__ float next_up(float x)
 }
 
 // Stash values (normalised messages, <= 0 since the normaliser rounds up) in 32 bits:
-//   v >= -1024: int32 units of 2^-21 log2, codes in [-2^31, 0] -- a uniform 2.4e-7
-//               resolution near the step's maximum, where a posterior term depends on it;
-//   v <  -1024: the binary32 bit pattern of -1024 - v (> 0), codes in [1, 0x7F800000] --
-//               an absolute precision of 2^-24 (-1024 - v), continuous with the fixed
-//               point at the boundary and fp32's relative precision far below it.
+//   v >= -1024: 2^31 + rint(v 2^21) -- units of 2^-21 log2, codes 0 .. 2^31: a uniform
+//               2.4e-7 resolution near the step's maximum, where a posterior term depends
+//               on it;
+//   v <  -1024: the binary32 bit pattern of v + 1024, a negative float (codes above
+//               2^31) -- an absolute precision of 2^-24 (-1024 - v), continuous with the
+//               fixed point at the boundary and fp32's relative precision far below it.
 // Far below the maximum a state can still matter at low temperature: its backward
 // message can lift it back, so the tail keeps finite, smoothly degrading values rather
-// than a clamp.
+// than a clamp.  Decoding gives v + kStashShift with a single conversion in either range
+// (from_fix_shifted); every caller folds the constant into an offset it subtracts anyway
+// or into a log-sum-exp, which a common shift leaves unchanged -- an explicit add here
+// costs the backward loops their register allocation.
 constexpr double kFixScale = 2097152.0;
+constexpr double kStashShift = 1024.0;
 __host__ __device__ __forceinline__ int to_fix(double v)
 {
-    if (v >= -1024.0) return (int)__builtin_rint(v * kFixScale);
-    return (int)__builtin_bit_cast(uint32_t, (float)(-1024.0 - v));
+    if (v >= -1024.0) return (int)(0x80000000u + (uint32_t)(int)__builtin_rint(v * kFixScale));
+    return (int)__builtin_bit_cast(uint32_t, (float)(v + kStashShift));
 }
-__host__ __device__ __forceinline__ double from_fix(int q)
+__host__ __device__ __forceinline__ double from_fix_shifted(int q)
 {
-    if (q <= 0) return (double)q * (1.0 / kFixScale);
-    return -1024.0 - (double)__builtin_bit_cast(float, (uint32_t)q);
+    const uint32_t u = (uint32_t)q;
+    if (u <= 0x80000000u) return (double)u * (1.0 / kFixScale);
+    return (double)__builtin_bit_cast(float, u);
 }
+// the code of 0 (= to_fix(0.0))
+constexpr int kFixZero = (int)0x80000000u;
+// the value itself (reference form; the kernels use from_fix_shifted)
+__host__ __device__ __forceinline__ double from_fix(int q) { return from_fix_shifted(q) - kStashShift; }
 
 // The wide stash of gradient mode at low temperature keeps the fp64 values themselves:
 // there a state whose forward message is thousands of log2 units below the step's
@@ -135,12 +145,17 @@ template <bool WIDE> struct StashVal;
 // The soft pass itself always reads the 32-bit form (so the soft codeword of a gradient
 // call is the soft pass's bit for bit at every temperature); the wide copy is written
 // alongside it for the gradient sweep.
+// get() returns the value plus kShift (the 32-bit form's decode, from_fix_shifted).
 template <> struct StashVal<false> {
     using T = int;
-    __device__ static double get(int q) { return from_fix(q); }
+    static constexpr int kZero = kFixZero;   // the stored form of 0
+    static constexpr double kShift = kStashShift;
+    __device__ static double get(int q) { return from_fix_shifted(q); }
 };
 template <> struct StashVal<true> {
     using T = double;
+    static constexpr double kZero = 0.0;
+    static constexpr double kShift = 0.0;
     __device__ static double get(double v) { return v; }
 };
 
@@ -299,6 +314,10 @@ struct PackedCodes {
     __device__ __forceinline__ void init(int tid, const CodeArg& ca)
     {
         constexpr int M = Trellis<L>::kGroups;
+        // the palette code of a state is the same function here as in the forward
+        // prologue: an opaque index keeps the compiler from carrying the prologue's values
+        // across the forward loop instead of recomputing them
+        if constexpr (CODE == kCodeXor) tid = keep(tid);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -308,6 +327,7 @@ struct PackedCodes {
                     const uint32_t j = (uint32_t)(a * M + 16 * tid + 4 * r + 2 * hx);
                     const float lo = code_raw<CODE>(j, ca), hi = code_raw<CODE>(j + 1, ca);
                     w[a][r][hx] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+                    if constexpr (CODE == kCodeXor) w[a][r][hx] = keep(w[a][r][hx]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
     }
@@ -383,6 +403,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 16 * tid + 4 * r + x), ca);
+                if constexpr (CODE == kCodeXor) Cv[a][r][x] = keep(Cv[a][r][x]);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
@@ -544,7 +565,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
         auto stash_at = [&](int a) -> int4 {
-            if (!produce) return make_int4(0, 0, 0, 0);
+            if (!produce) return make_int4(kFixZero, kFixZero, kFixZero, kFixZero);
             return xn_load<NT, VJP>(stash, (size_t)(t - 1), a, tid);
         };
         int4 xs_next = stash_at(0);
@@ -572,6 +593,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         H = uniform64(H + h64);                       // H_t
         const double Ot = uniform64(log2z - Gm - H);  // log2 Z - G_t - H_t
         if (VJP && tid == 0) ofs[t] = Ot;
+        const double OtS = uniform64(Ot + kStashShift);   // the stash decodes Xn + kStashShift
         Gm = uniform64(Gm - (double)gsh[t]);          // G_{t-1}
         const StepEnergy se = step_energy(t);
         float pg = 0.f, pc = 0.f;
@@ -606,7 +628,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     float qc = q[0] * cx[0];
 #pragma unroll
                     for (int x = 1; x < 4; ++x) qc = __builtin_fmaf(q[x], cx[x], qc);
-                    const double xo = from_fix(xsr[r]) - Ot;
+                    const double xo = from_fix_shifted(xsr[r]) - OtS;
                     const float pb = fast_exp2((float)(xo + m));
                     pg = __builtin_fmaf(pb, sq, pg);
                     pc = __builtin_fmaf(pb, qc, pc);

@@ -128,7 +128,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                 const float2 v = half(cur, rd(a), h);
                 phs[phi_slot(t - 1, a, h)] = v;
                 ph[a][0] = v.x; ph[a][1] = v.y;
-                Pair q{0, 0};
+                Pair q{SV::kZero, SV::kZero};   // Xn_0 = 0
                 if (t >= 2) q = x_pair(t - 1, a, h);
                 xq[a][0] = q.x; xq[a][1] = q.y;
             }
@@ -181,11 +181,11 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         const StepEnergy se = step_energy(u);
         const float gp = gu[u];
         const float sft = softs[u];
-        const double Ou = ofs[u];
+        const double OuS = ofs[u] + 2.0 * SV::kShift;
         float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
         // Xn_u and Phi_u of the groups (a, 4 tid + 2h + i), loaded one (h, a) ahead of use
         auto load_xp = [&](int h, int a, Pair& xq, float2& ph) {
-            xq = Pair{0, 0};   // Xn_0 = 0
+            xq = Pair{SV::kZero, SV::kZero};   // Xn_0 = 0
             if constexpr (PRODUCE) xq = x_pair(u, a, h);
             ph = phs[phi_slot(u, a, h)];
         };
@@ -247,7 +247,8 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                         s1 += qc;
                         t3 = __builtin_fmaf(qc, bk, t3);
                     }
-                    const float pb = fast_exp2((float)((SV::get(xqi[i]) - Ou) + m));
+                    // SV::get and m (through lq) both carry SV::kShift: OuS = O_u + 2 kShift
+                    const float pb = fast_exp2((float)((SV::get(xqi[i]) - OuS) + m));
                     S0 = __builtin_fmaf(pb, den, S0);
                     S1 = __builtin_fmaf(pb, s1, S1);
                     S2 = __builtin_fmaf(pb, __builtin_fmaf(phi[i], den, num), S2);

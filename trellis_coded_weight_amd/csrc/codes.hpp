@@ -97,18 +97,28 @@ __device__ __forceinline__ float code_3inst(uint32_t x)
 // palettes hold the FP4 values [-6, -1.5, 0, 2], [-4, -1, 0.5, 3], [-3, -0.5, 1, 4] and
 // [-2, 0, 1.5, 6], used as they are (exact in fp16 and binary32; a per-group scale of
 // the weights lies outside the trellis).  Here each value is stored doubled as a signed
-// byte, palette p in byte lanes 4p..4p+3 of a 128-bit constant.
+// byte, palette p in the four bytes of one 32-bit constant, entry e in byte e.
 __device__ __forceinline__ float code_xor(uint32_t x, const CodeArg& ca)
 {
     const uint32_t h = x >> 2;
     const uint32_t p = ((__builtin_popcount(h & ca.m[0]) & 1u) << 1) | (__builtin_popcount(h & ca.m[1]) & 1u);
     const uint32_t sh = ((__builtin_popcount(h & ca.m[2]) & 1u) << 1) | (__builtin_popcount(h & ca.m[3]) & 1u);
     const uint32_t e = (x & 3u) ^ sh;
-    constexpr uint64_t kPal01 = 0x0601FEF80400FDF4ull;   // 2 x [-6, -1.5, 0, 2], 2 x [-4, -1, 0.5, 3]
-    constexpr uint64_t kPal23 = 0x0C0300FC0802FFFAull;   // 2 x [-3, -0.5, 1, 4], 2 x [-2, 0, 1.5, 6]
-    const uint64_t pair = (p & 2u) ? kPal23 : kPal01;
-    const int twice = (int)(int8_t)(uint8_t)(pair >> (8u * (4u * (p & 1u) + e)));
+    const uint32_t d01 = (p & 1u) ? 0x0601FEF8u : 0x0400FDF4u;   // 2 x [-4, -1, 0.5, 3] : 2 x [-6, -1.5, 0, 2]
+    const uint32_t d23 = (p & 1u) ? 0x0C0300FCu : 0x0802FFFAu;   // 2 x [-2, 0, 1.5, 6] : 2 x [-3, -0.5, 1, 4]
+    const uint32_t d = (p & 2u) ? d23 : d01;
+    const int twice = (int)(d << (24u - 8u * e)) >> 24;          // byte e, sign-extended
     return (float)twice * 0.5f;
+}
+
+// A value the compiler must keep as computed: it may not recompute it later from its
+// inputs (which, for the cheap palette code, it would otherwise do inside the step loops,
+// at the cost of the registers of the inputs and constants).
+template <typename V>
+__device__ __forceinline__ V keep(V v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // The same values in the form the search kernels compute once per workgroup: the

@@ -146,6 +146,7 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 Cv[a][r][x] = code_value_prologue<CODE>((uint32_t)(a * M + 4 * (tid + r * NT) + x), ca);
+                if constexpr (CODE == kCodeXor) Cv[a][r][x] = keep(Cv[a][r][x]);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
