@@ -194,12 +194,16 @@ qtcq_status qtcq_bcjr_soft(const float* seq, const float* err_w, int64_t B, int 
  *     grad_seq[b][u] = (2 w_u / temperature) Cov_p( sum_t g[b][t] C(st[t]), C(st[u]) ),
  * computed by one more forward-backward pass with expectation messages (fp32
  * expectation messages centred on the soft codeword).  The result is within
- * 1e-5 * RMS_u(grad_seq[b]) of the exact value at temperatures down to 0.01 (tested on
- * N(0,1) targets, with and without log-normal weights, and on targets 4 + 3 N(0,1) far
- * outside the codebook's range).  Below 0.01 the message stashes are kept in fp64 and
- * the bound holds down to 3e-3 on N(0,1) targets (and to 1e-3 at L = 12); lower, the
- * gradient vanishes away from near-ties while the fp32 parts of the arithmetic keep a
- * fixed relative precision, and the relative error grows (1.7e-5 at L = 16, 1e-3). */
+ * 1e-5 * RMS_u(grad_seq[b]) + 2^-100 of the exact value (the absolute term covers
+ * gradients carried by posterior weights near binary32's underflow range) at
+ * temperatures from QTCQ_VJP_MIN_TEMPERATURE up (tested on N(0,1) targets, with and
+ * without log-normal weights, all three codes, and on targets 4 + 3 N(0,1) far outside
+ * the codebook's range; below 0.01 the message stashes are kept in fp64).  Below that
+ * floor the call is refused (QTCQ_ERR_UNSUPPORTED): there the gradient collapses onto a
+ * few near-ties while the fp32 expectation messages and exp2 weights keep a fixed
+ * relative precision, and the bound no longer holds (1.7e-5 * RMS measured at L = 16,
+ * temperature 1e-3).  The soft codeword itself (qtcq_bcjr_soft) has no such floor. */
+#define QTCQ_VJP_MIN_TEMPERATURE 3e-3f
 
 /* Workspace bytes qtcq_bcjr_vjp needs for `B` sequences in one pass (both message
  * directions of every step -- in 32 bits, fixed point near each step's maximum and
@@ -217,8 +221,9 @@ size_t qtcq_bcjr_vjp_workspace_bytes(int64_t B, int T, int L, int k);
  *             qtcq_bcjr_soft's
  *   log_z     [B] float32 (out) or NULL
  *   workspace: 16-byte aligned, >= qtcq_bcjr_vjp_workspace_bytes(1, T, L, k)
- * Errors: QTCQ_ERR_INVALID_ARG (also grad_soft or grad_seq NULL), QTCQ_ERR_UNSUPPORTED,
- * QTCQ_ERR_WORKSPACE, QTCQ_ERR_DEVICE. */
+ * Errors: QTCQ_ERR_INVALID_ARG (also grad_soft or grad_seq NULL), QTCQ_ERR_UNSUPPORTED
+ * (also a finite temperature below QTCQ_VJP_MIN_TEMPERATURE), QTCQ_ERR_WORKSPACE,
+ * QTCQ_ERR_DEVICE. */
 qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T, int L, int k,
                           qtcq_code code, float temperature, const float* grad_soft, float* grad_seq,
                           float* soft, float* log_z, void* workspace, size_t workspace_bytes,

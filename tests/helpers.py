@@ -86,4 +86,6 @@ def bcjr_err(soft_gpu, soft_ref):
     """Per sequence: max_t |soft_gpu - soft_ref| / RMS_t(soft_ref)."""
     soft_gpu = np.asarray(soft_gpu, dtype=np.float64)
     rms = np.sqrt((soft_ref ** 2).mean(axis=-1))
-    return np.abs(soft_gpu - soft_ref).max(axis=-1) / rms
+    dmax = np.abs(soft_gpu - soft_ref).max(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(rms > 0, dmax / rms, np.where(dmax > 0, np.inf, 0.0))

@@ -131,6 +131,10 @@ def test_bcjr_vjp_validation(nat):
 
     assert call(tau=0.0) == nat.QTCQ_ERR_INVALID_ARG
     assert call(tau=float("nan")) == nat.QTCQ_ERR_INVALID_ARG
+    # below the validated temperature floor (3e-3) the gradient is refused
+    assert call(tau=2.9e-3) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(tau=1e-6) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(tau=3e-3, wsb=ws - 1) == nat.QTCQ_ERR_WORKSPACE     # the floor passes validation
     assert call(T=0) == nat.QTCQ_ERR_INVALID_ARG
     assert call(L=9) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(code=3) == nat.QTCQ_ERR_UNSUPPORTED

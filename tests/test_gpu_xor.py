@@ -116,7 +116,7 @@ def test_bcjr_soft_weighted_L16(api):
 
 
 @pytest.mark.parametrize("L", [8, 12])
-@pytest.mark.parametrize("tau", [0.1, 0.01])
+@pytest.mark.parametrize("tau", [0.1, 0.01, 3e-3])
 def test_bcjr_vjp(api, L, tau):
     s = inputs.xor_targets(3, 48, 4600 + L)
     w = inputs.weights(3, 48, 4601)

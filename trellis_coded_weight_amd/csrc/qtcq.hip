@@ -164,6 +164,7 @@ qtcq_status qtcq_bcjr_vjp(const float* seq, const float* err_w, int64_t B, int T
     if (B < 0 || T < 1 || T > kMaxT) return QTCQ_ERR_INVALID_ARG;
     if (!(temperature > 0.0f) || !__builtin_isfinite(temperature)) return QTCQ_ERR_INVALID_ARG;
     if (!supported_trellis(L, k)) return QTCQ_ERR_UNSUPPORTED;
+    if (temperature < QTCQ_VJP_MIN_TEMPERATURE) return QTCQ_ERR_UNSUPPORTED;
     CodeSel cs;
     if (const qtcq_status pc = parse_code(code, L, &cs); pc != QTCQ_OK) return pc;
     if (B == 0) return QTCQ_OK;
