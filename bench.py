@@ -15,6 +15,7 @@ Extra objects on the line:
   bcjr          -- one BCJR soft-relaxation pass over 65,536 sequences (tau = 0.1)
   bcjr_vjp      -- the gradient of that soft codeword with respect to the targets
   decode        -- the decode kernels' own time and algorithmic HBM bytes
+  xor           -- the XOR palette code: encode/decode of a 4096x4096 matrix, matvec
   decode_matvec -- y = W x straight from the streams (per call, batch 1 and 8 with fp32
                    VALU products; batch 1, 8 and 32 with matrix-core products)
   configs       -- the other encode configurations (16 sequences; 4096x14336 3INST;
@@ -58,6 +59,133 @@ def acs_ops_per_sequence(T: int, weighted: bool = False) -> int:
     return (T - 1) * per_step + final
 
 
+# v_exp_f32 / v_log_f32 issue at one wave64 instruction per two CU cycles (measured):
+# a quarter of the fast rate above
+PEAK_TRANSC_TOPS = PEAK_VALU_TOPS / 4.0
+
+
+def bcjr_soft_ops(T: int, L: int = 16, weighted: bool = False):
+    """Algorithmic work of one soft pass over one sequence, as the BCJR-QAT abstract's
+    forward-backward defines it on 2^L states (N) and 2^(L-2) predecessor groups (G):
+      forward, every step: the energies w (C_j - s_t)^2 / tau (3 ops per state, 4
+        weighted) and la_t(j) = A_t(j >> 2) - energy (1); from step 1 on, each group's
+        A_t = log-sum-exp of its 4 predecessors (16 ops: 3 max, 4 sub, 4 exp, 3 add,
+        1 log, 1 add);
+      backward, steps T-2..0: lb - energy per state (1) and one 4-way log-sum-exp per
+        group (16);
+      posterior, every step: gamma = exp(la + lb - log Z) (3 ops, 1 exp) and the sums
+        sum gamma, sum gamma C (2).
+    Returns (ops, transcendental ops)."""
+    N, G = 1 << L, 1 << (L - 2)
+    e = 4 if weighted else 3
+    fwd = T * (e + 1) * N + (T - 1) * 16 * G
+    bwd = (T - 1) * (N + 16 * G)
+    post = T * 5 * N
+    transc = (T - 1) * 10 * G + T * N
+    return fwd + bwd + post, transc
+
+
+def bcjr_grad_ops(T: int, L: int = 16):
+    """Algorithmic work of the gradient beyond its soft pass, per sequence: the
+    expectation messages Psi (steps T-2..0) and Phi (steps 1..T-1), each group taking
+    4 transition weights (4 sub, 4 exp) and 4 multiply-adds of (g C + message) twice
+    (16 ops per group); and at every step the covariance from the posterior (3 ops,
+    1 exp), the message sum Phi + g C + Psi (2) and four weighted sums (5) per state.
+    Returns (ops, transcendental ops)."""
+    N, G = 1 << L, 1 << (L - 2)
+    ops = (T - 1) * 2 * 16 * G + T * 10 * N
+    transc = (T - 1) * 2 * 4 * G + T * N
+    return ops, transc
+
+
+def mix_ceiling(ops: float, transc: float) -> float:
+    """Top/s at which a mix of ops, transc of them exp2/log2, issues when every other op
+    runs at the fast VALU rate and the transcendentals at a quarter of it."""
+    return ops / (transc / PEAK_TRANSC_TOPS + (ops - transc) / PEAK_VALU_TOPS)
+
+
+def bcjr_stash_bytes(T: int, L: int = 16, grad: bool = False) -> int:
+    """HBM bytes of the message stashes per sequence, 32 bits per group and step: the soft
+    pass writes the forward messages once and reads them once; the gradient writes the
+    forward stash (read by the soft pass's backward and both halves of the gradient
+    sweep: 3 reads), the backward stash and the Phi stash (each written and read once)."""
+    G = 1 << (L - 2)
+    x = (T - 1) * G * 4
+    if not grad:
+        return 2 * x
+    return 4 * x + 2 * (T * G * 4) + 2 * (T * G * 4)
+
+
+def roofline_alu(ops: float, transc: float, seconds: float, nbytes: float) -> dict:
+    ach = ops / seconds / 1e12
+    ceil = mix_ceiling(ops, transc)
+    return {"bound": "alu", "achieved": ach, "peak": PEAK_VALU_TOPS, "unit": "Top/s",
+            "frac": ach / PEAK_VALU_TOPS, "mix_ceiling": ceil, "frac_of_mix": ach / ceil,
+            "transcendental_share": transc / ops,
+            "stash_gbs": nbytes / seconds / 1e9, "stash_frac_hbm": nbytes / seconds / 1e9 / PEAK_HBM_GBS}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, s_host) -> dict:
+    """The CPU oracle as it stands (single-threaded C, one sequence per call) fanned over
+    this host's threads (ctypes releases the GIL), on bounded samples of each
+    configuration: the first sequences of the 4096x4096 1MAD encode (the headline's
+    workload; its rate is `value`), of the 3INST 4096x14336 and weighted 4096x4096
+    encodes, all 16 sequences of the small encode, and the binary64 BCJR of the first
+    sequences of the BCJR workload at each temperature."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from trellis_coded_weight_amd import inputs
+
+    ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(16, ncpu))
+
+    def fan(fn, n):
+        parts = np.array_split(np.arange(n), min(threads, n))
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fn, parts))
+        return time.perf_counter() - t0
+
+    samples = {}
+    for name, n in (("enc4096x4096_1mad", args.cpu_seqs), ("enc4096x14336_3inst", args.cpu_seqs // 4),
+                    ("enc4096x4096_1mad_weighted", args.cpu_seqs // 4), ("enc16_1mad", 16)):
+        sh, wh, cd = inputs.workload(name, B=n)
+        C = oracle.code_table(cd, L)
+        sec = fan(lambda ix: oracle.viterbi(C, sh[ix], None if wh is None else wh[ix], L=L, k=K), n)
+        samples[name] = {"sequences": n, "seconds": sec, "weights_per_s": n * T / sec}
+    nb = args.cpu_bcjr_seqs
+    if nb > 0:
+        sh, _, _ = inputs.workload("bcjr4096x4096_1mad", B=nb)
+        C = oracle.code_table("1mad", L)
+        for tau in (1.0, 0.1, 0.01):
+            # one sequence per call: the binary64 oracle keeps every step's messages
+            sec = fan(lambda ix: [oracle.bcjr(C, sh[i:i + 1], tau, L=L, k=K) for i in ix], nb)
+            samples["bcjr4096x4096_1mad tau=%g" % tau] = {"sequences": nb, "seconds": sec,
+                                                         "weights_per_s": nb * T / sec}
+    head = samples["enc4096x4096_1mad"]
+    total = sum(v["seconds"] for v in samples.values())
+    print("[bench] cpu baseline %.1f s on %d threads" % (total, threads), file=sys.stderr, flush=True)
+    return {"value": head["weights_per_s"], "unit": "weights/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "oracle Viterbi encode of the first %d of the 65536 sequences of the "
+                      "4096x4096 1MAD workload, %d host threads, %.1f s; other configurations "
+                      "in 'configs'" % (head["sequences"], threads, head["seconds"]),
+            "host_cpu": cpu_model(), "host_cores": os.cpu_count(), "threads": threads,
+            "configs": samples}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,7 +197,11 @@ def main() -> int:
     ap.add_argument("--no-matvec", action="store_true", help="skip the decode -> matvec")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other encode / BCJR configurations")
-    ap.add_argument("--cpu-seqs", type=int, default=4096)
+    ap.add_argument("--no-xor", action="store_true", help="skip the XOR palette code")
+    ap.add_argument("--cpu-seqs", type=int, default=2048,
+                    help="CPU baseline: sequences of the 4096x4096 encode sample")
+    ap.add_argument("--cpu-bcjr-seqs", type=int, default=32,
+                    help="CPU baseline: sequences of the BCJR sample per temperature")
     ap.add_argument("--seqs", type=int, default=0,
                     help="profiling only: encode the first N sequences instead of all 65536")
     ap.add_argument("--bcjr-seqs", type=int, default=0,
@@ -290,6 +422,69 @@ def main() -> int:
         print("[bench] tail-biting %.2f ms" % (tsec * 1000.0), file=sys.stderr, flush=True)
         del tws
 
+    if not args.no_xor and not args.seqs:
+        # the XOR-Trellis palette code (the workload's four 14-bit parity masks): encode
+        # and decode of a 4096x4096 matrix, targets N(0,1) times the palettes' RMS (seed
+        # 8), and y = W x on a 28672x8192 tail-biting matrix of random streams (both
+        # products, batch 1 and 8)
+        xc = nat.qtcq_xor_code(*inputs.xor_masks(L))
+        sx = torch.from_numpy(inputs.xor_targets(65536, T, 8)).to(dev)
+        Bx = sx.shape[0]
+        xws = api.encode_workspace(Bx, T, L, K, max_bytes=64 << 30)
+        xbits = torch.empty((Bx, W), dtype=torch.int32, device=dev)
+        xmse = torch.empty(Bx, dtype=torch.float32, device=dev)
+        xrec = torch.empty((Bx, T), dtype=torch.float32, device=dev)
+        xmse2 = torch.empty(Bx, dtype=torch.float32, device=dev)
+
+        def x_enc():
+            nat.qtcq_viterbi_encode(sx.data_ptr(), None, Bx, T, L, K, xc, xbits.data_ptr(),
+                                    xmse.data_ptr(), None, xws.data_ptr(), xws.numel(), sptr)
+
+        def x_dec():
+            nat.qtcq_decode(xbits.data_ptr(), Bx, T, L, K, xc, xrec.data_ptr(), sx.data_ptr(),
+                            None, xmse2.data_ptr(), sptr)
+
+        def ev_time(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 1000.0 / reps
+
+        xesec = ev_time(x_enc, 2)
+        xdsec = ev_time(x_dec, 20)
+        xo = {"workload": "XOR palette code, 4096x4096 = %d sequences x T=256, N(0,1) x %.4f "
+                          "seed 8, L=16, masks %s" % (Bx, inputs.XOR_TARGET_SCALE,
+                                                      [hex(m) for m in inputs.xor_masks(L)]),
+              "encode_ms": xesec * 1e3, "decode_ms": xdsec * 1e3,
+              "encode_valu_frac": acs_ops_per_sequence(T) * Bx / xesec / 1e12 / PEAK_VALU_TOPS,
+              "mse_mean": float(xmse.mean().item()),
+              "decoded_mse_equal": bool(torch.equal(xmse, xmse2))}
+        del xws, xbits, xrec, sx
+        if not args.no_matvec:
+            g2 = np.random.default_rng(14)
+            Mx, Nx = 28672, 8192
+            xb = torch.from_numpy(g2.integers(0, 1 << 32, size=((Mx // 16) * (Nx // 16), 16),
+                                              dtype=np.uint32).view(np.int32)).to(dev)
+            mws = api.matvec_mfma_workspace(Nx)
+            for nb in (1, 8):
+                xv = torch.from_numpy(g2.standard_normal((nb, Nx), dtype=np.float32)).to(dev)
+                yv = torch.empty((nb, Mx), dtype=torch.float32, device=dev)
+                a_ = (xb.data_ptr(), Mx, Nx, L, K, xc, True, xv.data_ptr(), nb, yv.data_ptr())
+                t1 = ev_time(lambda: nat.qtcq_decode_matvec(*a_, sptr), max(1, args.matvec_reps))
+                t2 = ev_time(lambda: nat.qtcq_decode_matvec_mfma(*a_, mws.data_ptr(), mws.numel(), sptr),
+                             max(1, args.matvec_reps))
+                xo["matvec 28672x8192 tail-biting, batch %d" % nb] = {"us": t1 * 1e6, "weights_per_s": Mx * Nx / t1}
+                xo["matvec 28672x8192 tail-biting, batch %d, mfma" % nb] = {"us": t2 * 1e6, "weights_per_s": Mx * Nx / t2}
+            del xb, mws
+        out["xor"] = xo
+        print("[bench] xor encode %.2f ms, decode %.3f ms" % (xesec * 1e3, xdsec * 1e3),
+              file=sys.stderr, flush=True)
+
     if not args.no_bcjr:
         bname = "bcjr4096x4096_1mad"
         sb_host, _, _ = inputs.workload(bname, B=args.bcjr_seqs or None)
@@ -303,10 +498,15 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         bsec = e0.elapsed_time(e1) / 1000.0
+        nb_ = sb.shape[0]
+        sops, stransc = bcjr_soft_ops(T, L)
         out["bcjr"] = {"workload": "%d sequences x T=256, N(0,1) seed 5, L=16, 1MAD, tau=0.1"
-                                   % sb.shape[0],
-                       "seconds": bsec, "seq_per_s": sb.shape[0] / bsec,
-                       "weights_per_s": sb.shape[0] * T / bsec}
+                                   % nb_,
+                       "seconds": bsec, "seq_per_s": nb_ / bsec,
+                       "weights_per_s": nb_ * T / bsec,
+                       "ops_per_seq": sops,
+                       "roofline": roofline_alu(sops * nb_, stransc * nb_, bsec,
+                                                bcjr_stash_bytes(T, L) * nb_)}
         print("[bench] bcjr %.3f s" % bsec, file=sys.stderr, flush=True)
         del bws, soft, logz
 
@@ -321,10 +521,15 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         vsec = e0.elapsed_time(e1) / 1000.0
+        gops, gtransc = bcjr_grad_ops(T, L)
+        vops, vtransc = sops + gops, stransc + gtransc
         out["bcjr_vjp"] = {"workload": "gradient of the soft codeword w.r.t. the targets, "
                                        "%d sequences x T=256, N(0,1) seed 5, upstream "
-                                       "N(0,1) seed 9, L=16, 1MAD, tau=0.1" % sb.shape[0],
-                           "seconds": vsec, "seq_per_s": sb.shape[0] / vsec,
+                                       "N(0,1) seed 9, L=16, 1MAD, tau=0.1" % nb_,
+                           "seconds": vsec, "seq_per_s": nb_ / vsec,
+                           "ops_per_seq": vops,
+                           "roofline": roofline_alu(vops * nb_, vtransc * nb_, vsec,
+                                                    bcjr_stash_bytes(T, L, True) * nb_),
                            "finite": bool(torch.isfinite(grad).all().item())}
         print("[bench] bcjr vjp %.3f s" % vsec, file=sys.stderr, flush=True)
         del vws, grad, g
@@ -366,10 +571,12 @@ def main() -> int:
         sh, _, _ = inputs.workload("bcjr4096x4096_1mad")
         sd = torch.from_numpy(sh).to(dev)
         bws = api.bcjr_workspace(sd.shape[0], T, L, K)
+        sops, stransc = bcjr_soft_ops(T, L)
         for tau in (1.0, 0.1, 0.01):
             bsec, (bsoft, _) = timed(lambda: api.bcjr_soft(sd, tau, workspace=bws))
             cfg["bcjr4096x4096_1mad tau=%g" % tau] = {
                 "sequences": sd.shape[0], "seconds": bsec, "seq_per_s": sd.shape[0] / bsec,
+                "valu_frac": sops * sd.shape[0] / bsec / 1e12 / PEAK_VALU_TOPS,
                 "finite": bool(torch.isfinite(bsoft).all().item())}
         del sd, bws
         out["configs"] = cfg
@@ -377,24 +584,7 @@ def main() -> int:
                                              for k, v in cfg.items()), file=sys.stderr, flush=True)
 
     if not args.no_cpu:
-        import oracle
-        from concurrent.futures import ThreadPoolExecutor
-        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-        cores = max(1, min(16, ncpu))
-        nseq = max(cores, args.cpu_seqs)
-        C = oracle.code_table("1mad", L)
-        sample = s_host[:nseq]
-        chunks = np.array_split(np.arange(nseq), cores)
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(cores) as ex:
-            list(ex.map(lambda ix: oracle.viterbi(C, sample[ix], L=L, k=K), chunks))
-        csec = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": nseq * T / csec, "unit": "weights/s", "cores": cores,
-                               "kind": "oracle",
-                               "sample": "oracle Viterbi encode of the first %d of the 65536 "
-                                         "sequences, %d host threads, %.1f s" % (nseq, cores, csec)}
-        print("[bench] cpu baseline %.1f s on %d threads" % (csec, cores), file=sys.stderr,
-              flush=True)
+        out["cpu_baseline"] = cpu_baseline(args, s_host)
 
     print(json.dumps(out))
     return 0
