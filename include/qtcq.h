@@ -95,8 +95,9 @@ typedef enum { QTCQ_CODE_1MAD = 0, QTCQ_CODE_3INST = 1, QTCQ_CODE_XOR = 2 } qtcq
  * 14 bits. */
 qtcq_code qtcq_xor_code(uint32_t m0, uint32_t m1, uint32_t m2, uint32_t m3);
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char* qtcq_status_string(qtcq_status s);
+/* Human-readable name of a status code (static string, never NULL); takes any int, and
+ * values outside qtcq_status give "unknown status". */
+const char* qtcq_status_string(int status);
 
 /* Words per sequence of the bitstream: ceil((L + k*(T-1)) / 32).  17 at (16, 2, 256).
  * Returns -1 for arguments outside 1 <= k <= L <= 32, T >= 1. */

@@ -27,15 +27,26 @@ CODE_3INST = 1
 _CODES = {"1mad": CODE_1MAD, "3inst": CODE_3INST, CODE_1MAD: CODE_1MAD, CODE_3INST: CODE_3INST}
 
 
-def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc (no contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+# QTCQ_ORACLE_SANITIZE=1 builds and loads an AddressSanitizer + UndefinedBehaviorSanitizer
+# build instead (liboracle_san.so; the process must preload the ASan runtime).
+_SANITIZE = os.environ.get("QTCQ_ORACLE_SANITIZE") == "1"
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+
+
+def build(force: bool = False, sanitize: bool = _SANITIZE) -> str:
+    """Compile liboracle.so with gcc (no contraction, no fast-math); with sanitize, the
+    ASan/UBSan build liboracle_san.so (UB reports abort the process)."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
                "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+        if sanitize:
+            cmd[1:1] = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                        "-fno-omit-frame-pointer"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -44,8 +55,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(build())
         f32p = ctypes.POINTER(ctypes.c_float)
         f64p = ctypes.POINTER(ctypes.c_double)
         u32p = ctypes.POINTER(ctypes.c_uint32)

@@ -10,9 +10,9 @@ using qtcq::kCodeXor;
 
 extern "C" {
 
-const char* qtcq_status_string(qtcq_status s)
+const char* qtcq_status_string(int status)
 {
-    switch (s) {
+    switch (status) {
     case QTCQ_OK: return "ok";
     case QTCQ_ERR_INVALID_ARG: return "invalid argument";
     case QTCQ_ERR_UNSUPPORTED: return "unsupported trellis or code";
