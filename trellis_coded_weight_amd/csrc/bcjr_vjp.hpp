@@ -49,7 +49,10 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     constexpr int NB = Tr::kButterflies;
     constexpr int kWaves = Ly::kWaves;
     constexpr int WID = NT < 64 ? NT : 64;
-    __shared__ float4 buf[2][NB];
+    // expectation messages, double-buffered: chunk g (4 consecutive groups) keeps its two
+    // halves (groups 0-1 and 2-3) in separate planes, so that the half accesses (8 bytes
+    // per lane) are as lane-contiguous as the whole-chunk ones (16 bytes as two halves)
+    __shared__ float2 bufp[2][2][NB];
     __shared__ float softs[kBcjrMaxT];   // soft_t, formed as the soft pass's finalize forms it
 
     const int tid = threadIdx.x;
@@ -101,8 +104,16 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     };
     auto rd = [&](int a) { return lds_chunk(a * NT + opaque_tid()); };   // groups (a, 4tid + r)
     auto wr = [&](int r) { return lds_chunk(4 * opaque_tid() + r); };   // groups (4tid + r, x)
+    auto put4 = [&](int cur, int chunk, float4 v) {
+        bufp[cur][0][chunk] = make_float2(v.x, v.y);
+        bufp[cur][1][chunk] = make_float2(v.z, v.w);
+    };
+    auto get4 = [&](int cur, int chunk) -> float4 {
+        const float2 lo = bufp[cur][0][chunk], hi = bufp[cur][1][chunk];
+        return make_float4(lo.x, lo.y, hi.x, hi.y);
+    };
     auto half = [&](int cur, int chunk, int h) -> float2& {
-        return reinterpret_cast<float2*>(&buf[cur][chunk])[h];
+        return bufp[cur][h][chunk];
     };
     // the soft pass's (shifted) energy terms: its posterior offsets O_u were formed with them
     auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
@@ -112,7 +123,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 
     // ---------------- forward: Phi ----------------
 #pragma unroll
-    for (int r = 0; r < 4; ++r) buf[0][wr(r)] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 4; ++r) put4(0, wr(r), make_float4(0.f, 0.f, 0.f, 0.f));
     __syncthreads();
     int cur = 0;
     for (int t = 1; t < T; ++t) {
@@ -155,7 +166,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                     }
                     out[x] = num * __builtin_amdgcn_rcpf(den);   // den >= 1: its largest term is 2^0
                 }
-                buf[cur ^ 1][wr(r)] = make_float4(out[0], out[1], out[2], out[3]);
+                put4(cur ^ 1, wr(r), make_float4(out[0], out[1], out[2], out[3]));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -171,7 +182,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     // ---------------- backward: Psi and the covariance sums ----------------
     // Psi_{T-1} = 0 (the buffer not read by the last forward step)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) buf[cur ^ 1][wr(r)] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 4; ++r) put4(cur ^ 1, wr(r), make_float4(0.f, 0.f, 0.f, 0.f));
     cur ^= 1;
     __syncthreads();   // also orders this workgroup's Phi stores before their reads
     // One backward step at u: the covariance sums of step u and, if PRODUCE (u >= 1),
@@ -198,7 +209,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
             ST yq[2][4];      // Yn_u[(4 tid + 2h + i, x)]
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const float4 v = buf[cur][wr(2 * h + i)];
+                const float4 v = get4(cur, wr(2 * h + i));
                 ps[i][0] = v.x; ps[i][1] = v.y; ps[i][2] = v.z; ps[i][3] = v.w;
                 if constexpr (WIDE) {
                     const size_t k = ((size_t)u * 4 + 2 * h + i) * 2;
