@@ -161,3 +161,83 @@ def test_invalid_masks_rejected(api):
     with pytest.raises(ValueError):
         api.encode(s, L=16, code=("xor", (1 << 14, 0, 0, 0)))
     sync()
+
+
+# ---- the LDS-table decode of the matrix-core product ------------------------------------
+# For the XOR code the product reads each window's code from a 2^L-entry table in LDS
+# once a workgroup has enough tiles to pay for writing it: 2^(L-8) tiles at batch <= 16,
+# twice that at wider batches (one workgroup per compute unit at L = 16, looping over
+# bands).  The values and their order are the arithmetic decode's, so the bits match.
+
+def cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("L,M,N,batch", [(16, 32, 4096, 1), (16, 48, 4112, 8), (16, 16, 8192, 20),
+                                         (16, 16, 8208, 32), (14, 64, 1040, 3), (12, 64, 1040, 32),
+                                         (10, 48, 272, 9), (6, 32, 48, 2)])
+def test_matvec_table_path_oracle(api, tb, L, M, N, batch):
+    words = random_words(M, N, L, tb, 4900 + M + N + L + batch)
+    x = inputs.targets(batch, N, 4901 + N + batch)
+    mfma_check(api, words, M, N, L, xcode(L), tb, x, "xor table")
+
+
+def test_matvec_table_path_matches_arithmetic_path(api):
+    """At L = 16 and batch 20 (three fragments) a workgroup needs 512 tiles before the
+    table pays: 256 bands of N = 4096 (one band per workgroup on 256 compute units) run
+    the arithmetic decode, 512 bands (two per workgroup) the table.  The first 256 bands
+    are the same streams in both, and their outputs the same bits."""
+    import torch
+    if cus() != 256:
+        pytest.skip("the split between the two paths assumes 256 compute units")
+    L, N, batch = 16, 4096, 20
+    words = random_words(512 * 16, N, L, True, 4950)
+    x = inputs.targets(batch, N, 4951)
+    say("xor matvec table vs arithmetic")
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    y_tab = api.decode_matvec_mfma(bd, 512 * 16, N, dev(x), L=L, code=xcode(L), tailbiting=True)
+    n_half = 256 * (N // 16)          # tiles of the first 256 bands
+    y_ar = api.decode_matvec_mfma(bd[:n_half], 256 * 16, N, dev(x), L=L, code=xcode(L), tailbiting=True)
+    sync()
+    assert np.array_equal(u32(y_tab)[:, :256 * 16], u32(y_ar))
+    # and the table path against the oracle on the second half of the rows
+    mfma_check(api, words[n_half:], 256 * 16, N, L, xcode(L), True, x[:, :], "xor second half")
+
+
+def test_matvec_table_path_bands_per_workgroup(api):
+    """700 bands over the resident workgroups (several bands each at L = 16): every band's
+    outputs equal the same band computed in a 16-band matrix, bit for bit, and the whole
+    product meets the oracle bound."""
+    import torch
+    L, N, M = 16, 4096, 700 * 16
+    words = random_words(M, N, L, False, 4960)
+    x = inputs.targets(3, N, 4961)
+    y = mfma_check(api, words, M, N, L, xcode(L), False, x, "xor 700 bands")
+    Wd = oracle.stream_words(L, 2, 256)
+    for b0 in (0, 300, 684):
+        part = words[b0 * (N // 16):(b0 + 16) * (N // 16)]
+        bd = torch.from_numpy(part.view(np.int32)).cuda()
+        say("xor matvec bands %d..%d alone" % (b0, b0 + 15))
+        yp = api.decode_matvec_mfma(bd, 256, N, dev(x), L=L, code=xcode(L), tailbiting=False)
+        sync()
+        assert part.shape[1] == Wd
+        assert np.array_equal(u32(y)[:, b0 * 16:(b0 + 16) * 16], u32(yp))
+
+
+def test_matvec_table_path_one_hot_columns_exact(api):
+    import torch
+    M, N, L = 32, 4096, 16
+    words = random_words(M, N, L, True, 4970)
+    C = oracle.code_table(xcode(L), L)
+    _, rec = oracle.tb_decode(words, 256, C, L, 2)
+    Wm = oracle.tiles_to_matrix(rec, M, N)
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    for n in (0, 1234, 4095):
+        x = np.zeros((1, N), dtype=np.float32)
+        x[0, n] = 1.0
+        say("xor table matvec one-hot column %d" % n)
+        ym = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, code=xcode(L), tailbiting=True)
+        sync()
+        assert np.array_equal(ym.cpu().numpy()[0], Wm[:, n].astype(np.float32))

@@ -7,7 +7,9 @@ times over without changing any result.  No GPU needed.
 * every kernel keeps a private segment of 0 bytes, except the weighted soft passes in
   gradient mode at L = 16 (at most 16 bytes, every code) and the XOR-code matrix-core
   product at four B fragments with two bands per workgroup (at most 64 bytes);
-* nothing anywhere exceeds 64 bytes.
+* nothing anywhere exceeds 64 bytes;
+* the matrix-core product's LDS-table kernels (XOR code) keep no static LDS: they read
+  the table at LDS address 0, where the dynamic area then starts.
 """
 import os
 import re
@@ -24,7 +26,8 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
 def kernels(tmp_path):
-    """[(mangled name, private segment bytes, vgpr spill count)] of every gfx950 kernel."""
+    """[(mangled name, private segment bytes, vgpr spill count, static LDS bytes)] of every
+    gfx950 kernel."""
     fat = tmp_path / "fatbin.bin"
     subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "-O", "binary", "--only-section=.hip_fatbin",
                     LIB, str(fat)], check=True)
@@ -48,7 +51,8 @@ def kernels(tmp_path):
                                    check=True, capture_output=True, text=True).stdout
             doc = notes[notes.index("---"):notes.index("\n...") + 4]
             for k in yaml.safe_load(doc)["amdhsa.kernels"]:
-                out.append((k[".name"], k[".private_segment_fixed_size"], k[".vgpr_spill_count"]))
+                out.append((k[".name"], k[".private_segment_fixed_size"], k[".vgpr_spill_count"],
+                            k[".group_segment_fixed_size"]))
         p = data.find(MAGIC, p + 1)
     return out
 
@@ -71,7 +75,7 @@ def test_kernels_keep_their_registers(tmp_path):
                 "decode_matvec_mfma"):
         assert any(fam in n for n in names), fam
     bad = []
-    for name, priv, spill in ks:
+    for name, priv, spill, _ in ks:
         code = code_of(name)
         allowed = 0
         if re.search(r"bcjr_sweepILi16ELi[012]ELb1ELb1E", name):
@@ -81,3 +85,14 @@ def test_kernels_keep_their_registers(tmp_path):
         if priv > allowed:
             bad.append((name, priv, spill))
     assert not bad, "kernels spilling to scratch: %s" % bad
+
+
+@pytest.mark.skipif(not (os.path.exists(LIB) and os.path.exists(os.path.join(LLVM, "llvm-readelf"))),
+                    reason="library or ROCm LLVM tools missing")
+def test_table_kernels_keep_no_static_lds(tmp_path):
+    table = [k for k in kernels(tmp_path) if re.search(r"decode_matvec_mfmaILi\d+ELi\d+ELb[01]ELi\dELi\dELb1E", k[0])]
+    # XOR code only: six trellis sizes x plain / tail-biting x four fragment counts
+    assert len(table) == 48
+    assert all(code_of(k[0]) == 2 for k in table)
+    assert all(k[3] == 0 for k in table), [(k[0], k[3]) for k in table if k[3]]
+    assert all(k[1] == 0 for k in table), [(k[0], k[1]) for k in table if k[1]]

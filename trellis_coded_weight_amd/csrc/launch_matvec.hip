@@ -46,6 +46,65 @@ qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream
     return launch_status();
 }
 
+// ---- the XOR code through the LDS code table -------------------------------------------
+// The table kernel (decode_matvec_mfma<..., TABLE = true>) holds the 2^L codes in dynamic
+// LDS and loops over bands, so its grid is as many workgroups as stay resident.  Per
+// device and instantiation, once: raise the kernel's dynamic-LDS limit to what it needs
+// and read how many of its workgroups one compute unit holds (0: the table path is off
+// on this device, and the arithmetic decode runs instead).
+constexpr int kTableMaxDevices = 64;
+
+struct TableLaunchState {
+    std::once_flag once[kTableMaxDevices];
+    int per_cu[kTableMaxDevices] = {};
+};
+
+template <int L, int NF>
+int table_workgroups_per_cu(const void* kernel, TableLaunchState& state)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTableMaxDevices) return 0;
+    std::call_once(state.once[dev], [&]() {
+        const size_t lds = mv_table_lds_bytes<L, NF, 1>();
+        int occ = 0;
+        hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, MatvecMfmaShape::kThreads, lds);
+        if (e == hipSuccess)
+            state.per_cu[dev] = occ > 0 ? occ : 0;
+        else
+            (void)hipGetLastError();   // a refused query leaves no error behind for the launch
+    });
+    return state.per_cu[dev];
+}
+
+// Launches the table kernel and returns true when it pays: writing the table costs each
+// workgroup about as much as the arithmetic decode of 2^(L-8) tiles saves (measured on
+// MI355X: break-even near 256 tiles per workgroup at L = 16, at batch <= 16; twice as
+// many at wider batches, where the decode is a smaller share of the work).  Otherwise
+// launches nothing and returns false.
+template <int L, int CODE, bool TB, int NF>
+bool launch_table(const uint32_t* bits, int M, int N, const uint4* xs, const float* sc, int batch,
+                  float* y, const CodeArg& ca, hipStream_t st)
+{
+    static TableLaunchState state;
+    const auto kernel = decode_matvec_mfma<L, CODE, TB, NF, 1, true>;
+    const int per_cu = table_workgroups_per_cu<L, NF>(reinterpret_cast<const void*>(kernel), state);
+    int dev = 0, cus = 0;
+    if (per_cu < 1 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return false;
+    const int nb = M / 16;
+    const int grid = (int)((int64_t)per_cu * cus < nb ? (int64_t)per_cu * cus : nb);
+    const int64_t tiles_per_wg = (int64_t)((nb + grid - 1) / grid) * (N / 16);
+    constexpr int need_log2 = L - 8 + (NF >= 3 ? 1 : 0);
+    if (tiles_per_wg < (need_log2 > 0 ? (int64_t)1 << need_log2 : 1)) return false;
+    constexpr size_t lds = mv_table_lds_bytes<L, NF, 1>();
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MatvecMfmaShape::kThreads), lds, st, bits, M, N,
+                       xs, sc, batch, y, ca);
+    return true;
+}
+
 // the same product with the decoded weights and the split x on the matrix cores; x ==
 // nullptr: the workspace already holds the split of this (N, batch)
 template <int L, int CODE, bool TB>
@@ -65,6 +124,16 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
     // M / 16 >= 1024, so the grid keeps >= 512 workgroups (two per CU).  Results do not
     // depend on the choice (same arithmetic, same order).
     const int nb = M / 16;
+    if constexpr (CODE == kCodeXor) {
+        bool done = false;
+        switch (nf) {
+        case 1: done = launch_table<L, CODE, TB, 1>(bits, M, N, xs, sc, batch, y, ca, st); break;
+        case 2: done = launch_table<L, CODE, TB, 2>(bits, M, N, xs, sc, batch, y, ca, st); break;
+        case 3: done = launch_table<L, CODE, TB, 3>(bits, M, N, xs, sc, batch, y, ca, st); break;
+        default: done = launch_table<L, CODE, TB, 4>(bits, M, N, xs, sc, batch, y, ca, st); break;
+        }
+        if (done) return launch_status();
+    }
     const bool two = nf >= 3 && nb >= 1024;
     const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
 #define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \

@@ -185,7 +185,23 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
 // BANDS = 2: a workgroup takes bands 2 blockIdx.x and 2 blockIdx.x + 1 (the second may be
 // absent when M / 16 is odd), and every B fragment it loads serves both, which halves
 // the split x's reads from L2 at wide batches.
-template <int L, int CODE, bool TB, int NF, int BANDS>
+//
+// TABLE: the workgroup first writes the code of every L-bit state (before its rescale, in
+// fp16) into a 2^L-entry LDS table, then takes bands BANDS blockIdx.x, + BANDS gridDim.x,
+// ... in turn, reading every window's code from the table: one LDS read and two and a
+// half VALU operations (shift, mask, half a pack of two halves) per weight.  The values, the products and their order are those
+// of the arithmetic decode, so results are the same bits.  It pays for the XOR palette
+// code, whose arithmetic decode takes several times that; a random 16-bit LDS read costs
+// the compute unit about as much as the 1MAD or 3INST arithmetic it would replace.
+// Dynamic LDS (TABLE): mv_table_lds_bytes<L, NF, BANDS>(), of which the table is the
+// first 2^(L+1) bytes.
+template <int L, int NF, int BANDS>
+constexpr size_t mv_table_lds_bytes()
+{
+    return ((size_t)2 << L) + sizeof(float) * MatvecMfmaShape::kWaves * BANDS * 8 * NF * 16;
+}
+
+template <int L, int CODE, bool TB, int NF, int BANDS, bool TABLE = false>
 __global__ void __launch_bounds__(MatvecMfmaShape::kThreads)
 decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
                    const uint4* __restrict__ xs, const float* __restrict__ sc, int batch,
@@ -200,14 +216,33 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     // one MFMA result per band and fragment held back a k-block (hides its latency)
     // when there are few of them; with more, the later MFMAs cover the earlier ones
     constexpr bool DEFER = NF * BANDS <= 2;
-    __shared__ float red[NW][BANDS * 8 * NF][16];
+    // per-wave partial sums; with a table they follow it in dynamic LDS, so the table
+    // starts at LDS address 0 and a window's table address is just twice the window
+    typedef float Red[NW][BANDS * 8 * NF][16];
+    __shared__ float red_static[TABLE ? 1 : NW * BANDS * 8 * NF * 16];
+    extern __shared__ __align__(16) uint32_t mv_table[];   // TABLE: 2^(L-1) fp16 pairs
+    Red& red = *reinterpret_cast<Red*>(TABLE ? reinterpret_cast<float*>(mv_table + (1 << (L - 1)))
+                                             : red_static);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int NTJ = N >> 4, nkb = (NTJ + 1) >> 1;
     const int nbands = M >> 4;
-    const int I0 = BANDS * blockIdx.x;
+    // loop-invariant operands held in VGPRs (an SGPR operand halves a VALU op's issue rate)
+    const uint32_t kbias = vgpr_u32(0xE5FEE5FEu);   // fp16 -1534 in both halves
+    if constexpr (TABLE) {
+        // entry x holds the raw code of state x (pair e: states 2e, 2e + 1)
+        for (int e = tid; e < (1 << (L - 1)); e += MatvecMfmaShape::kThreads)
+            mv_table[e] = code_raw_pair_f16<CODE>(2u * e, 2u * e + 1u, kbias, ca);
+        __syncthreads();
+    }
+    // the table read through a literal LDS address (the dynamic area starts at 0: the
+    // kernel has no static LDS with TABLE), so the window times two is the whole address
+    // and no base is added per read
+    typedef const __attribute__((address_space(3))) _Float16 LdsHalf;
+    LdsHalf* tab16 = reinterpret_cast<LdsHalf*>(static_cast<uintptr_t>(0));
+    for (int I0 = BANDS * blockIdx.x; I0 < nbands; I0 += BANDS * gridDim.x) {
     // f = bits [16 (g & 1), + 32) of words (r, r + 1): alignbit(w_hi, w_lo, sh); for even
     // g the lane's "lo" word is word r itself and the shift is 0
     const uint32_t sh = (g & 1) ? 16u : 0u;
@@ -300,7 +335,12 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
             for (int p = 0; p < 4; ++p) {
                 const uint32_t w0 = (fw >> (32 - L - 4 * p)) & ((1u << L) - 1u);
                 const uint32_t w1 = (fw >> (30 - L - 4 * p)) & ((1u << L) - 1u);
-                a[p] = code_raw_pair_f16<CODE>(w0, w1, kbias, ca);
+                if constexpr (TABLE) {
+                    const mv_half2 h = {tab16[w0], tab16[w1]};
+                    a[p] = __builtin_bit_cast(uint32_t, h);
+                } else {
+                    a[p] = code_raw_pair_f16<CODE>(w0, w1, kbias, ca);
+                }
             }
             av[b] = __builtin_bit_cast(mv_half8, make_uint4(a[0], a[1], a[2], a[3]));
         }
@@ -362,6 +402,8 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
 #pragma unroll
         for (int q = 1; q < NW; ++q) s += red[q][b * 8 * NF + i][rr];
         y[(size_t)i * M + 16 * (I0 + b) + rr] = code_rescale<CODE>(s);
+    }
+    if (I0 + BANDS * (int)gridDim.x < nbands) __syncthreads();   // red is rewritten next
     }
 }
 
