@@ -161,3 +161,22 @@ def test_matvec_encoded_4096x4096(api, tb):
     assert 0.2 < rel < 0.3
     del bits
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("code", ["1mad", "3inst"])
+def test_matvec_bands_per_workgroup(api, code, batch):
+    """1100 bands, one workgroup each: every output against the oracle, and sampled bands
+    equal the same bands computed as a 16-band matrix, bit for bit (a band's outputs
+    depend on its own streams only)."""
+    import torch
+    M, N, L = 1100 * 16, 272, 16
+    words = random_words(M, N, L, True, 1200 + batch)
+    x = inputs.targets(batch, N, 1201 + batch)
+    y = check(api, words, M, N, L, code, True, x, "1100 bands")
+    NTJ = N // 16
+    for b0 in (0, 517, 1084):
+        part = torch.from_numpy(words[b0 * NTJ:(b0 + 16) * NTJ].view(np.int32)).cuda()
+        yp = api.decode_matvec(part, 256, N, dev(x), L=L, code=code, tailbiting=True)
+        sync()
+        assert np.array_equal(u32(y)[:, 16 * b0:16 * (b0 + 16)], u32(yp)), "bands %d.." % b0

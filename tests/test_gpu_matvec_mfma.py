@@ -295,3 +295,22 @@ def test_matvec_mfma_presplit_equals_one_call(api, batch):
         sync()
         assert torch.equal(y1, y2), "M=%d" % M
     assert torch.equal(split.workspace, before)
+
+
+@pytest.mark.parametrize("batch", [1, 8, 32])
+@pytest.mark.parametrize("code", ["1mad", "3inst"])
+def test_matvec_mfma_bands_per_workgroup(api, code, batch):
+    """1100 bands (two per workgroup at batch 32): every output against the oracle, and
+    sampled bands equal the same bands computed as a 16-band matrix, bit for bit (a
+    band's outputs depend on its own streams only)."""
+    import torch
+    M, N, L = 1100 * 16, 272, 16
+    words = random_words(M, N, L, True, 1100 + batch)
+    x = inputs.targets(batch, N, 1101 + batch)
+    y = check(api, words, M, N, L, code, True, x, "1100 bands")
+    NTJ = N // 16
+    for b0 in (0, 517, 1084):
+        part = torch.from_numpy(words[b0 * NTJ:(b0 + 16) * NTJ].view(np.int32)).cuda()
+        yp = api.decode_matvec_mfma(part, 256, N, dev(x), L=L, code=code, tailbiting=True)
+        sync()
+        assert np.array_equal(u32(y)[:, 16 * b0:16 * (b0 + 16)], u32(yp)), "bands %d.." % b0

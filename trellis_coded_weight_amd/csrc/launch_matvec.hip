@@ -10,6 +10,45 @@ namespace qtcq {
 namespace host {
 namespace {
 
+// ---- the LDS-table kernel's grid --------------------------------------------------------
+// The table kernel loops over bands (16-row tile rows), one workgroup per resident slot.
+// Per device and kernel, once: raise its dynamic-LDS limit and read how many of its
+// workgroups one compute unit holds; 0 when the runtime refuses either query.
+constexpr int kGridMaxDevices = 64;
+
+struct ResidentState {
+    std::once_flag once[kGridMaxDevices];
+    int per_cu[kGridMaxDevices] = {};
+};
+
+inline int resident_per_cu(const void* kernel, int threads, size_t dyn_lds, ResidentState& state)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kGridMaxDevices) return 0;
+    std::call_once(state.once[dev], [&]() {
+        int occ = 0;
+        hipError_t e = hipSuccess;
+        if (dyn_lds > 0)
+            e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_lds);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, dyn_lds);
+        if (e == hipSuccess)
+            state.per_cu[dev] = occ > 0 ? occ : 0;
+        else
+            (void)hipGetLastError();   // a refused query leaves no error behind for the launch
+    });
+    return state.per_cu[dev];
+}
+
+inline int device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 template <int L, int CODE, bool TB>
 qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int batch, float* y,
                         const CodeArg& ca, hipStream_t st)
@@ -46,38 +85,6 @@ qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream
     return launch_status();
 }
 
-// ---- the XOR code through the LDS code table -------------------------------------------
-// The table kernel (decode_matvec_mfma<..., TABLE = true>) holds the 2^L codes in dynamic
-// LDS and loops over bands, so its grid is as many workgroups as stay resident.  Per
-// device and instantiation, once: raise the kernel's dynamic-LDS limit to what it needs
-// and read how many of its workgroups one compute unit holds (0: the table path is off
-// on this device, and the arithmetic decode runs instead).
-constexpr int kTableMaxDevices = 64;
-
-struct TableLaunchState {
-    std::once_flag once[kTableMaxDevices];
-    int per_cu[kTableMaxDevices] = {};
-};
-
-template <int L, int NF>
-int table_workgroups_per_cu(const void* kernel, TableLaunchState& state)
-{
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTableMaxDevices) return 0;
-    std::call_once(state.once[dev], [&]() {
-        const size_t lds = mv_table_lds_bytes<L, NF, 1>();
-        int occ = 0;
-        hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, MatvecMfmaShape::kThreads, lds);
-        if (e == hipSuccess)
-            state.per_cu[dev] = occ > 0 ? occ : 0;
-        else
-            (void)hipGetLastError();   // a refused query leaves no error behind for the launch
-    });
-    return state.per_cu[dev];
-}
-
 // Launches the table kernel and returns true when it pays: writing the table costs each
 // workgroup about as much as the arithmetic decode of 2^(L-8) tiles saves (measured on
 // MI355X: break-even near 256 tiles per workgroup at L = 16, at batch <= 16; twice as
@@ -87,19 +94,17 @@ template <int L, int CODE, bool TB, int NF>
 bool launch_table(const uint32_t* bits, int M, int N, const uint4* xs, const float* sc, int batch,
                   float* y, const CodeArg& ca, hipStream_t st)
 {
-    static TableLaunchState state;
+    static ResidentState state;
     const auto kernel = decode_matvec_mfma<L, CODE, TB, NF, 1, true>;
-    const int per_cu = table_workgroups_per_cu<L, NF>(reinterpret_cast<const void*>(kernel), state);
-    int dev = 0, cus = 0;
-    if (per_cu < 1 || hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        return false;
+    constexpr size_t lds = mv_table_lds_bytes<L, NF, 1>();
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel), MatvecMfmaShape::kThreads, lds, state);
+    const int cus = device_cus();
+    if (per_cu < 1 || cus < 1) return false;
     const int nb = M / 16;
     const int grid = (int)((int64_t)per_cu * cus < nb ? (int64_t)per_cu * cus : nb);
     const int64_t tiles_per_wg = (int64_t)((nb + grid - 1) / grid) * (N / 16);
     constexpr int need_log2 = L - 8 + (NF >= 3 ? 1 : 0);
-    if (tiles_per_wg < (need_log2 > 0 ? (int64_t)1 << need_log2 : 1)) return false;
-    constexpr size_t lds = mv_table_lds_bytes<L, NF, 1>();
+    if (tiles_per_wg < ((int64_t)1 << (need_log2 > 0 ? need_log2 : 0))) return false;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MatvecMfmaShape::kThreads), lds, st, bits, M, N,
                        xs, sc, batch, y, ca);
     return true;
@@ -135,16 +140,18 @@ qtcq_status matvec_mfma_impl(const uint32_t* bits, int M, int N, const float* x,
         if (done) return launch_status();
     }
     const bool two = nf >= 3 && nb >= 1024;
-    const dim3 grid1((unsigned)nb), grid2((unsigned)((nb + 1) / 2)), block(MatvecMfmaShape::kThreads);
-#define QTCQ_MV(NF_, B_, G_) hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF_, B_>), G_, block, 0, st, \
-                                               bits, M, N, xs, sc, batch, y, ca)
+    auto go = [&](auto nf_c, auto bands_c) {
+        constexpr int NF = decltype(nf_c)::value, BANDS = decltype(bands_c)::value;
+        const dim3 grid((unsigned)((nb + BANDS - 1) / BANDS));
+        hipLaunchKernelGGL((decode_matvec_mfma<L, CODE, TB, NF, BANDS>), grid, dim3(MatvecMfmaShape::kThreads), 0, st,
+                           bits, M, N, xs, sc, batch, y, ca);
+    };
     switch (nf) {
-    case 1: QTCQ_MV(1, 1, grid1); break;
-    case 2: if (two) QTCQ_MV(2, 2, grid2); else QTCQ_MV(2, 1, grid1); break;
-    case 3: if (two) QTCQ_MV(3, 2, grid2); else QTCQ_MV(3, 1, grid1); break;
-    default: if (two) QTCQ_MV(4, 2, grid2); else QTCQ_MV(4, 1, grid1); break;
+    case 1: go(int_c<1>{}, int_c<1>{}); break;
+    case 2: if (two) go(int_c<2>{}, int_c<2>{}); else go(int_c<2>{}, int_c<1>{}); break;
+    case 3: if (two) go(int_c<3>{}, int_c<2>{}); else go(int_c<3>{}, int_c<1>{}); break;
+    default: if (two) go(int_c<4>{}, int_c<2>{}); else go(int_c<4>{}, int_c<1>{}); break;
     }
-#undef QTCQ_MV
     return launch_status();
 }
 
