@@ -57,6 +57,9 @@ decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
 {
     constexpr int NJS = MatvecShape::kJSlots;
     static_assert(NB >= 1 && NB <= MatvecShape::kMaxBatch, "batch width");
+    // the LCG's three-instruction form where it measured faster: 1MAD at eight rows
+    // (132 against 146 us on 28672x8192); 3INST at eight rows is slower with it
+    constexpr bool kSplitLcg = CODE == kCode1Mad && NB >= 8;
     __shared__ float red[MatvecShape::kWaves][NB][16];
 
     const int tid = threadIdx.x;
@@ -102,7 +105,7 @@ decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
             float wv[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                wv[b] = code_raw<CODE>((f >> (32 - L - 2 * b)) & ((1u << L) - 1u), ca);
+                wv[b] = code_raw<CODE, kSplitLcg>((f >> (32 - L - 2 * b)) & ((1u << L) - 1u), ca);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 acc[a][i] = __builtin_fmaf(wv[0], xv[i].x, acc[a][i]);
