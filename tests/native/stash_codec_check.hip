@@ -3,6 +3,7 @@
 //   - next_up(x) is the next binary32 above x (no float in between), for x of both signs,
 //     zero, subnormals and the largest finite values;
 //   - to_fix codes, read as unsigned: fixed point (0 .. 2^31) exactly for v in [-1024, 0],
+//     equal to their definition 2^31 + rint(v 2^21) (ties to even, exact halves included),
 //     tail codes (above 2^31) below; to_fix(0) = kFixZero;
 //   - round trip: |from_fix(to_fix(v)) - v| <= 2^-22 in the fixed range and
 //     <= 2^-24 (-1024 - v) (binary32 rounding of the distance) below it;
@@ -46,6 +47,9 @@ int main()
     std::vector<double> vs = {0.0, -0.0, -1e-300, -2.3841857910156250e-07, -1.0, -1023.9999999,
                               -1024.0, -1024.0000000001, -1024.5, -1100.0, -2048.0, -1e5,
                               -3.3e9, -1e12, -1e30};
+    // exact halves of the fixed-point unit: the ties of the rounding
+    for (int k = 0; k < 4096; ++k) vs.push_back(-(k + 0.5) * 0x1p-21);
+    for (int k = 0; k < 4096; ++k) vs.push_back(-1024.0 + (k + 0.5) * 0x1p-21);
     for (int i = 0; i < 200000; ++i) {
         const double mag = std::ldexp(1.0, (int)(rng() % 44)) * (double)(rng() >> 11) * 0x1p-53;
         vs.push_back(-mag);
@@ -60,6 +64,9 @@ int main()
         const double r = from_fix(q);
         const double rs = qtcq::from_fix_shifted(q);
         if (v >= -1024.0) {
+            // the code is its definition: 2^31 + rint(v 2^21), ties to even
+            const uint32_t def = 0x80000000u + (uint32_t)(int)std::nearbyint(v * 2097152.0);
+            if (u != def) return fail("fixed code definition", v, u, def);
             if (u > 0x80000000u) return fail("fixed code range", v, u, 0x80000000u);
             if (std::fabs(r - v) > 0x1p-22) return fail("fixed round trip", v, r, 0x1p-22);
             if (rs - qtcq::kStashShift != r) return fail("fixed shifted decode", v, rs, r);
