@@ -23,9 +23,11 @@
  *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
  *    row-major and contiguous; [B][T] means sequence b's element t at b*T + t.
  *  - The caller owns every buffer.  The library allocates no device memory and keeps
- *    no mutable global state, with one exception (qtcq_decode_matvec_mfma_noalloc's
- *    per-device scratch array); calls on different streams may run concurrently as long
- *    as their output and workspace buffers do not overlap.
+ *    no mutable global state, with two exceptions: qtcq_decode_matvec_mfma_noalloc's
+ *    per-device scratch array, and a per-device, once-only set-up of the matrix-core
+ *    product's LDS-table kernel (its dynamic-LDS limit raised, its resident workgroups
+ *    per compute unit read; thread-safe).  Calls on different streams may run
+ *    concurrently as long as their output and workspace buffers do not overlap.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued on it and the call returns without synchronising; outputs are valid
  *    once the stream has reached that point.
@@ -317,7 +319,10 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
  * plus
  *   workspace  device scratch, 16-byte aligned, >= qtcq_decode_matvec_mfma_workspace_bytes(N)
  *              (the split x and its block scales; contents on entry are ignored)
- * Two kernels are enqueued on `stream` (the split, then the product).
+ * Two kernels are enqueued on `stream` (the split, then the product).  For the XOR
+ * code, when each workgroup's share of the matrix is large enough to pay for it
+ * (2^(L-8) tiles of 16x16, twice that above 16 rows of x), the product reads the codes
+ * from a 2^L-entry table in LDS instead of computing them: the same results bit for bit.
  * Errors: as qtcq_decode_matvec (QTCQ_ERR_UNSUPPORTED for batch > 32), also
  * QTCQ_ERR_UNSUPPORTED for N > 2^22, and QTCQ_ERR_WORKSPACE (workspace NULL, misaligned
  * or too small). */

@@ -29,11 +29,11 @@
 // one bit-field extract per weight.
 //
 // Mapping.  One workgroup of 16 waves per band of 16 output rows (tile row I), or per two
-// bands at wide batches on tall matrices; wave w takes k-blocks w, w + 16, ...  Each MFMA
-// starts from zero; its 4 outputs per lane,
-// times the block's 2^-s (exact), are added to the lane's accumulators in k-block order
-// by FMA; then hi + lo (lanes l and l ^ 8), the 16 waves in sequence and the code's
-// rescale.  Results are bit-deterministic and a one-hot x (its block scaled to 2^14,
+// bands at wide batches on tall matrices (with the LDS code table, each resident
+// workgroup loops over bands); wave w takes k-blocks w, w + 16, ...  Each MFMA starts
+// from zero; its 4 outputs per lane, times the block's 2^-s (exact), are added to the
+// lane's accumulators in k-block order by FMA; then hi + lo (lanes l and l ^ 8), the 16
+// waves in sequence and the code's rescale.  Results are bit-deterministic and a one-hot x (its block scaled to 2^14,
 // xl = 0) returns a column of W bit for bit.
 //
 // Rounding: with K = ceil(ceil(N / 32) / 16) k-blocks per wave, u = 2^-24, and allowing
@@ -179,7 +179,8 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
     }
 }
 
-// grid.x = ceil((M / 16) / BANDS), block = MatvecMfmaShape::kThreads.  bits
+// grid.x = ceil((M / 16) / BANDS) (any grid.x >= 1 is correct: workgroup g takes band
+// groups g, g + grid.x, ...), block = MatvecMfmaShape::kThreads.  bits
 // [(M/16)(N/16)][Wd] with Wd = MatvecMfmaShape::stream_words<L, TB>(); xs, sc as written
 // by matvec_split_x for this x; y [batch][M].  NF = frags(batch) B fragments per k-block.
 // BANDS = 2: a workgroup takes bands 2 blockIdx.x and 2 blockIdx.x + 1 (the second may be
@@ -189,8 +190,9 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
 // TABLE: the workgroup first writes the code of every L-bit state (before its rescale, in
 // fp16) into a 2^L-entry LDS table, then takes bands BANDS blockIdx.x, + BANDS gridDim.x,
 // ... in turn, reading every window's code from the table: one LDS read and two and a
-// half VALU operations (shift, mask, half a pack of two halves) per weight.  The values, the products and their order are those
-// of the arithmetic decode, so results are the same bits.  It pays for the XOR palette
+// half VALU operations (shift, mask, half a pack of two halves) per weight.  The values,
+// the products and their order are those of the arithmetic decode, so results are the
+// same bits.  It pays for the XOR palette
 // code, whose arithmetic decode takes several times that; a random 16-bit LDS read costs
 // the compute unit about as much as the 1MAD or 3INST arithmetic it would replace.
 // Dynamic LDS (TABLE): mv_table_lds_bytes<L, NF, BANDS>(), of which the table is the
