@@ -321,7 +321,7 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
  *              (the split x and its block scales; contents on entry are ignored)
  * Two kernels are enqueued on `stream` (the split, then the product).  For the XOR
  * code, when each workgroup's share of the matrix is large enough to pay for it
- * (2^(L-8) tiles of 16x16, twice that above 16 rows of x), the product reads the codes
+ * (2^(L-9) tiles of 16x16), the product reads the codes
  * from a 2^L-entry table in LDS instead of computing them: the same results bit for bit.
  * Errors: as qtcq_decode_matvec (QTCQ_ERR_UNSUPPORTED for batch > 32), also
  * QTCQ_ERR_UNSUPPORTED for N > 2^22, and QTCQ_ERR_WORKSPACE (workspace NULL, misaligned

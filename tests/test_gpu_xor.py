@@ -19,7 +19,8 @@ from test_gpu_bcjr import run_and_compare as bcjr_compare
 from test_gpu_bcjr_vjp import run_and_compare as vjp_compare, upstream
 from test_gpu_encode import check_encode
 from test_gpu_matvec import check as matvec_check, random_words
-from test_gpu_matvec_mfma import check as mfma_check
+from test_gpu_matvec import matrix as mfma_matrix
+from test_gpu_matvec_mfma import bound as mfma_bound, check as mfma_check
 from test_gpu_tailbiting import check_tb
 
 pytestmark = pytest.mark.gpu
@@ -165,9 +166,9 @@ def test_invalid_masks_rejected(api):
 
 # ---- the LDS-table decode of the matrix-core product ------------------------------------
 # For the XOR code the product reads each window's code from a 2^L-entry table in LDS
-# once a workgroup has enough tiles to pay for writing it: 2^(L-8) tiles at batch <= 16,
-# twice that at wider batches (one workgroup per compute unit at L = 16, looping over
-# bands).  The values and their order are the arithmetic decode's, so the bits match.
+# once a workgroup has enough tiles to pay for writing it: 2^(L-9) tiles (one workgroup
+# per compute unit at L = 16, looping over bands).  The values and their order are the
+# arithmetic decode's, so the bits match.
 
 def cus():
     import torch
@@ -184,26 +185,31 @@ def test_matvec_table_path_oracle(api, tb, L, M, N, batch):
     mfma_check(api, words, M, N, L, xcode(L), tb, x, "xor table")
 
 
-def test_matvec_table_path_matches_arithmetic_path(api):
-    """At L = 16 and batch 20 (three fragments) a workgroup needs 512 tiles before the
-    table pays: 256 bands of N = 4096 (one band per workgroup on 256 compute units) run
-    the arithmetic decode, 512 bands (two per workgroup) the table.  The first 256 bands
-    are the same streams in both, and their outputs the same bits."""
+@pytest.mark.parametrize("batch", [1, 20])
+def test_matvec_table_path_matches_arithmetic_path(api, batch):
+    """At L = 16 a workgroup needs 128 tiles before the table pays.  With N = 1024 a band
+    is 64 tiles: 256 bands (one per workgroup on 256 compute units) run the arithmetic
+    decode, 512 bands (two per workgroup) the table.  The first 256 bands are the same
+    streams in both, and their outputs the same bits."""
     import torch
     if cus() != 256:
         pytest.skip("the split between the two paths assumes 256 compute units")
-    L, N, batch = 16, 4096, 20
-    words = random_words(512 * 16, N, L, True, 4950)
-    x = inputs.targets(batch, N, 4951)
-    say("xor matvec table vs arithmetic")
+    L, N = 16, 1024
+    words = random_words(512 * 16, N, L, True, 4950 + batch)
+    x = inputs.targets(batch, N, 4951 + batch)
+    say("xor matvec table vs arithmetic, batch %d" % batch)
     bd = torch.from_numpy(words.view(np.int32)).cuda()
     y_tab = api.decode_matvec_mfma(bd, 512 * 16, N, dev(x), L=L, code=xcode(L), tailbiting=True)
     n_half = 256 * (N // 16)          # tiles of the first 256 bands
     y_ar = api.decode_matvec_mfma(bd[:n_half], 256 * 16, N, dev(x), L=L, code=xcode(L), tailbiting=True)
     sync()
     assert np.array_equal(u32(y_tab)[:, :256 * 16], u32(y_ar))
-    # and the table path against the oracle on the second half of the rows
-    mfma_check(api, words[n_half:], 256 * 16, N, L, xcode(L), True, x[:, :], "xor second half")
+    # and the table run's second half of the rows against the oracle
+    C = oracle.code_table(xcode(L), L)
+    y_o = oracle.decode_matvec(words[n_half:], 256 * 16, N, C, x, L, 2, tailbiting=True)
+    Wm = mfma_matrix(words[n_half:], 256 * 16, N, C, L, True)
+    err = np.abs(y_tab.cpu().numpy()[:, 256 * 16:].astype(np.float64) - y_o)
+    assert np.all(err <= mfma_bound(x, Wm, N))
 
 
 def test_matvec_table_path_bands_per_workgroup(api):

@@ -121,14 +121,21 @@ __device__ __forceinline__ float code_3inst(uint32_t x)
 // [-2, 0, 1.5, 6], used as they are (exact in fp16 and binary32; a per-group scale of
 // the weights lies outside the trellis).  Here each value is stored doubled as a signed
 // byte, palette p in the four bytes of one 32-bit constant, entry e in byte e.
+constexpr uint32_t kXorPaletteTwice[4] = {
+    0x0400FDF4u,   // 2 x [-6, -1.5, 0, 2]
+    0x0601FEF8u,   // 2 x [-4, -1, 0.5, 3]
+    0x0802FFFAu,   // 2 x [-3, -0.5, 1, 4]
+    0x0C0300FCu,   // 2 x [-2, 0, 1.5, 6]
+};
+
 __device__ __forceinline__ float code_xor(uint32_t x, const CodeArg& ca)
 {
     const uint32_t h = x >> 2;
     const uint32_t p = ((__builtin_popcount(h & ca.m[0]) & 1u) << 1) | (__builtin_popcount(h & ca.m[1]) & 1u);
     const uint32_t sh = ((__builtin_popcount(h & ca.m[2]) & 1u) << 1) | (__builtin_popcount(h & ca.m[3]) & 1u);
     const uint32_t e = (x & 3u) ^ sh;
-    const uint32_t d01 = (p & 1u) ? 0x0601FEF8u : 0x0400FDF4u;   // 2 x [-4, -1, 0.5, 3] : 2 x [-6, -1.5, 0, 2]
-    const uint32_t d23 = (p & 1u) ? 0x0C0300FCu : 0x0802FFFAu;   // 2 x [-2, 0, 1.5, 6] : 2 x [-3, -0.5, 1, 4]
+    const uint32_t d01 = (p & 1u) ? kXorPaletteTwice[1] : kXorPaletteTwice[0];
+    const uint32_t d23 = (p & 1u) ? kXorPaletteTwice[3] : kXorPaletteTwice[2];
     const uint32_t d = (p & 2u) ? d23 : d01;
     const int twice = (int)(d << (24u - 8u * e)) >> 24;          // byte e, sign-extended
     return (float)twice * 0.5f;

@@ -86,10 +86,9 @@ qtcq_status split_x_launch(const float* x, int N, int batch, void* ws, hipStream
 }
 
 // Launches the table kernel and returns true when it pays: writing the table costs each
-// workgroup about as much as the arithmetic decode of 2^(L-8) tiles saves (measured on
-// MI355X: break-even near 256 tiles per workgroup at L = 16, at batch <= 16; twice as
-// many at wider batches, where the decode is a smaller share of the work).  Otherwise
-// launches nothing and returns false.
+// workgroup about as much as the arithmetic decode of 2^(L-9) tiles saves (measured on
+// MI355X at L = 12, 14 and 16, batch 1 to 32: 1.05-1.5x at the threshold and above,
+// 0.6-1.0x below it).  Otherwise launches nothing and returns false.
 template <int L, int CODE, bool TB, int NF>
 bool launch_table(const uint32_t* bits, int M, int N, const uint4* xs, const float* sc, int batch,
                   float* y, const CodeArg& ca, hipStream_t st)
@@ -103,7 +102,7 @@ bool launch_table(const uint32_t* bits, int M, int N, const uint4* xs, const flo
     const int nb = M / 16;
     const int grid = (int)((int64_t)per_cu * cus < nb ? (int64_t)per_cu * cus : nb);
     const int64_t tiles_per_wg = (int64_t)((nb + grid - 1) / grid) * (N / 16);
-    constexpr int need_log2 = L - 8 + (NF >= 3 ? 1 : 0);
+    constexpr int need_log2 = L - 9;
     if (tiles_per_wg < ((int64_t)1 << (need_log2 > 0 ? need_log2 : 0))) return false;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MatvecMfmaShape::kThreads), lds, st, bits, M, N,
                        xs, sc, batch, y, ca);
