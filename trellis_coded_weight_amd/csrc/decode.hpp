@@ -128,6 +128,107 @@ decode_tile(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
     }
 }
 
+// The same tile decode four consecutive weights at a time, for T % 4 == 0 and targets,
+// weights and reconstructions 16-byte aligned: quad q of the tile is row q / (T/4),
+// steps t0 .. t0 + 3 with t0 = 4 (q mod T/4).  Their windows start at bits 2 t0 .. 2 t0 + 6
+// (2 t0 a multiple of 8), so one funnel of the two stream words around bit 2 t0 holds all
+// four (L + 6 <= 32): one shift and mask each, instead of a funnel, two LDS reads and
+// the index steps per weight.  Targets, weights and reconstructions move as float4, the
+// step errors go to LDS as float4; the per-sequence sum in t order is decode_tile's.
+// Tail-biting windows that run past the end of the stream (the last L/2 steps of a row)
+// take their last bits from the head, as in decode_tile.  Same grid, block and LDS.
+template <int L, int CODE, bool MSE_, bool WEIGHTED, bool TB = false>
+__global__ void __launch_bounds__(DecodeTile::kThreads)
+decode_tile4(const uint32_t* __restrict__ bits, const float* __restrict__ seq,
+             const float* __restrict__ wts, int64_t B, int T, int W, int SB,
+             float* __restrict__ recon, float* __restrict__ mse, CodeArg ca)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int NT = DecodeTile::kThreads;
+    extern __shared__ __align__(16) char dyn_lds[];
+    float* lerr = reinterpret_cast<float*>(dyn_lds);
+    uint32_t* lbits = reinterpret_cast<uint32_t*>(dyn_lds) + (MSE_ ? SB * DecodeTile::err_stride(T) : 0);
+
+    const int tid = threadIdx.x;
+    const int64_t b0 = (int64_t)blockIdx.x * SB;
+    const int n = (int)((B - b0) < SB ? (B - b0) : SB);
+    const int TQ = T >> 2;                    // quads per row
+    const int nq = n * TQ;                    // <= kMaxWeights / 4: at most U per thread
+    const int64_t base = b0 * T;
+    constexpr int U = DecodeTile::kMaxWeights / 4 / NT;
+
+    f4 sv[U], wv[U];
+    if constexpr (MSE_) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = tid + u * NT;
+            const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f}, one = {1.0f, 1.0f, 1.0f, 1.0f};
+            sv[u] = q < nq ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(seq + base) + q) : zero;
+            wv[u] = (WEIGHTED && q < nq) ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(wts + base) + q) : one;
+        }
+    }
+    const int nw = n * W;
+    const uint32_t* gb = bits + b0 * W;
+    for (int i = tid; i < nw; i += NT) lbits[i] = gb[i];
+    __syncthreads();
+
+    const int ES = DecodeTile::err_stride(T);
+    int r = tid / TQ, tq = tid - r * TQ;      // quad q = r * TQ + tq, advanced by NT
+    const int dr = NT / TQ, dq = NT - dr * TQ;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = tid + u * NT;
+        if (q >= nq) break;
+        const int t0 = 4 * tq;
+        const int p = 2 * t0;                 // first stream bit of the quad's first window
+        const int wi = p >> 5;
+        const uint32_t hi = lbits[r * W + wi];
+        const uint32_t lo = (wi + 1 < W) ? lbits[r * W + wi + 1] : 0u;
+        const uint32_t f = (p & 31) ? __builtin_amdgcn_alignbit(hi, lo, 32 - (p & 31)) : hi;
+        float c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t win = (f >> (32 - L - 2 * j)) & ((1u << L) - 1u);
+            if constexpr (TB) {
+                const int nf = 2 * T - (p + 2 * j);   // stream bits left from the window's start
+                if (nf < L) {                          // the first nf bits, then L - nf from bit 0
+                    const uint32_t head = lbits[r * W];
+                    win = (((f << (2 * j)) >> (32 - nf)) << (L - nf)) | (head >> (32 - (L - nf)));
+                }
+            }
+            c[j] = code_value<CODE>(win, ca);
+        }
+        if (recon) {
+            const f4 cv = {c[0], c[1], c[2], c[3]};
+            __builtin_nontemporal_store(cv, reinterpret_cast<f4*>(recon + base) + q);
+        }
+        if constexpr (MSE_) {
+            const f4 e = {step_err<WEIGHTED>(c[0], sv[u].x, wv[u].x), step_err<WEIGHTED>(c[1], sv[u].y, wv[u].y),
+                          step_err<WEIGHTED>(c[2], sv[u].z, wv[u].z), step_err<WEIGHTED>(c[3], sv[u].w, wv[u].w)};
+            *reinterpret_cast<f4*>(lerr + r * ES + t0) = e;
+        }
+        r += dr;
+        tq += dq;
+        if (tq >= TQ) { tq -= TQ; ++r; }
+    }
+    if constexpr (MSE_) {
+        __syncthreads();
+        if (tid < n) {
+            const float* e = lerr + tid * ES;
+            float acc = 0.0f;
+            int u = 0;
+            for (; u + 4 <= T; u += 4) {
+                const float4 qv = *reinterpret_cast<const float4*>(e + u);
+                acc = acc + qv.x;
+                acc = acc + qv.y;
+                acc = acc + qv.z;
+                acc = acc + qv.w;
+            }
+            mse[b0 + tid] = acc / (float)T;
+        }
+    }
+}
+
 // Code table: out[x] = code(x) for x < n.
 template <int CODE>
 __global__ void __launch_bounds__(256)

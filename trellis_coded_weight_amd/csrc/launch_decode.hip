@@ -16,15 +16,23 @@ qtcq_status decode_impl(const uint32_t* bits, int64_t B, int T, float* recon, co
         return QTCQ_ERR_UNSUPPORTED;      // not reachable for T <= 4096, L <= 16
     const dim3 grid(blocks_for(B, SB)), block(DecodeTile::kThreads);
     const size_t lds = DecodeTile::lds_bytes(T, Wd, mse != nullptr);
+    // four weights per step of a thread when rows are whole float4s (same results)
+    const bool quads = T % 4 == 0 && aligned16(seq) && aligned16(w) && aligned16(recon);
+    auto go = [&](auto mse_c, auto w_c) {
+        constexpr bool MSE_ = decltype(mse_c)::value, WEIGHTED = decltype(w_c)::value;
+        if (quads)
+            hipLaunchKernelGGL((decode_tile4<L, CODE, MSE_, WEIGHTED, TB>), grid, block, lds, st, bits, seq, w,
+                               B, T, Wd, SB, recon, mse, ca);
+        else
+            hipLaunchKernelGGL((decode_tile<L, CODE, MSE_, WEIGHTED, TB>), grid, block, lds, st, bits, seq, w,
+                               B, T, Wd, SB, recon, mse, ca);
+    };
     if (!mse)
-        hipLaunchKernelGGL((decode_tile<L, CODE, false, false, TB>), grid, block, lds, st, bits,
-                           seq, w, B, T, Wd, SB, recon, mse, ca);
+        go(bool_c<false>{}, bool_c<false>{});
     else if (w)
-        hipLaunchKernelGGL((decode_tile<L, CODE, true, true, TB>), grid, block, lds, st, bits, seq,
-                           w, B, T, Wd, SB, recon, mse, ca);
+        go(bool_c<true>{}, bool_c<true>{});
     else
-        hipLaunchKernelGGL((decode_tile<L, CODE, true, false, TB>), grid, block, lds, st, bits,
-                           seq, w, B, T, Wd, SB, recon, mse, ca);
+        go(bool_c<true>{}, bool_c<false>{});
     return launch_status();
 }
 
