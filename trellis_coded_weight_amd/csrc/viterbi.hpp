@@ -225,10 +225,22 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
         return word;
     };
 
-    // A's first inputs: mu_0 (all +0 unless pinned, so no LDS read is needed then)
+    // A's first inputs: mu_0, formed in registers (+0 everywhere, or pinned: +0 in group
+    // o only), the same values muA holds; no LDS read before the loop, so the pinned and
+    // free kernels' step loops get the same register assignment.  (At L = 6, a one-thread
+    // workgroup, the pinned kernel reads them back from muA instead: the register form
+    // kept a stack array there.)
     float inA[4][4], inB[4][4];
-    if constexpr (PINNED) {
+    if constexpr (PINNED && L == 6) {
         load_in(muA, inA);
+    } else if constexpr (PINNED) {
+        const uint32_t oA = pin[qa];
+        const float inf = __builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                inA[r][a] = (uint32_t)(a * NB + tid + r * NT) == oA ? 0.f : inf;
     } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
