@@ -288,7 +288,7 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
  * qtcq_tailbiting_decode when `tailbiting` != 0, at T = 256).
  *   bits  [(M/16)*(N/16)][W] uint32, W = qtcq_bitstream_words(L,k,256) (17 at L=16) or,
  *         tail-biting, qtcq_tailbiting_words(L,k,256) (16)
- *   M, N  multiples of 16 (N = 0 gives y = 0)
+ *   M, N  multiples of 16, N <= 2^22 (N = 0 gives y = 0)
  *   x     [batch][N] float32, 16-byte aligned (may be NULL when N = 0);
  *         y [batch][M] float32 (out)
  *   batch 0..8 activation rows (0: nothing to do)
@@ -297,7 +297,7 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
  * (bit-deterministic; a one-hot x returns a column of W exactly); error
  * <= (4 ceil(N/1024) + 22) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.
  * Errors: QTCQ_ERR_INVALID_ARG (M or N negative or not multiples of 16, NULL or
- * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8),
+ * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8, N > 2^22),
  * QTCQ_ERR_DEVICE. */
 qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k, qtcq_code code,
                                int tailbiting, const float* x, int batch, float* y, void* stream);

@@ -48,6 +48,7 @@ qtcq_status launch_bcjr_vjp(int, const CodeSel&, bool, const float*, const float
                             int, float, float*, float*, float*, void*, size_t, hipStream_t)
 { return stand_in(); }
 int matvec_max_batch() { return MatvecShape::kMaxBatch; }
+int matvec_max_n() { return MatvecShape::kMaxN; }
 // the matrix-core shapes (matvec_mfma.hpp holds a kernel, so its constants are restated
 // here from its declaration: 4 fragments of 8 rows, N up to 2^22, 4224 bytes per
 // 32-column block, 256-byte rounding plus 256)
@@ -161,6 +162,7 @@ int main()
     // matvec products
     CHECK("matvec ok", qtcq_decode_matvec(u, 32, 64, 16, 2, 0, 0, f, 8, f, nullptr), kLaunched);
     CHECK("matvec batch 9", qtcq_decode_matvec(u, 32, 64, 16, 2, 0, 0, f, 9, f, nullptr), QTCQ_ERR_UNSUPPORTED);
+    CHECK("matvec N > 2^22", qtcq_decode_matvec(u, 32, (1 << 22) + 16, 16, 2, 0, 0, f, 1, f, nullptr), QTCQ_ERR_UNSUPPORTED);
     CHECK("matvec M odd", qtcq_decode_matvec(u, 33, 64, 16, 2, 0, 0, f, 1, f, nullptr), QTCQ_ERR_INVALID_ARG);
     CHECK("matvec x misaligned", qtcq_decode_matvec(u, 32, 64, 16, 2, 0, 0, f + 1, 1, f, nullptr), QTCQ_ERR_INVALID_ARG);
     CHECK("mfma ok", qtcq_decode_matvec_mfma(u, 32, 64, 16, 2, 0, 1, f, 32, f, ws, mv_ws, nullptr), kLaunched);

@@ -165,6 +165,9 @@ def test_decode_matvec_validation(nat):
     assert call(batch=9) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(L=7) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(code=4) == nat.QTCQ_ERR_UNSUPPORTED
+    # the kernel reads through buffer descriptors: at most 2^22 columns
+    assert call(N=(1 << 22) + 16) == nat.QTCQ_ERR_UNSUPPORTED
+    assert call(N=(1 << 22) + 16, M=0, bits=None, x=None, y=None) == nat.QTCQ_ERR_UNSUPPORTED
     assert call(x=None) == nat.QTCQ_ERR_INVALID_ARG
     assert call(x=FAKE + 4) == nat.QTCQ_ERR_INVALID_ARG
     assert call(y=None) == nat.QTCQ_ERR_INVALID_ARG

@@ -141,6 +141,11 @@ __device__ __forceinline__ float code_xor(uint32_t x, const CodeArg& ca)
     return (float)twice * 0.5f;
 }
 
+// Fourth word of a raw (unstructured, stride 0) buffer descriptor on gfx9-family chips:
+// DATA_FORMAT = 32 bits, no swizzle, no index, so the range check compares each byte
+// offset against the descriptor's size and an access past it returns zero.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // A value the compiler must keep as computed: it may not recompute it later from its
 // inputs (which, for the cheap palette code, it would otherwise do inside the step loops,
 // at the cost of the registers of the inputs and constants).

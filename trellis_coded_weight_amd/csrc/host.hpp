@@ -156,6 +156,7 @@ qtcq_status launch_bcjr_vjp(int L, const CodeSel& code, bool weighted, const flo
                      float* soft, float* log_z, void* ws, size_t wsb, hipStream_t st);
 // launch_matvec.hip
 int matvec_max_batch();
+int matvec_max_n();
 int matvec_mfma_max_batch();
 int matvec_mfma_max_n();
 size_t matvec_mfma_workspace_bytes(int N);

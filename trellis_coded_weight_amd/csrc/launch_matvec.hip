@@ -190,6 +190,7 @@ void* scratch_for_current_device()
 }  // namespace
 
 int matvec_max_batch() { return MatvecShape::kMaxBatch; }
+int matvec_max_n() { return MatvecShape::kMaxN; }
 int matvec_mfma_max_batch() { return MatvecMfmaShape::kMaxBatch; }
 int matvec_mfma_max_n() { return MatvecMfmaShape::kMaxN; }
 size_t matvec_mfma_workspace_bytes(int N) { return MatvecMfmaShape::workspace_bytes(N); }

@@ -40,11 +40,15 @@
 
 namespace qtcq {
 
+typedef float mv4f __attribute__((ext_vector_type(4)));
+
 struct MatvecShape {
     static constexpr int kThreads = 1024;
     static constexpr int kJSlots = kThreads / 16;   // NJS: tile columns in flight per band
     static constexpr int kWaves = kThreads / 64;
     static constexpr int kMaxBatch = 8;
+    // columns: keeps the buffer descriptors' sizes and offsets within 32-bit integers
+    static constexpr int kMaxN = 1 << 22;
 };
 
 // grid.x = M / 16, block = MatvecShape::kThreads.  bits [(M/16)(N/16)][Wd]; x [batch][N]
@@ -68,8 +72,30 @@ decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
     const int I = blockIdx.x;
     const int NTJ = N >> 4;
     const uint32_t* band = bits + (size_t)I * NTJ * Wd;
-    // funnel shift that brings bit 8 cq of a row to the top (cq = 0: the row's first word)
-    const int sh = (32 - 8 * cq) & 31;
+
+    // The four windows of row 4 rq + a in column quarter cq span row bits
+    // [8 cq, 8 cq + 6 + L).  The funnel f_a holds row bits [8 cq - 4, 8 cq + 28): for
+    // cq >= 1 the pair (word 4 rq + a, word 4 rq + a + 1) shifted by 36 - 8 cq, for cq = 0
+    // the pair (word 4 rq + a - 1, word 4 rq + a) shifted by 4, whose first word only
+    // lends f_a its top 4 bits, which no window reads.  So every lane takes
+    // f_a = alignbit(v[a], v[a + 1], s) with its own five words v and one shift, and window
+    // b of f_a sits 4 + 2 b bits below its top.  v[0] of a cq = 0 lane is therefore any
+    // word: it reads word 4 rq.  Word 16 of a tail-biting stream is word 0 again.
+    const int c1 = cq != 0 ? 1 : 0;
+    // byte offsets of a lane's words within its tile
+    const int o0 = 4 * (js * Wd + 4 * rq);                                  // v[0]
+    const int o1 = o0 + 4 * c1;                                              // v[1..3]
+    const int o4 = (TB && rq == 3 && c1) ? 4 * js * Wd : o1 + 12;           // v[4]
+    const uint32_t s = (uint32_t)(36 - 8 * cq) & 31u;
+    const int ox = 4 * (16 * js + 4 * cq);                                  // x[16 J + 4 cq]
+    // The streams of the band and x are read through buffer descriptors: the lane offsets
+    // above stay in registers, and a thread's k-th tile J = js + k NJS adds the uniform
+    // k NJS Wd words (x: 16 k NJS floats) as the scalar offset, so stepping to the next
+    // tile takes no vector instruction.  Every access is inside the descriptors' ranges.
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(band), (short)0, NTJ * Wd * 4, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x), (short)0, batch * N * 4, kRawBufferWord3);
 
     float acc[4][NB];
 #pragma unroll
@@ -77,44 +103,55 @@ decode_matvec(const uint32_t* __restrict__ bits, int M, int N, int Wd,
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[a][i] = 0.0f;
 
-    auto load_words = [&](int J, uint32_t (&w)[5]) {
-        const uint32_t* sw = band + (size_t)J * Wd + 4 * rq;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = sw[q];
-        w[4] = (TB && rq == 3) ? sw[-12] : sw[4];
+    auto load_words = [&](int k, uint32_t (&v)[5]) {
+        const int so = k * (NJS * Wd * 4);
+        v[0] = __builtin_amdgcn_raw_buffer_load_b32(br, o0, so, 0);
+        v[1] = __builtin_amdgcn_raw_buffer_load_b32(br, o1, so, 0);
+        v[2] = __builtin_amdgcn_raw_buffer_load_b32(br, o1 + 4, so, 0);
+        v[3] = __builtin_amdgcn_raw_buffer_load_b32(br, o1 + 8, so, 0);
+        v[4] = __builtin_amdgcn_raw_buffer_load_b32(br, o4, so, 0);
     };
-    uint32_t wn[5] = {0u, 0u, 0u, 0u, 0u};
-    if (js < NTJ) load_words(js, wn);
-    for (int J = js; J < NTJ; J += NJS) {
-        uint32_t w[5];
-#pragma unroll
-        for (int q = 0; q < 5; ++q) w[q] = wn[q];
-        if (J + NJS < NTJ) load_words(J + NJS, wn);
+    auto tile = [&](int k, const uint32_t (&v)[5]) {
         // rows i >= batch re-read the last row: their sums are never stored, and the
         // products need no per-row guard
-        float4 xv[NB];
+        mv4f xv[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int ii = i < batch ? i : batch - 1;
-            xv[i] = *reinterpret_cast<const float4*>(x + (size_t)ii * N + 16 * (size_t)J + 4 * cq);
+            xv[i] = __builtin_bit_cast(mv4f, __builtin_amdgcn_raw_buffer_load_b128(
+                xr, ox, (ii * N + 16 * NJS * k) * 4, 0));
         }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            // bits [8 cq, 8 cq + 32) of row 4 rq + a
-            const uint32_t f = cq == 0 ? w[a] : __builtin_amdgcn_alignbit(w[a], w[a + 1], sh);
+            const uint32_t f = __builtin_amdgcn_alignbit(v[a], v[a + 1], s);
             float wv[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                wv[b] = code_raw<CODE, kSplitLcg>((f >> (32 - L - 2 * b)) & ((1u << L) - 1u), ca);
+                wv[b] = code_raw<CODE, kSplitLcg>((f >> (28 - L - 2 * b)) & ((1u << L) - 1u), ca);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                acc[a][i] = __builtin_fmaf(wv[0], xv[i].x, acc[a][i]);
-                acc[a][i] = __builtin_fmaf(wv[1], xv[i].y, acc[a][i]);
-                acc[a][i] = __builtin_fmaf(wv[2], xv[i].z, acc[a][i]);
-                acc[a][i] = __builtin_fmaf(wv[3], xv[i].w, acc[a][i]);
+                acc[a][i] = __builtin_fmaf(wv[0], xv[i][0], acc[a][i]);
+                acc[a][i] = __builtin_fmaf(wv[1], xv[i][1], acc[a][i]);
+                acc[a][i] = __builtin_fmaf(wv[2], xv[i][2], acc[a][i]);
+                acc[a][i] = __builtin_fmaf(wv[3], xv[i][3], acc[a][i]);
             }
         }
+    };
+    // two word buffers in turn: the next tile's words load while this one decodes
+    // (the loop runs the workgroup's largest tile count, so k and the scalar offsets are
+    // uniform; each lane works on its own tiles only)
+    uint32_t va[5], vb[5];
+    const int ntiles = js < NTJ ? (NTJ - js + NJS - 1) / NJS : 0;
+    const int kmax = (NTJ + NJS - 1) / NJS;
+    if (ntiles > 0) load_words(0, va);
+    int k = 0;
+    for (; k + 1 < kmax; k += 2) {
+        if (k + 1 < ntiles) load_words(k + 1, vb);
+        if (k < ntiles) tile(k, va);
+        if (k + 2 < ntiles) load_words(k + 2, va);
+        if (k + 1 < ntiles) tile(k + 1, vb);
     }
+    if (k < ntiles) tile(k, va);
 
     // partial sums of row 4 rq + a: lanes differing in cq (bits 1:0) and tile (bits 5:4)
 #pragma unroll

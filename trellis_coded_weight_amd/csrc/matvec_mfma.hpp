@@ -48,11 +48,6 @@
 
 namespace qtcq {
 
-// Fourth word of a raw (unstructured, stride 0) buffer descriptor on gfx9-family chips:
-// DATA_FORMAT = 32 bits, no swizzle, no index, so the range check compares each byte
-// offset against the descriptor's size and an access past it returns zero.
-constexpr int kRawBufferWord3 = 0x00020000;
-
 typedef _Float16 mv_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mv_half2 __attribute__((ext_vector_type(2)));
 typedef float mv_float4 __attribute__((ext_vector_type(4)));

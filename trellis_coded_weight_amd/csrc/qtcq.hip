@@ -182,7 +182,7 @@ qtcq_status qtcq_decode_matvec(const uint32_t* bits, int M, int N, int L, int k,
     if (!supported_trellis(L, k)) return QTCQ_ERR_UNSUPPORTED;
     CodeSel cs;
     if (const qtcq_status pc = parse_code(code, L, &cs); pc != QTCQ_OK) return pc;
-    if (batch > host::matvec_max_batch()) return QTCQ_ERR_UNSUPPORTED;
+    if (batch > host::matvec_max_batch() || N > host::matvec_max_n()) return QTCQ_ERR_UNSUPPORTED;
     if (M == 0 || batch == 0) return QTCQ_OK;
     if (!y || (N > 0 && (!x || !aligned16(x) || !bits))) return QTCQ_ERR_INVALID_ARG;
     return host::launch_decode_matvec(L, cs, tailbiting != 0, bits, M, N, x, batch, y, as_stream(stream));
