@@ -11,17 +11,17 @@
 // (rows 4 rq + a, columns 4 cq + b) of tiles J = js, js + NJS, ... (lane bits: cq = 1:0,
 // rq = 3:2, tile 5:4; js = tid >> 4).  Row 4 rq + a of a tile is stream bits
 // [32 (4 rq + a), ... + 30 + L), inside words 4 rq + a and 4 rq + a + 1 (word 16 of a
-// tail-biting stream is word 0 again), so a thread reads words 4 rq .. 4 rq + 4, one
-// funnel shift per row gives the bits of its four columns and each weight is a bit-field
-// of that, then the code.  The thread needs x[16 J + 4 cq .. + 3] of each batch row (one
-// float4) and accumulates its four rows by FMA in b order.  The products use the code
-// before its rescale (1MAD: S - 510; 3INST: the fp16 sum -- both exact in binary32) and
-// each output is rescaled once at the end (code_rescale: exact for any raw value, so a
-// one-hot x still reproduces a column of W bit for bit).  The stream words of the next
-// tile are loaded while the current one is decoded.  Partial sums of a row are then
-// added in a fixed order (the 4 column groups and the 4 tiles of a wave by xor-shuffles,
-// then the 16 waves in sequence), so results are bit-deterministic, and a one-hot x
-// reproduces a column of W exactly.
+// tail-biting stream is word 0 again), so a thread reads five words of its four rows,
+// one funnel shift per row gives the bits of its four columns and each weight is a
+// bit-field of that, then the code.  The thread needs x[16 J + 4 cq .. + 3] of each batch
+// row (one float4) and accumulates its four rows by FMA in b order.  The products use the
+// code before its rescale (1MAD: S - 510; 3INST: the fp16 sum -- both exact in binary32)
+// and each output is rescaled once at the end (code_rescale: exact for any raw value, so
+// a one-hot x still reproduces a column of W bit for bit).  The stream words of the next
+// tile are loaded while the current one is decoded, into two register sets in turn.
+// Partial sums of a row are then added in a fixed order (the 4 column groups and the 4
+// tiles of a wave by xor-shuffles, then the 16 waves in sequence), so results are
+// bit-deterministic, and a one-hot x reproduces a column of W exactly.
 //
 // Rounding: every output is a sum of N products; along its longest chain there are
 // 4 * ceil((N/16) / NJS) FMAs, 4 shuffle additions and 15 wave additions; the raw code
@@ -30,8 +30,9 @@
 //     |y - W x| <= (4 ceil(N / (16 NJS)) + 22) * 2^-24 * sum_n |W[m][n] x[n]|  (to first order).
 //
 // This path is decode-ALU-bound on this chip, not HBM-bound: at 2 bits per weight the
-// HBM streams ~3.2e13 weights/s, while the window, LCG, byte sum and exact rescale of a
-// computed code cost ~7 CU cycles per 64 weights (~5e12 weights/s at 2.4 GHz).  The
+// HBM streams ~3.2e13 weights/s, while the window, LCG, byte sum, conversion and FMA of a
+// computed code take 6 VALU instructions per weight, mostly of the one-per-cycle kind:
+// ~6 CU cycles per 64 weights, ~6.5e12 weights/s at 2.4 GHz on 256 CUs.  The
 // products are fp32 VALU FMAs: fp32 MFMA runs at the same rate as fp32 VALU FMA here and
 // an fp16 / bf16 MFMA would round the decoded weights.
 #pragma once
