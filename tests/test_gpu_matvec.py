@@ -180,3 +180,34 @@ def test_matvec_bands_per_workgroup(api, code, batch):
         yp = api.decode_matvec(part, 256, N, dev(x), L=L, code=code, tailbiting=True)
         sync()
         assert np.array_equal(u32(y)[:, 16 * b0:16 * (b0 + 16)], u32(yp)), "bands %d.." % b0
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("code,M,N,tb", [("1mad", 28672, 8192, True), ("3inst", 4096, 14336, True),
+                                         ("1mad", 4096, 4096, False)])
+def test_matvec_full_size_sampled_bands(api, code, M, N, tb, batch):
+    """The benchmark's shapes and launch (one workgroup per band of 16 rows, the whole
+    matrix in one call) at batch 1 and 8, random streams: 16 sampled bands (first, last
+    and seeded) against the oracle on those bands' streams, at the bar above."""
+    import torch
+    L = 16
+    n, W = words_for(M, N, L, tb)
+    rng = np.random.default_rng(70 + M + N + batch)
+    words = rng.integers(0, 1 << 32, size=(n, W), dtype=np.uint32)
+    x = inputs.targets(batch, N, 71 + batch)
+    say("matvec full size %dx%d %s tb=%s batch %d" % (M, N, code, tb, batch))
+    y = api.decode_matvec(torch.from_numpy(words.view(np.int32)).cuda(), M, N, dev(x), L=L, k=2,
+                          code=code, tailbiting=tb)
+    sync()
+    yh = y.cpu().numpy()
+    bands = sorted({0, M // 16 - 1} | set(rng.choice(M // 16, size=14, replace=False).tolist()))
+    NTJ = N // 16
+    sub = np.concatenate([words[I * NTJ:(I + 1) * NTJ] for I in bands])
+    Ms = 16 * len(bands)
+    C = oracle.code_table(code, L)
+    y_o = oracle.decode_matvec(sub, Ms, N, C, x, L, 2, tailbiting=tb)
+    Wm = matrix(sub, Ms, N, C, L, tb)
+    bound = (4 * -(-N // 1024) + 23) * U32 * (np.abs(x.astype(np.float64)) @ np.abs(Wm).T)
+    cols = np.concatenate([np.arange(16 * I, 16 * I + 16) for I in bands])
+    err = np.abs(yh[:, cols].astype(np.float64) - y_o)
+    assert np.all(err <= bound), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()

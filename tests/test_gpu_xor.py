@@ -247,3 +247,38 @@ def test_matvec_table_path_one_hot_columns_exact(api):
         ym = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, code=xcode(L), tailbiting=True)
         sync()
         assert np.array_equal(ym.cpu().numpy()[0], Wm[:, n].astype(np.float32))
+
+
+@pytest.mark.parametrize("product,batch", [("valu", 1), ("valu", 8), ("mfma", 1), ("mfma", 8), ("mfma", 32)])
+def test_matvec_full_size_sampled_bands(api, product, batch):
+    """The benchmark's XOR shape, 28672x8192 tail-biting with random streams, through both
+    products in the benchmark's launch (the matrix-core product through its LDS code
+    table): 16 sampled bands of 16 output rows (first, last and seeded) against the
+    oracle on those bands' streams, each at its product's bar."""
+    import torch
+    L, M, N = 16, 28672, 8192
+    words = random_words(M, N, L, True, 5100 + batch)
+    rng = np.random.default_rng(5101 + batch)
+    x = inputs.targets(batch, N, 5102 + batch)
+    say("xor matvec full size, %s batch %d" % (product, batch))
+    bd = torch.from_numpy(words.view(np.int32)).cuda()
+    if product == "valu":
+        y = api.decode_matvec(bd, M, N, dev(x), L=L, k=2, code=xcode(L), tailbiting=True)
+    else:
+        y = api.decode_matvec_mfma(bd, M, N, dev(x), L=L, code=xcode(L), tailbiting=True)
+    sync()
+    yh = y.cpu().numpy()
+    bands = sorted({0, M // 16 - 1} | set(rng.choice(M // 16, size=14, replace=False).tolist()))
+    NTJ = N // 16
+    sub = np.concatenate([words[I * NTJ:(I + 1) * NTJ] for I in bands])
+    Ms = 16 * len(bands)
+    C = oracle.code_table(xcode(L), L)
+    y_o = oracle.decode_matvec(sub, Ms, N, C, x, L, 2, tailbiting=True)
+    Wm = mfma_matrix(sub, Ms, N, C, L, True)
+    if product == "valu":
+        bar = (4 * -(-N // 1024) + 23) * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(Wm).T)
+    else:
+        bar = mfma_bound(x, Wm, N)
+    cols = np.concatenate([np.arange(16 * I, 16 * I + 16) for I in bands])
+    err = np.abs(yh[:, cols].astype(np.float64) - y_o)
+    assert np.all(err <= bar), "worst err/bar %g" % (err / np.maximum(bar, 1e-300)).max()
