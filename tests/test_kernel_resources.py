@@ -8,8 +8,8 @@ times over without changing any result.  No GPU needed.
   gradient mode at L = 16 (at most 16 bytes, every code) and the XOR-code matrix-core
   product at four B fragments with two bands per workgroup (at most 64 bytes);
 * nothing anywhere exceeds 64 bytes;
-* the matrix-core product's LDS-table kernels (XOR code) keep no static LDS: they read
-  the table at LDS address 0, where the dynamic area then starts.
+* the LDS-table kernels of both products (XOR code) keep no static LDS: they read the
+  table at LDS address 0, where the dynamic area then starts.
 """
 import os
 import re
@@ -90,9 +90,16 @@ def test_kernels_keep_their_registers(tmp_path):
 @pytest.mark.skipif(not (os.path.exists(LIB) and os.path.exists(os.path.join(LLVM, "llvm-readelf"))),
                     reason="library or ROCm LLVM tools missing")
 def test_table_kernels_keep_no_static_lds(tmp_path):
-    table = [k for k in kernels(tmp_path) if re.search(r"decode_matvec_mfmaILi\d+ELi\d+ELb[01]ELi\dELi\dELb1E", k[0])]
+    """The LDS-table kernels place the table at LDS address 0 (a window's address is twice
+    the window), so they may hold no static LDS; and they use no scratch."""
+    ks = kernels(tmp_path)
+    table = [k for k in ks if re.search(r"decode_matvec_mfmaILi\d+ELi\d+ELb[01]ELi\dELi\dELb1E", k[0])]
     # XOR code only: six trellis sizes x plain / tail-biting x four fragment counts
     assert len(table) == 48
-    assert all(code_of(k[0]) == 2 for k in table)
-    assert all(k[3] == 0 for k in table), [(k[0], k[3]) for k in table if k[3]]
-    assert all(k[1] == 0 for k in table), [(k[0], k[1]) for k in table if k[1]]
+    valu = [k for k in ks if re.search(r"13decode_matvecILi\d+ELi\d+ELb[01]ELi\dELb1E", k[0])]
+    # the fp32 VALU product's: six trellis sizes x plain / tail-biting x four batch widths
+    assert len(valu) == 48
+    for k in table + valu:
+        assert code_of(k[0]) == 2, k[0]
+        assert k[3] == 0, (k[0], k[3])
+        assert k[1] == 0, (k[0], k[1])

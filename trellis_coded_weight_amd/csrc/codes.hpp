@@ -141,6 +141,48 @@ __device__ __forceinline__ float code_xor(uint32_t x, const CodeArg& ca)
     return (float)twice * 0.5f;
 }
 
+// fp16 bits of twice / 2 for a small integer twice (the palette values: exact in fp16)
+constexpr uint32_t f16_of_half(int twice)
+{
+    if (twice == 0) return 0u;
+    const uint32_t sign = twice < 0 ? 0x8000u : 0u;
+    const uint32_t a = (uint32_t)(twice < 0 ? -twice : twice);
+    int e = 0;
+    while ((a >> (e + 1)) != 0u) ++e;                 // a in [2^e, 2^(e+1))
+    return sign | ((uint32_t)(e - 1 + 15) << 10) | ((a - (1u << e)) << (10 - e));
+}
+// entries 2 w and 2 w + 1 of XOR palette p as an fp16 pair (entry 2 w in the low half)
+constexpr uint32_t xor_pal_pair_f16(int p, int w)
+{
+    const uint32_t d = kXorPaletteTwice[p];
+    const int e0 = (int)(int8_t)(uint8_t)(d >> (16 * w)), e1 = (int)(int8_t)(uint8_t)(d >> (16 * w + 8));
+    return f16_of_half(e0) | (f16_of_half(e1) << 16);
+}
+static_assert(xor_pal_pair_f16(0, 0) == 0xBE00C600u && xor_pal_pair_f16(3, 1) == 0x46003E00u,
+              "fp16 palette pairs");
+
+// The XOR palette code of every L-bit state as fp16 (the palette values themselves) in
+// table[0 .. 2^(L-1)) words, state x in half x, written by threads tid = 0 .. nthreads - 1
+// together.  Per history h, the four states 4 h + b at once: palette 2 p0 + p1 as two
+// fp16 pairs, entry b taking palette entry b XOR (2 s0 + s1) -- s1 swaps the halves of
+// each pair, s0 swaps the pairs -- stored as 8 bytes.  The same values as code_xor.
+template <int L>
+__device__ __forceinline__ void xor_table_f16(uint32_t* table, const CodeArg& ca, int tid, int nthreads)
+{
+    for (int h = tid; h < (1 << (L - 2)); h += nthreads) {
+        const uint32_t hh = (uint32_t)h;
+        const bool p0 = __builtin_popcount(hh & ca.m[0]) & 1, p1 = __builtin_popcount(hh & ca.m[1]) & 1;
+        const bool s0 = __builtin_popcount(hh & ca.m[2]) & 1, s1 = __builtin_popcount(hh & ca.m[3]) & 1;
+        const uint32_t lo = p0 ? (p1 ? xor_pal_pair_f16(3, 0) : xor_pal_pair_f16(2, 0))
+                               : (p1 ? xor_pal_pair_f16(1, 0) : xor_pal_pair_f16(0, 0));
+        const uint32_t hi = p0 ? (p1 ? xor_pal_pair_f16(3, 1) : xor_pal_pair_f16(2, 1))
+                               : (p1 ? xor_pal_pair_f16(1, 1) : xor_pal_pair_f16(0, 1));
+        const uint32_t lo1 = s1 ? __builtin_amdgcn_alignbit(lo, lo, 16) : lo;
+        const uint32_t hi1 = s1 ? __builtin_amdgcn_alignbit(hi, hi, 16) : hi;
+        *reinterpret_cast<uint2*>(&table[2 * h]) = make_uint2(s0 ? hi1 : lo1, s0 ? lo1 : hi1);
+    }
+}
+
 // Fourth word of a raw (unstructured, stride 0) buffer descriptor on gfx9-family chips:
 // DATA_FORMAT = 32 bits, no swizzle, no index, so the range check compares each byte
 // offset against the descriptor's size and an access past it returns zero.

@@ -49,11 +49,46 @@ inline int device_cus()
     return cus;
 }
 
+// The fp32 VALU product of the XOR code through its LDS table (decode_matvec<..., TABLE>),
+// when each workgroup gets at least 2^(L-9) tiles, the same threshold as the matrix-core
+// table kernel's below; otherwise launches nothing and returns false.
+template <int L, bool TB, int NB>
+bool launch_valu_table(const uint32_t* bits, int M, int N, int Wd, const float* x, int batch,
+                       float* y, const CodeArg& ca, hipStream_t st)
+{
+    static ResidentState state;
+    const auto kernel = decode_matvec<L, kCodeXor, TB, NB, true>;
+    constexpr size_t lds = matvec_table_lds_bytes<L, NB>();
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel), MatvecShape::kThreads, lds, state);
+    const int cus = device_cus();
+    if (per_cu < 1 || cus < 1) return false;
+    const int nb = M / 16;
+    const int grid = (int)((int64_t)per_cu * cus < nb ? (int64_t)per_cu * cus : nb);
+    const int64_t tiles_per_wg = (int64_t)((nb + grid - 1) / grid) * (N / 16);
+    constexpr int need_log2 = L - 9;
+    if (tiles_per_wg < ((int64_t)1 << (need_log2 > 0 ? need_log2 : 0))) return false;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MatvecShape::kThreads), lds, st, bits, M, N, Wd,
+                       x, batch, y, ca);
+    return true;
+}
+
 template <int L, int CODE, bool TB>
 qtcq_status matvec_impl(const uint32_t* bits, int M, int N, const float* x, int batch, float* y,
                         const CodeArg& ca, hipStream_t st)
 {
     const int Wd = (int)(TB ? tb_stream_words(2, 256) : stream_words(L, 2, 256));
+    if constexpr (CODE == kCodeXor) {
+        bool done;
+        if (batch <= 1)
+            done = launch_valu_table<L, TB, 1>(bits, M, N, Wd, x, batch, y, ca, st);
+        else if (batch <= 2)
+            done = launch_valu_table<L, TB, 2>(bits, M, N, Wd, x, batch, y, ca, st);
+        else if (batch <= 4)
+            done = launch_valu_table<L, TB, 4>(bits, M, N, Wd, x, batch, y, ca, st);
+        else
+            done = launch_valu_table<L, TB, 8>(bits, M, N, Wd, x, batch, y, ca, st);
+        if (done) return launch_status();
+    }
     const dim3 grid((unsigned)(M / 16)), block(MatvecShape::kThreads);
     if (batch <= 1)
         hipLaunchKernelGGL((decode_matvec<L, CODE, TB, 1>), grid, block, 0, st, bits, M, N, Wd, x, batch, y, ca);

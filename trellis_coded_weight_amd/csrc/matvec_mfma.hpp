@@ -192,26 +192,6 @@ __device__ __forceinline__ uint32_t code_raw_pair_f16(uint32_t w0, uint32_t w1, 
 // the compute unit about as much as the 1MAD or 3INST arithmetic it would replace.
 // Dynamic LDS (TABLE): mv_table_lds_bytes<L, NF, BANDS>(), of which the table is the
 // first 2^(L+1) bytes.
-// fp16 bits of twice / 2 for a small integer twice (the palette values: exact in fp16)
-constexpr uint32_t mv_f16_of_half(int twice)
-{
-    if (twice == 0) return 0u;
-    const uint32_t sign = twice < 0 ? 0x8000u : 0u;
-    const uint32_t a = (uint32_t)(twice < 0 ? -twice : twice);
-    int e = 0;
-    while ((a >> (e + 1)) != 0u) ++e;                 // a in [2^e, 2^(e+1))
-    return sign | ((uint32_t)(e - 1 + 15) << 10) | ((a - (1u << e)) << (10 - e));
-}
-// entries 2 w and 2 w + 1 of XOR palette p as an fp16 pair (entry 2 w in the low half)
-constexpr uint32_t mv_xor_pal_pair(int p, int w)
-{
-    const uint32_t d = kXorPaletteTwice[p];
-    const int e0 = (int)(int8_t)(uint8_t)(d >> (16 * w)), e1 = (int)(int8_t)(uint8_t)(d >> (16 * w + 8));
-    return mv_f16_of_half(e0) | (mv_f16_of_half(e1) << 16);
-}
-static_assert(mv_xor_pal_pair(0, 0) == 0xBE00C600u && mv_xor_pal_pair(3, 1) == 0x46003E00u,
-              "fp16 palette pairs");
-
 template <int L, int NF, int BANDS>
 constexpr size_t mv_table_lds_bytes()
 {
@@ -251,21 +231,7 @@ decode_matvec_mfma(const uint32_t* __restrict__ bits, int M, int N,
     if constexpr (TABLE) {
         // entry x holds the raw code of state x (pair e: states 2e, 2e + 1)
         if constexpr (CODE == kCodeXor) {
-            // per history h, the four states 4 h + b at once: palette 2 p0 + p1 as two fp16
-            // pairs, entry b taking palette entry b XOR (2 s0 + s1) -- s1 swaps the halves
-            // of each pair, s0 swaps the pairs -- stored as 8 bytes
-            for (int h = tid; h < (1 << (L - 2)); h += MatvecMfmaShape::kThreads) {
-                const uint32_t hh = (uint32_t)h;
-                const bool p0 = __builtin_popcount(hh & ca.m[0]) & 1, p1 = __builtin_popcount(hh & ca.m[1]) & 1;
-                const bool s0 = __builtin_popcount(hh & ca.m[2]) & 1, s1 = __builtin_popcount(hh & ca.m[3]) & 1;
-                const uint32_t lo = p0 ? (p1 ? mv_xor_pal_pair(3, 0) : mv_xor_pal_pair(2, 0))
-                                       : (p1 ? mv_xor_pal_pair(1, 0) : mv_xor_pal_pair(0, 0));
-                const uint32_t hi = p0 ? (p1 ? mv_xor_pal_pair(3, 1) : mv_xor_pal_pair(2, 1))
-                                       : (p1 ? mv_xor_pal_pair(1, 1) : mv_xor_pal_pair(0, 1));
-                const uint32_t lo1 = s1 ? __builtin_amdgcn_alignbit(lo, lo, 16) : lo;
-                const uint32_t hi1 = s1 ? __builtin_amdgcn_alignbit(hi, hi, 16) : hi;
-                *reinterpret_cast<uint2*>(&mv_table[2 * h]) = make_uint2(s0 ? hi1 : lo1, s0 ? lo1 : hi1);
-            }
+            xor_table_f16<L>(mv_table, ca, tid, MatvecMfmaShape::kThreads);
         } else {
             for (int e = tid; e < (1 << (L - 1)); e += MatvecMfmaShape::kThreads)
                 mv_table[e] = code_raw_pair_f16<CODE>(2u * e, 2u * e + 1u, kbias, ca);
