@@ -24,9 +24,9 @@
  *    row-major and contiguous; [B][T] means sequence b's element t at b*T + t.
  *  - The caller owns every buffer.  The library allocates no device memory and keeps
  *    no mutable global state, with two exceptions: qtcq_decode_matvec_mfma_noalloc's
- *    per-device scratch array, and a per-device, once-only set-up of the matrix-core
- *    product's LDS-table kernel (its dynamic-LDS limit raised, its resident workgroups
- *    per compute unit read; thread-safe).  Calls on different streams may run
+ *    per-device scratch array, and a per-device, once-only set-up of each matvec
+ *    product's LDS-table kernels (their dynamic-LDS limit raised, their resident
+ *    workgroups per compute unit read; thread-safe).  Calls on different streams may run
  *    concurrently as long as their output and workspace buffers do not overlap.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued on it and the call returns without synchronising; outputs are valid
@@ -295,7 +295,9 @@ qtcq_status qtcq_tailbiting_decode(const uint32_t* bits, int64_t B, int T, int L
  * Arithmetic: fp32 FMA of each code value before its rescale (exact in fp32) with x,
  * partial sums added in a fixed order, then the code's rescale applied once per output
  * (bit-deterministic; a one-hot x returns a column of W exactly); error
- * <= (4 ceil(N/1024) + 22) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.
+ * <= (4 ceil(N/1024) + 22) * 2^-24 * sum_n |W[m][n] x[i][n]| to first order.  For the
+ * XOR code, when each workgroup's share of the matrix is large enough (2^(L-9) tiles),
+ * the codes are read from a 2^L-entry table in LDS: the same results bit for bit.
  * Errors: QTCQ_ERR_INVALID_ARG (M or N negative or not multiples of 16, NULL or
  * misaligned buffers), QTCQ_ERR_UNSUPPORTED ((L, k) or code, batch > 8, N > 2^22),
  * QTCQ_ERR_DEVICE. */
