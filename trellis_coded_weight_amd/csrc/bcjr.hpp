@@ -46,6 +46,7 @@
 #include "codes.hpp"
 #include "viterbi.hpp"
 
+
 namespace qtcq {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -311,13 +312,15 @@ template <int L, int CODE>
 struct PackedCodes {
     uint32_t w[4][4][2];   // [a][r][x >> 1], x even in the low half
 
+    // OPAQUE: the raw code of a state is the same function here as in the forward
+    // prologue; an opaque index keeps the compiler from carrying the prologue's values
+    // across the forward loop (spilled) instead of recomputing them.  Needed for the cheap
+    // palette code, and wherever the forward loop holds more registers.
+    template <bool OPAQUE = (CODE == kCodeXor)>
     __device__ __forceinline__ void init(int tid, const CodeArg& ca)
     {
         constexpr int M = Trellis<L>::kGroups;
-        // the palette code of a state is the same function here as in the forward
-        // prologue: an opaque index keeps the compiler from carrying the prologue's values
-        // across the forward loop instead of recomputing them
-        if constexpr (CODE == kCodeXor) tid = keep(tid);
+        if constexpr (OPAQUE) tid = keep(tid);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -407,20 +410,49 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                 __builtin_amdgcn_sched_barrier(0);
             }
 
-    // byte addresses of the chunks (a, 4tid..4tid+3) and (4tid+r, 0..3), recomputed at
-    // each use from an opaque copy of the thread index, so that the compiler cannot hoist
-    // eight loop-invariant addresses out of the step loops (they would be spilled)
+    // byte addresses of the chunks (a, 4tid..4tid+3) and (4tid+r, 0..3).  With at least
+    // 64 threads (L >= 12) the chunk swizzle leaves a * NT alone, so chunk (a, 4tid + ..)
+    // is at rb + addr(a * NT), a compile-time offset, and chunk (4tid + r, ..) at wb XOR 16 r
+    // (r flips the two low chunk bits, which are bits 4 and 5 of the byte address).  The two
+    // bases are derived once per step from an opaque copy of the thread index (derive()),
+    // so they are never live across steps and the compiler cannot hoist eight
+    // loop-invariant addresses out of the step loops (they would be spilled).  Without
+    // the split (smaller workgroups, or instantiations whose registers are full) each
+    // address is recomputed at its use from an opaque copy of the thread index.
+    // (The split costs registers across a step: the weighted gradient-mode forward and
+    // every weighted or gradient-mode backward would spill with it.)
+    constexpr bool kSplitFwd = NT >= 64 && !(WEIGHTED && VJP);
+    constexpr bool kSplitBwd = NT >= 64 && !WEIGHTED && !VJP;
     auto opaque_tid = [&]() {
         int v = tid;
         asm volatile("v_mov_b32 %0, %0" : "+v"(v));
         return v;
     };
-    auto rd = [&](int a) { return Ld::addr(lds_chunk(a * NT + opaque_tid())); };
-    auto wr = [&](int r) { return Ld::addr(lds_chunk(4 * opaque_tid() + r)); };
+    int rb = 0, wb = 0;
+    auto derive = [&]() {
+        const int t = opaque_tid();
+        rb = Ld::addr(lds_chunk(t));
+        wb = Ld::addr(lds_chunk(4 * t));
+    };
+    auto rd_at = [&](int a, auto split) {
+        if constexpr (decltype(split)::value) return rb + Ld::addr(a * NT);
+        else return Ld::addr(lds_chunk(a * NT + opaque_tid()));
+    };
+    auto wr_at = [&](int r, auto split) {
+        if constexpr (decltype(split)::value) return wb ^ (16 * r);
+        else return Ld::addr(lds_chunk(4 * opaque_tid() + r));
+    };
+    using FwdSplit = std::integral_constant<bool, kSplitFwd>;
+    using BwdSplit = std::integral_constant<bool, kSplitBwd>;
+    auto rd = [&](int a) { return rd_at(a, FwdSplit{}); };
+    auto wr = [&](int r) { return wr_at(r, FwdSplit{}); };
+    auto rdb = [&](int a) { return rd_at(a, BwdSplit{}); };
+    auto wrb = [&](int r) { return wr_at(r, BwdSplit{}); };
 
     auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
 
     // ---------------- forward ----------------
+    derive();
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
     if (tid < kWaves) wmax[0][tid] = 0.f;
@@ -430,6 +462,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     double Sh = 0.0;   // sum of the energy shifts kappa w s^2 of the steps so far
     int par = 0;
     for (int t = 1; t < T; ++t) {
+        derive();
         float g = wmax[par][0];
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) g = __builtin_fmaxf(g, wmax[par][q]);
@@ -494,6 +527,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     if (tid == 0) gsh[T - 1] = gl;
     double log2z;
     {
+        derive();
         const StepEnergy se = step_energy(T - 1);
         Sh = uniform64(Sh + se.shift(s[T - 1]));
         const double gl64 = (double)gl;
@@ -550,10 +584,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // it holds the code values packed (PackedCodes): 32 registers instead of 64, which
     // keeps the step loop free of spills.
     PackedCodes<L, CODE> Ch;
-    Ch.init(tid, ca);
+    Ch.template init<CODE == kCodeXor || kSplitFwd>(tid, ca);
     // Y_{T-1} = 0
+    derive();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
+    for (int r = 0; r < 4; ++r) lds_write4(buf, wrb(r), P, 0.0, 0.0, 0.0, 0.0);
     if (tid < kWaves) wmax[par][tid] = 0.f;
     __syncthreads();
 
@@ -562,6 +597,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // One backward step at t (t >= 1 produces Y_{t-1}); the posterior of step t is
     // accumulated on the way.  At t = 0 only the posterior is formed (X_0 = 0).
     auto bstep = [&](int t, bool produce) {
+        derive();
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
         auto stash_at = [&](int a) -> int4 {
@@ -577,7 +613,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         double yn[4][4];    // [r][x]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            lds_read4(buf, wr(r), P, yn[r]);
+            lds_read4(buf, wrb(r), P, yn[r]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) yn[r][x] -= h64;
             if constexpr (VJP && WIDE) {   // Yn_t[(4 tid + r, x)]
@@ -637,7 +673,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                         ymax = __builtin_fmaxf(ymax, (float)y[rr]);
                     }
                 }
-                if (produce) *reinterpret_cast<double2*>(buf + rd(a) + h * P) = make_double2(y[0], y[1]);
+                if (produce) *reinterpret_cast<double2*>(buf + rdb(a) + h * P) = make_double2(y[0], y[1]);
                 __builtin_amdgcn_sched_barrier(0);   // bound live ranges
             }
         }
