@@ -97,13 +97,35 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     PackedCodes<L, CODE> Cp;   // code values of the states (a, c = 4 tid + r, x)
     Cp.init(tid, ca);
 
+    // chunk indices of the groups (a, 4tid + r) and (4tid + r, x).  With at least 64
+    // threads (L >= 12) the swizzle leaves a * NT alone: rd(a) = c0 + a NT and
+    // wr(r) = c1 XOR r, from two bases derived once per step (derive()) from an opaque copy
+    // of the thread index, so that neither they nor eight loop-invariant indices are
+    // carried across steps.  Smaller workgroups recompute each index at its use, and so
+    // does the palette code's weighted wide-stash sweep, whose registers are full (it
+    // would spill).
+    constexpr bool kSplit = NT >= 64 && !(CODE == kCodeXor && WEIGHTED && WIDE);
     auto opaque_tid = [&]() {
         int v = tid;
         asm volatile("v_mov_b32 %0, %0" : "+v"(v));
         return v;
     };
-    auto rd = [&](int a) { return lds_chunk(a * NT + opaque_tid()); };   // groups (a, 4tid + r)
-    auto wr = [&](int r) { return lds_chunk(4 * opaque_tid() + r); };   // groups (4tid + r, x)
+    int c0 = 0, c1 = 0;
+    auto derive = [&]() {
+        if constexpr (kSplit) {
+            const int t = opaque_tid();
+            c0 = lds_chunk(t);
+            c1 = lds_chunk(4 * t);
+        }
+    };
+    auto rd = [&](int a) {   // groups (a, 4tid + r)
+        if constexpr (kSplit) return c0 + a * NT;
+        else return lds_chunk(a * NT + opaque_tid());
+    };
+    auto wr = [&](int r) {   // groups (4tid + r, x)
+        if constexpr (kSplit) return c1 ^ r;
+        else return lds_chunk(4 * opaque_tid() + r);
+    };
     auto put4 = [&](int cur, int chunk, float4 v) {
         bufp[cur][0][chunk] = make_float2(v.x, v.y);
         bufp[cur][1][chunk] = make_float2(v.z, v.w);
@@ -122,11 +144,13 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     };
 
     // ---------------- forward: Phi ----------------
+    derive();
 #pragma unroll
     for (int r = 0; r < 4; ++r) put4(0, wr(r), make_float4(0.f, 0.f, 0.f, 0.f));
     __syncthreads();
     int cur = 0;
     for (int t = 1; t < T; ++t) {
+        derive();
         const StepEnergy se = step_energy(t - 1);
         const float gp = gu[t - 1];
         const float sft = softs[t - 1];
@@ -174,6 +198,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         __syncthreads();
     }
     // Phi_{T-1}
+    derive();
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -181,6 +206,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
 
     // ---------------- backward: Psi and the covariance sums ----------------
     // Psi_{T-1} = 0 (the buffer not read by the last forward step)
+    derive();
 #pragma unroll
     for (int r = 0; r < 4; ++r) put4(cur ^ 1, wr(r), make_float4(0.f, 0.f, 0.f, 0.f));
     cur ^= 1;
@@ -189,6 +215,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     // Psi_{u-1}.  The step with u = 0 is peeled so that the loop body has no branches.
     auto bstep = [&](int u, auto produce_tag) {
         constexpr bool PRODUCE = decltype(produce_tag)::value;
+        derive();
         const StepEnergy se = step_energy(u);
         const float gp = gu[u];
         const float sft = softs[u];
