@@ -122,10 +122,18 @@ __host__ __device__ __forceinline__ float next_up(float x)
 // costs the backward loops their register allocation.
 constexpr double kFixScale = 2097152.0;
 constexpr double kStashShift = 1024.0;
+// Encoded without a branch.  For v in [-1024, 0] the sum t = v + (1.5 2^31 + 2^10) lies in
+// [1.5 2^31, 1.5 2^31 + 2^10], where a binary64 unit in the last place is 2^-21, and the
+// constant is a multiple of 2^-21: the single rounding of the sum is the constant plus
+// rint(v 2^21) 2^-21 (ties to even, the constant's last place being even).  The low word
+// of t is then 2^31 + rint(v 2^21) (its mantissa is 2^51 + 2^31 + rint(v 2^21)).  Both
+// codes are formed and one is selected.
 __host__ __device__ __forceinline__ int to_fix(double v)
 {
-    if (v >= -1024.0) return (int)(0x80000000u + (uint32_t)(int)__builtin_rint(v * kFixScale));
-    return (int)__builtin_bit_cast(uint32_t, (float)(v + kStashShift));
+    const double t = v + (0x1.8p31 + 0x1p10);
+    const uint32_t fixed = (uint32_t)__builtin_bit_cast(uint64_t, t);
+    const uint32_t tail = __builtin_bit_cast(uint32_t, (float)(v + kStashShift));
+    return (int)(v >= -1024.0 ? fixed : tail);
 }
 __host__ __device__ __forceinline__ double from_fix_shifted(int q)
 {
@@ -633,7 +641,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         Gm = uniform64(Gm - (double)gsh[t]);          // G_{t-1}
         const StepEnergy se = step_energy(t);
         float pg = 0.f, pc = 0.f;
-        float ymax = -__builtin_inff();
+        double ymax = -__builtin_inf();   // fp64 maximum, rounded to binary32 once below
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int4 xs = xs_next;
@@ -670,7 +678,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
                     pc = __builtin_fmaf(pb, qc, pc);
                     if (produce) {
                         y[rr] = m + (double)fast_log2(sq);
-                        ymax = __builtin_fmaxf(ymax, (float)y[rr]);
+                        ymax = max64(ymax, y[rr]);
                     }
                 }
                 if (produce) *reinterpret_cast<double2*>(buf + rdb(a) + h * P) = make_double2(y[0], y[1]);
@@ -684,8 +692,9 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
             part[((size_t)t * kWaves + wave) * 2 + 1] = pc;
         }
         if (produce) {
-            ymax = wave_max<WID>(ymax);
-            if (lane == 0) wmax[par ^ 1][wave] = next_up(ymax);
+            // rounding is monotonic: the same value as the maximum of the rounded messages
+            const float ymax32 = wave_max<WID>((float)ymax);
+            if (lane == 0) wmax[par ^ 1][wave] = next_up(ymax32);
             par ^= 1;
             __syncthreads();
         }
