@@ -149,7 +149,11 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
     for (int r = 0; r < 4; ++r) put4(0, wr(r), make_float4(0.f, 0.f, 0.f, 0.f));
     __syncthreads();
     int cur = 0;
-    for (int t = 1; t < T; ++t) {
+    // One forward step at t (1 <= t < T): Phi_t from Phi_{t-1}.  HAS_X: Xn_{t-1} comes from
+    // the stash (t >= 2); the step with t = 1 (Xn_0 = 0) is peeled so that the loop body
+    // has no branches.
+    auto fstep = [&](int t, auto has_x_tag) {
+        constexpr bool HAS_X = decltype(has_x_tag)::value;
         derive();
         const StepEnergy se = step_energy(t - 1);
         const float gp = gu[t - 1];
@@ -164,7 +168,7 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
                 phs[phi_slot(t - 1, a, h)] = v;
                 ph[a][0] = v.x; ph[a][1] = v.y;
                 Pair q{SV::kZero, SV::kZero};   // Xn_0 = 0
-                if (t >= 2) q = x_pair(t - 1, a, h);
+                if constexpr (HAS_X) q = x_pair(t - 1, a, h);
                 xq[a][0] = q.x; xq[a][1] = q.y;
             }
 #pragma unroll
@@ -196,7 +200,9 @@ bcjr_vjp_sweep(const float* __restrict__ seq, const float* __restrict__ wts,
         }
         cur ^= 1;
         __syncthreads();
-    }
+    };
+    if (T >= 2) fstep(1, std::false_type{});
+    for (int t = 2; t < T; ++t) fstep(t, std::true_type{});
     // Phi_{T-1}
     derive();
 #pragma unroll
