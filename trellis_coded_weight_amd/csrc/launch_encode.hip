@@ -7,6 +7,25 @@ namespace qtcq {
 namespace host {
 namespace {
 
+// The search over n sequences of the chunk: pairs of sequences per workgroup, or one
+// (its minima then double-buffered in the kernel) when the batch is small enough that
+// pairs would leave compute units idle.
+template <int L, int CODE, bool W, bool PINNED>
+void launch_forward(const float* seq, const float* w, int T, int64_t b0, int64_t n, int rot,
+                    const uint32_t* pin, uint32_t* bp, uint32_t* fin, float* fin_cost, float* mse,
+                    const CodeArg& ca, hipStream_t st)
+{
+    using Tr = Trellis<L>;
+    const int per_wg = search_seqs_per_wg(n);
+    const dim3 grid(blocks_for(n, per_wg)), block(Tr::kThreads);
+    if (per_wg == 1)
+        hipLaunchKernelGGL((viterbi_forward<L, CODE, W, PINNED, true>), grid, block, 0, st, seq, w, T,
+                           b0, n, per_wg, rot, pin, bp, fin, fin_cost, mse, ca);
+    else
+        hipLaunchKernelGGL((viterbi_forward<L, CODE, W, PINNED, false>), grid, block, 0, st, seq, w, T,
+                           b0, n, per_wg, rot, pin, bp, fin, fin_cost, mse, ca);
+}
+
 template <int L, int CODE, bool W>
 qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n, int T,
                          uint32_t* bits, float* mse, uint32_t* states, char* ws,
@@ -16,9 +35,7 @@ qtcq_status encode_chunk(const float* seq, const float* w, int64_t b0, int64_t n
     uint32_t* bp = reinterpret_cast<uint32_t*>(ws);
     uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
     float* fin_cost = reinterpret_cast<float*>(fin + n);
-    const int per_wg = search_seqs_per_wg(n);
-    hipLaunchKernelGGL((viterbi_forward<L, CODE, W>), dim3(blocks_for(n, per_wg)), dim3(Tr::kThreads),
-                       0, st, seq, w, T, b0, n, per_wg, 0, nullptr, bp, fin, fin_cost, mse, ca);
+    launch_forward<L, CODE, W, false>(seq, w, T, b0, n, 0, nullptr, bp, fin, fin_cost, mse, ca, st);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     const int Wd = (int)stream_words(L, 2, T);
@@ -59,19 +76,15 @@ qtcq_status tb_chunk(const float* seq, const float* w, int64_t b0, int64_t n, in
     uint32_t* fin = bp + (size_t)n * (T - 1) * Tr::kBpWords;
     float* fin_cost = reinterpret_cast<float*>(fin + n);
     uint32_t* overlap = reinterpret_cast<uint32_t*>(fin_cost + n);
-    const int per_wg = search_seqs_per_wg(n);
-    const dim3 grid(blocks_for(n, per_wg)), block(Tr::kThreads);
     const int rot = T / 2;
-    hipLaunchKernelGGL((viterbi_forward<L, CODE, W, false>), grid, block, 0, st, seq, w, T, b0, n,
-                       per_wg, rot, nullptr, bp, fin, fin_cost, nullptr, ca);
+    launch_forward<L, CODE, W, false>(seq, w, T, b0, n, rot, nullptr, bp, fin, fin_cost, nullptr, ca, st);
     qtcq_status rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     hipLaunchKernelGGL((viterbi_seam<L>), dim3(blocks_for(n, 256)), dim3(256), 0, st, bp, fin, T, n,
                        (T - rot) % T, overlap);
     rc = launch_status();
     if (rc != QTCQ_OK) return rc;
-    hipLaunchKernelGGL((viterbi_forward<L, CODE, W, true>), grid, block, 0, st, seq, w, T, b0, n,
-                       per_wg, 0, overlap, bp, fin, fin_cost, mse, ca);
+    launch_forward<L, CODE, W, true>(seq, w, T, b0, n, 0, overlap, bp, fin, fin_cost, mse, ca, st);
     rc = launch_status();
     if (rc != QTCQ_OK) return rc;
     hipLaunchKernelGGL((viterbi_traceback<L, true>), dim3(blocks_for(n, 256)), dim3(256), 0, st,

@@ -111,7 +111,7 @@ constexpr int kBitDelay = 1;
 // minima: a buffer is only written in the phase after every thread's reads of it have
 // completed (a barrier in between), and only read after the barrier that follows its
 // writes.  The code-value registers are shared by both sequences.
-template <int L, int CODE, bool WEIGHTED, bool PINNED = false>
+template <int L, int CODE, bool WEIGHTED, bool PINNED = false, bool SINGLE = false>
 __global__ void __launch_bounds__(Trellis<L>::kThreads)
 viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, int T, int64_t b0,
                 int64_t n, int per_wg, int rot, const uint32_t* __restrict__ pin,
@@ -281,6 +281,40 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
 
     float spA = ring_at(0, 0), spB = 0.f;
     float wpA = WEIGHTED ? ring_at(2, 0) : 1.0f, wpB = 1.0f;
+    if constexpr (SINGLE) {
+        // One sequence per workgroup (per_wg = 1): muB is free, so the group minima
+        // alternate between the two buffers (mu_t in muB for odd t, muA for even t) and one
+        // barrier per step orders both the reads of mu_{t-1} before the writes that reuse
+        // its buffer one step later and the writes of mu_t before their reads.  Each step
+        // reads its inputs at its start, so every use waits only for its own read, and
+        // then the next step's target.  Target ring: index t is read during step t, and
+        // chunk k + 1 is loaded into the slot of chunk k - 1 at the start of step
+        // 256 k + 1, two barriers after its last read (step 256 k - 1) and a barrier
+        // before its first (step 256 (k + 1)).  Step 1 takes mu_0 from the registers.
+        float spN = 0.f, wpN = 1.0f;   // the next step's target and weight
+        if (T > 1) {
+            if (T > 2) {
+                spN = ring_at(0, 1);
+                if constexpr (WEIGHTED) wpN = ring_at(2, 1);
+            }
+            const uint32_t wordA = acs(inA, spA, wpA, muB);
+            bpa[tid] = wordA;
+            __syncthreads();
+        }
+        for (int t = 2; t < T; ++t) {
+            if (t > kChunk && t % kChunk == 1 && (t / kChunk + 1) * kChunk < T) fill(t / kChunk + 1);
+            load_in((t & 1) ? muA : muB, inA);          // mu_{t-1}
+            spA = spN;
+            wpA = wpN;
+            if (t + 1 < T) {
+                spN = ring_at(0, t);
+                if constexpr (WEIGHTED) wpN = ring_at(2, t);
+            }
+            const uint32_t wordA = acs(inA, spA, wpA, (t & 1) ? muB : muA);
+            bpa[(int64_t)(t - 1) * Tr::kBpWords + tid] = wordA;
+            __syncthreads();
+        }
+    } else {
     for (int t = 1; t < T; ++t) {
         if (t > kChunk && t % kChunk == 1 && (t / kChunk + 1) * kChunk < T) fill(t / kChunk + 1);
         // phase 1: fetch B's inputs and target, step A
@@ -301,6 +335,7 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
             bpb[(int64_t)(t - 1) * Tr::kBpWords + tid] = wordB;
         }
         __syncthreads();
+    }
     }
 
     // final costs cost_{T-1}(i) = mu_{T-1}[i >> 2] + e_{T-1}(i); lowest i wins ties
@@ -363,7 +398,8 @@ viterbi_forward(const float* __restrict__ seq, const float* __restrict__ wts, in
             if (mse) mse[b0 + q] = best / (float)T;
         }
     };
-    finish(muA, sa, wa, qa);
+    // mu_{T-1}: in muA, or with one sequence per workgroup in the buffer of step T - 1
+    finish(SINGLE && ((T - 1) & 1) ? muB : muA, sa, wa, qa);
     if (has_b) finish(muB, sb, wb, qb);
 }
 
