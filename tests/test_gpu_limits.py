@@ -1,8 +1,10 @@
 """GPU parity at the largest sizes the C ABI accepts and at odd batch shapes: sequences
 of T = 4096 weights (the maximum) through the plain and tail-biting encoders, the
 decoders, the BCJR soft pass and its gradient; odd batches (the encoder interleaves two
-sequences per workgroup); the decode -> matvec with a 65,536-wide inner dimension.
-Each against the oracle at the bar of its own test module."""
+sequences per workgroup); the decode -> matvec with a 65,536-wide inner dimension;
+batches just above the device's compute-unit count, where the search switches from one
+sequence per workgroup to interleaved pairs.  Each against the oracle at the bar of its
+own test module."""
 import numpy as np
 import pytest
 
@@ -63,6 +65,46 @@ def test_tailbiting_ring_boundaries(api, T):
 def test_encode_odd_batch_L16(api):
     s = inputs.targets(7, 256, 4444)
     check_encode(api, s, None, 16, "1mad")
+
+
+# The search runs one sequence per workgroup when the batch fits in one round of compute
+# units, and interleaved pairs above that; the small batches above run the first form.
+# These batches take the paired form at every trellis size, with sequence lengths around
+# the target ring's chunk boundaries.
+def n_cus():
+    import torch
+    return torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+
+
+@pytest.mark.parametrize("L,T,code,weighted", [(6, 17, "1mad", False), (8, 256, "3inst", True),
+                                               (10, 513, "1mad", False), (10, 1025, "xor", True),
+                                               (12, 257, "1mad", True)])
+def test_encode_paired_workgroups(api, L, T, code, weighted):
+    B = n_cus() + 3
+    s = inputs.targets(B, T, 5000 + 10 * L + T % 7)
+    w = inputs.weights(B, T, 5001 + L) if weighted else None
+    if code == "xor":
+        code = ("xor", inputs.xor_masks(L))
+    check_encode(api, s, w, L, code)
+
+
+@pytest.mark.parametrize("L,T", [(8, 513), (12, 256)])
+def test_tailbiting_paired_workgroups(api, L, T):
+    B = n_cus() + 1
+    check_tb(api, inputs.targets(B, T, 5100 + L), None, L, "1mad")
+
+
+def test_encode_single_and_paired_agree(api):
+    """The last batch of one sequence per workgroup and the first of pairs give the same
+    bits for the rows they share (L = 16)."""
+    import torch
+    n = n_cus()
+    s = dev(inputs.targets(n + 1, 256, 5200))
+    b1, m1, x1 = api.encode(s[:n].contiguous(), want_states=True)
+    b2, m2, x2 = api.encode(s, want_states=True)
+    sync()
+    assert torch.equal(b1, b2[:n]) and torch.equal(x1, x2[:n])
+    assert torch.equal(m1.view(torch.int32), m2[:n].view(torch.int32))
 
 
 @pytest.mark.parametrize("tau", [1.0, 0.01])
