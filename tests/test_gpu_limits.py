@@ -88,7 +88,7 @@ def test_encode_paired_workgroups(api, L, T, code, weighted):
     check_encode(api, s, w, L, code)
 
 
-@pytest.mark.parametrize("L,T", [(8, 513), (12, 256)])
+@pytest.mark.parametrize("L,T", [(6, 37), (8, 513), (12, 256)])
 def test_tailbiting_paired_workgroups(api, L, T):
     B = n_cus() + 1
     check_tb(api, inputs.targets(B, T, 5100 + L), None, L, "1mad")
