@@ -422,7 +422,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // 64 threads (L >= 12) the chunk swizzle leaves a * NT alone, so chunk (a, 4tid + ..)
     // is at rb + addr(a * NT), a compile-time offset, and chunk (4tid + r, ..) at wb XOR 16 r
     // (r flips the two low chunk bits, which are bits 4 and 5 of the byte address).  The two
-    // bases are derived once per step from an opaque copy of the thread index (derive()),
+    // bases are derived once per step from an opaque copy of the thread index (derive),
     // so they are never live across steps and the compiler cannot hoist eight
     // loop-invariant addresses out of the step loops (they would be spilled).  Without
     // the split (smaller workgroups, or instantiations whose registers are full) each
@@ -436,11 +436,16 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         asm volatile("v_mov_b32 %0, %0" : "+v"(v));
         return v;
     };
+    using FwdSplit = std::integral_constant<bool, kSplitFwd>;
+    using BwdSplit = std::integral_constant<bool, kSplitBwd>;
     int rb = 0, wb = 0;
-    auto derive = [&]() {
-        const int t = opaque_tid();
-        rb = Ld::addr(lds_chunk(t));
-        wb = Ld::addr(lds_chunk(4 * t));
+    // derive<SPLIT>(): only where the phase uses the bases (no dead opaque copy otherwise)
+    auto derive = [&](auto split) {
+        if constexpr (decltype(split)::value) {
+            const int t = opaque_tid();
+            rb = Ld::addr(lds_chunk(t));
+            wb = Ld::addr(lds_chunk(4 * t));
+        }
     };
     auto rd_at = [&](int a, auto split) {
         if constexpr (decltype(split)::value) return rb + Ld::addr(a * NT);
@@ -450,8 +455,6 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         if constexpr (decltype(split)::value) return wb ^ (16 * r);
         else return Ld::addr(lds_chunk(4 * opaque_tid() + r));
     };
-    using FwdSplit = std::integral_constant<bool, kSplitFwd>;
-    using BwdSplit = std::integral_constant<bool, kSplitBwd>;
     auto rd = [&](int a) { return rd_at(a, FwdSplit{}); };
     auto wr = [&](int r) { return wr_at(r, FwdSplit{}); };
     auto rdb = [&](int a) { return rd_at(a, BwdSplit{}); };
@@ -460,7 +463,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
 
     // ---------------- forward ----------------
-    derive();
+    derive(FwdSplit{});
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wr(r), P, 0.0, 0.0, 0.0, 0.0);
     if (tid < kWaves) wmax[0][tid] = 0.f;
@@ -470,7 +473,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     double Sh = 0.0;   // sum of the energy shifts kappa w s^2 of the steps so far
     int par = 0;
     for (int t = 1; t < T; ++t) {
-        derive();
+        derive(FwdSplit{});
         float g = wmax[par][0];
 #pragma unroll
         for (int q = 1; q < kWaves; ++q) g = __builtin_fmaxf(g, wmax[par][q]);
@@ -535,7 +538,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     if (tid == 0) gsh[T - 1] = gl;
     double log2z;
     {
-        derive();
+        derive(FwdSplit{});
         const StepEnergy se = step_energy(T - 1);
         Sh = uniform64(Sh + se.shift(s[T - 1]));
         const double gl64 = (double)gl;
@@ -594,7 +597,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     PackedCodes<L, CODE> Ch;
     Ch.template init<CODE == kCodeXor || kSplitFwd>(tid, ca);
     // Y_{T-1} = 0
-    derive();
+    derive(BwdSplit{});
 #pragma unroll
     for (int r = 0; r < 4; ++r) lds_write4(buf, wrb(r), P, 0.0, 0.0, 0.0, 0.0);
     if (tid < kWaves) wmax[par][tid] = 0.f;
@@ -605,7 +608,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // One backward step at t (t >= 1 produces Y_{t-1}); the posterior of step t is
     // accumulated on the way.  At t = 0 only the posterior is formed (X_0 = 0).
     auto bstep = [&](int t, bool produce) {
-        derive();
+        derive(BwdSplit{});
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
         auto stash_at = [&](int a) -> int4 {
