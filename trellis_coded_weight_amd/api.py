@@ -105,15 +105,18 @@ BCJR_WS_CAP = 16 << 30
 VJP_WS_CAP = 32 << 30
 
 
-def _chunk_bytes(B: int, per: int, max_bytes: int | None) -> int:
+def _chunk_bytes(B: int, per: int, max_bytes: int | None, seqs_per_wg: int = 1) -> int:
     """Workspace bytes for min(B, what max_bytes holds) sequences of `per` bytes.  A
-    partial batch is rounded down to whole multiples of the device's CU count, so that
-    no launch ends with a nearly empty round of workgroups."""
+    partial batch is rounded down to whole multiples of the device's CU count times the
+    sequences one workgroup takes (two in the search once a chunk exceeds the CU count),
+    so that no launch ends with a partly empty round of workgroups."""
     if max_bytes is None or B * per <= max_bytes:
         return max(1, B) * per
     n = max(1, max_bytes // per)
     cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    if n > cus:
+    if n > cus * seqs_per_wg:
+        n = n // (cus * seqs_per_wg) * (cus * seqs_per_wg)
+    elif n > cus:
         n = n // cus * cus
     return n * per
 
@@ -121,7 +124,7 @@ def _chunk_bytes(B: int, per: int, max_bytes: int | None) -> int:
 def encode_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
                      max_bytes: int | None = ENCODE_WS_CAP) -> torch.Tensor:
     per = nat.qtcq_encode_workspace_bytes(1, T, L, k)
-    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
+    return torch.empty(_chunk_bytes(B, per, max_bytes, 2), dtype=torch.uint8, device="cuda")
 
 
 def bcjr_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
@@ -219,7 +222,7 @@ def tailbiting_words(L: int = 16, k: int = 2, T: int = 256) -> int:
 def tailbiting_workspace(B: int, T: int = 256, L: int = 16, k: int = 2,
                          max_bytes: int | None = ENCODE_WS_CAP) -> torch.Tensor:
     per = nat.qtcq_tailbiting_workspace_bytes(1, T, L, k)
-    return torch.empty(_chunk_bytes(B, per, max_bytes), dtype=torch.uint8, device="cuda")
+    return torch.empty(_chunk_bytes(B, per, max_bytes, 2), dtype=torch.uint8, device="cuda")
 
 
 def tailbiting_encode(seq: torch.Tensor, weights: torch.Tensor | None = None, L: int = 16,
