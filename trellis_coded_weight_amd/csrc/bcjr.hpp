@@ -427,9 +427,11 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // loop-invariant addresses out of the step loops (they would be spilled).  Without
     // the split (smaller workgroups, or instantiations whose registers are full) each
     // address is recomputed at its use from an opaque copy of the thread index.
-    // (The split costs registers across a step: the weighted gradient-mode forward and
-    // every weighted or gradient-mode backward would spill with it.)
+    // (The split costs registers across a step: the weighted gradient-mode forward would
+    // spill with it, and so would every weighted or gradient-mode backward with the write
+    // base, which stays live over the step; the backward's read base is used at once.)
     constexpr bool kSplitFwd = NT >= 64 && !(WEIGHTED && VJP);
+    constexpr bool kSplitBwdRd = NT >= 64;
     constexpr bool kSplitBwd = NT >= 64 && !WEIGHTED && !VJP;
     auto opaque_tid = [&]() {
         int v = tid;
@@ -438,8 +440,9 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     };
     using FwdSplit = std::integral_constant<bool, kSplitFwd>;
     using BwdSplit = std::integral_constant<bool, kSplitBwd>;
+    using BwdRdSplit = std::integral_constant<bool, kSplitBwdRd>;
     int rb = 0, wb = 0;
-    // derive<SPLIT>(): only where the phase uses the bases (no dead opaque copy otherwise)
+    // derive(split): only where the phase uses the bases (no dead opaque copy otherwise)
     auto derive = [&](auto split) {
         if constexpr (decltype(split)::value) {
             const int t = opaque_tid();
@@ -458,6 +461,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     auto rd = [&](int a) { return rd_at(a, FwdSplit{}); };
     auto wr = [&](int r) { return wr_at(r, FwdSplit{}); };
     auto rdb = [&](int a) { return rd_at(a, BwdSplit{}); };
+    auto wrb_rd = [&](int r) { return wr_at(r, BwdRdSplit{}); };   // the backward's reads
     auto wrb = [&](int r) { return wr_at(r, BwdSplit{}); };
 
     auto step_energy = [&](int t) { return StepEnergy(kappa, s[t], WEIGHTED ? w[t] : 1.0f); };
@@ -608,7 +612,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
     // One backward step at t (t >= 1 produces Y_{t-1}); the posterior of step t is
     // accumulated on the way.  At t = 0 only the posterior is formed (X_0 = 0).
     auto bstep = [&](int t, bool produce) {
-        derive(BwdSplit{});
+        derive(BwdRdSplit{});
         // Xn_t[(a, 4 tid + r)], r = 0..3, from the stash (Xn_0 = 0), prefetched one a
         // ahead; the first before the step's LDS reads and barrier
         auto stash_at = [&](int a) -> int4 {
@@ -624,7 +628,7 @@ bcjr_sweep(const float* __restrict__ seq, const float* __restrict__ wts, int T, 
         double yn[4][4];    // [r][x]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            lds_read4(buf, wrb(r), P, yn[r]);
+            lds_read4(buf, wrb_rd(r), P, yn[r]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) yn[r][x] -= h64;
             if constexpr (VJP && WIDE) {   // Yn_t[(4 tid + r, x)]
