@@ -117,3 +117,24 @@ def test_presplit_checks_its_split(api):
     y = api.decode_matvec_mfma_presplit(bits, 64, 64, sp)
     torch.cuda.synchronize()
     assert tuple(y.shape) == (8, 64)
+
+
+def test_default_workspaces_hold_whole_rounds(api):
+    """A capped workspace holds whole rounds of workgroups: twice the CU count of
+    sequences for the search (two per workgroup), the CU count for the soft pass."""
+    import torch
+    from trellis_coded_weight_amd import _native as nat
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    per = nat.qtcq_encode_workspace_bytes(1, 256, 16, 2)
+    ws = api.encode_workspace(10 * cus, 256, 16, 2, max_bytes=per * (2 * cus + 5))
+    assert ws.numel() == per * 2 * cus
+    tper = nat.qtcq_tailbiting_workspace_bytes(1, 256, 16, 2)
+    ws = api.tailbiting_workspace(10 * cus, 256, 16, 2, max_bytes=tper * (3 * cus))
+    assert ws.numel() == tper * 2 * cus
+    bper = nat.qtcq_bcjr_workspace_bytes(1, 256, 16, 2)
+    ws = api.bcjr_workspace(10 * cus, 256, 16, 2, max_bytes=bper * (cus + 5))
+    assert ws.numel() == bper * cus
+    del ws
+    # a cap below one round is taken as it is
+    ws = api.encode_workspace(10 * cus, 256, 16, 2, max_bytes=per * 7)
+    assert ws.numel() == per * 7
